@@ -1,0 +1,201 @@
+/*
+ * dwref.c -- CPU oracle for the forward depthwise 2-D convolution.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file; only the test suite, the smoke check and the bench's CPU-baseline
+ * leg do.  It shares no code, header or constant with the HIP library.
+ *
+ * What it computes (all references are to the pages this project follows):
+ *
+ *   * "Flash-DWC: Making Depthwise Convolution Compute-Efficient on GPUs",
+ *     section 2.1 (standard vs. depthwise convolution): in a depthwise
+ *     convolution every channel has its own FH x FW filter, IC = OC, and each
+ *     output element is the inner product of one channel's input patch with
+ *     that channel's filter.  Section 2.3 fixes the channel-last layout:
+ *     X is N x IH x IW x C, Y is N x OH x OW x C and the filter is re-laid as
+ *     FH x FW x C.
+ *   * "Tiles, halos and partial sums", section "Partition tensors to fit
+ *     storage": an output extent T with stride S, dilation D and kernel R needs
+ *     an input extent (T-1)S + (R-1)D + 1, and border padding is generated
+ *     (zeros), not fetched.  The output extent used here is the largest T
+ *     whose span fits the zero-padded input H + 2P.  The same passage says the
+ *     bias is added once and the partial sum is never rounded in between.
+ *   * "Outline of Programming Massively Parallel Processors Parallel Concepts
+ *     Part", section "2D Convolution": the filter is applied without flipping
+ *     (input index = output index - radius + filter index) and positions that
+ *     fall outside the image count as zero.
+ *
+ * So, for every n, oh, ow, c:
+ *
+ *   Y[n,oh,ow,c] = bias[c]
+ *                + sum_{fh<FH, fw<FW} X[n, oh*S - P + fh*D, ow*S - P + fw*D, c]
+ *                                     * W[fh, fw, c]
+ *
+ * with out-of-image X taken as zero.  Floating-point inputs arrive already
+ * widened to double (every fp32/fp16/bf16 value is exact in double, and so is
+ * every product of two of them); the sum is accumulated in double.  int8
+ * inputs accumulate exactly in int64.  Alongside each float output the oracle
+ * returns sum |x*w| over the same taps, the scale that the floating-point
+ * tolerance is stated against.
+ *
+ * The loop nest is deliberately plain: no blocking, no reordering, one output
+ * at a time.
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <math.h>
+
+/* Output extent along one axis: the largest O >= 1 whose input span
+ * (O-1)*S + (F-1)*D + 1 fits in IN + 2*P, or 0 when not even one output fits
+ * or an argument is out of range. */
+int dwref_out_dim(int in, int f, int s, int d, int p)
+{
+    if (in < 1 || f < 1 || s < 1 || d < 1 || p < 0) return 0;
+    long long room = (long long)in + 2LL * p - (long long)(f - 1) * d - 1;
+    if (room < 0) return 0;
+    long long o = room / s + 1;
+    if (o > 0x7fffffffLL) return 0;
+    return (int)o;
+}
+
+static int shape_ok(int N, int H, int W, int C, int FH, int FW, int S, int D, int P,
+                    int *OH, int *OW)
+{
+    if (N < 1 || C < 1) return 0;
+    *OH = dwref_out_dim(H, FH, S, D, P);
+    *OW = dwref_out_dim(W, FW, S, D, P);
+    return *OH > 0 && *OW > 0;
+}
+
+/* One output element, floating point.  Returns the exact-ish (fp64) sum and
+ * writes sum |x*w| to *scale. */
+static double one_out_f64(const double *x, const double *w, const double *bias,
+                          int H, int W, int C, int FH, int FW, int S, int D, int P,
+                          long long n, int oh, int ow, int c, double *scale)
+{
+    double acc = bias ? bias[c] : 0.0;
+    double sabs = 0.0;
+    for (int fh = 0; fh < FH; ++fh) {
+        int ih = oh * S - P + fh * D;
+        if (ih < 0 || ih >= H) continue;          /* generated zero padding */
+        for (int fw = 0; fw < FW; ++fw) {
+            int iw = ow * S - P + fw * D;
+            if (iw < 0 || iw >= W) continue;
+            double xv = x[((n * H + ih) * (long long)W + iw) * C + c];
+            double wv = w[((long long)fh * FW + fw) * C + c];
+            double prod = xv * wv;
+            acc += prod;
+            sabs += fabs(prod);
+        }
+    }
+    *scale = sabs;
+    return acc;
+}
+
+static int64_t one_out_i8(const int8_t *x, const int8_t *w, const int32_t *bias,
+                          int H, int W, int C, int FH, int FW, int S, int D, int P,
+                          long long n, int oh, int ow, int c)
+{
+    int64_t acc = bias ? (int64_t)bias[c] : 0;
+    for (int fh = 0; fh < FH; ++fh) {
+        int ih = oh * S - P + fh * D;
+        if (ih < 0 || ih >= H) continue;
+        for (int fw = 0; fw < FW; ++fw) {
+            int iw = ow * S - P + fw * D;
+            if (iw < 0 || iw >= W) continue;
+            int64_t xv = x[((n * H + ih) * (long long)W + iw) * C + c];
+            int64_t wv = w[((long long)fh * FW + fw) * C + c];
+            acc += xv * wv;
+        }
+    }
+    return acc;
+}
+
+/* Full forward pass, floating point.  x: N*H*W*C doubles, w: FH*FW*C doubles,
+ * bias: C doubles or NULL, y and scale: N*OH*OW*C doubles (scale may be NULL).
+ * Only images [n0, n1) are computed, so a caller can split the batch.
+ * Returns 0 on success, -1 on a bad shape. */
+int dwref_fwd_f64(const double *x, const double *w, const double *bias,
+                  double *y, double *scale,
+                  int N, int H, int W, int C, int FH, int FW, int S, int D, int P,
+                  int n0, int n1)
+{
+    int OH, OW;
+    if (!shape_ok(N, H, W, C, FH, FW, S, D, P, &OH, &OW)) return -1;
+    if (n0 < 0 || n1 > N || n0 > n1) return -1;
+    for (long long n = n0; n < n1; ++n)
+        for (int oh = 0; oh < OH; ++oh)
+            for (int ow = 0; ow < OW; ++ow)
+                for (int c = 0; c < C; ++c) {
+                    long long o = ((n * OH + oh) * (long long)OW + ow) * C + c;
+                    double s;
+                    y[o] = one_out_f64(x, w, bias, H, W, C, FH, FW, S, D, P,
+                                       n, oh, ow, c, &s);
+                    if (scale) scale[o] = s;
+                }
+    return 0;
+}
+
+/* Full forward pass, int8 x int8 with an int32 bias, accumulated exactly in
+ * int64.  Same layouts and batch split as dwref_fwd_f64. */
+int dwref_fwd_i8(const int8_t *x, const int8_t *w, const int32_t *bias, int64_t *y,
+                 int N, int H, int W, int C, int FH, int FW, int S, int D, int P,
+                 int n0, int n1)
+{
+    int OH, OW;
+    if (!shape_ok(N, H, W, C, FH, FW, S, D, P, &OH, &OW)) return -1;
+    if (n0 < 0 || n1 > N || n0 > n1) return -1;
+    for (long long n = n0; n < n1; ++n)
+        for (int oh = 0; oh < OH; ++oh)
+            for (int ow = 0; ow < OW; ++ow)
+                for (int c = 0; c < C; ++c) {
+                    long long o = ((n * OH + oh) * (long long)OW + ow) * C + c;
+                    y[o] = one_out_i8(x, w, bias, H, W, C, FH, FW, S, D, P,
+                                      n, oh, ow, c);
+                }
+    return 0;
+}
+
+/* Selected outputs only: idx[k] is a flat index into the N*OH*OW*C output.
+ * Used where the full pass would take too long on the CPU. */
+int dwref_points_f64(const double *x, const double *w, const double *bias,
+                     const int64_t *idx, int64_t npts, double *y, double *scale,
+                     int N, int H, int W, int C, int FH, int FW, int S, int D, int P)
+{
+    int OH, OW;
+    if (!shape_ok(N, H, W, C, FH, FW, S, D, P, &OH, &OW)) return -1;
+    long long total = (long long)N * OH * OW * C;
+    for (int64_t k = 0; k < npts; ++k) {
+        long long o = idx[k];
+        if (o < 0 || o >= total) return -1;
+        int c = (int)(o % C);
+        long long r = o / C;
+        int ow = (int)(r % OW); r /= OW;
+        int oh = (int)(r % OH);
+        long long n = r / OH;
+        double s;
+        y[k] = one_out_f64(x, w, bias, H, W, C, FH, FW, S, D, P, n, oh, ow, c, &s);
+        if (scale) scale[k] = s;
+    }
+    return 0;
+}
+
+int dwref_points_i8(const int8_t *x, const int8_t *w, const int32_t *bias,
+                    const int64_t *idx, int64_t npts, int64_t *y,
+                    int N, int H, int W, int C, int FH, int FW, int S, int D, int P)
+{
+    int OH, OW;
+    if (!shape_ok(N, H, W, C, FH, FW, S, D, P, &OH, &OW)) return -1;
+    long long total = (long long)N * OH * OW * C;
+    for (int64_t k = 0; k < npts; ++k) {
+        long long o = idx[k];
+        if (o < 0 || o >= total) return -1;
+        int c = (int)(o % C);
+        long long r = o / C;
+        int ow = (int)(r % OW); r /= OW;
+        int oh = (int)(r % OH);
+        long long n = r / OH;
+        y[k] = one_out_i8(x, w, bias, H, W, C, FH, FW, S, D, P, n, oh, ow, c);
+    }
+    return 0;
+}
