@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of the forward depthwise convolution on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--variant auto|direct|rowwin|ldstile|mfma] [--no-cpu]
+
+A step is one forward pass (one launch of the library's kernel) over one batch
+of seeded synthetic input.  The inputs are copied to HBM before timing.  So
+that no step finds its input in the 256 MB Infinity Cache (MALL) or in L2
+from an earlier step, the bench keeps several copies of x and y, at least
+1 GiB in all, and steps walk through them in turn.
+
+Prints one JSON line:
+  value           algorithmic GB/s of the whole timed region (bytes / wall time)
+  roofline        the kernel's own duration (HIP events around each launch,
+                  averaged) against MI355X's 8 TB/s HBM, plus the HBM traffic
+                  the rocprofv3 counters measured for this kernel (or null)
+  cpu_baseline    the CPU oracle timed on this host's cores on a sample
+Algorithmic bytes count x, w, bias and y once each; halo re-reads and
+padding are not counted.  FLOPs are 2 per tap per output.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "depthwise-conv fwd GB/s + GFLOP/s and fraction of HBM roofline, 1 MI355X"
+DEFAULT_WORKLOAD = "mobilenet_f32_3x3"
+HBM_PEAK_GBS = 8000.0
+MALL_FLUSH_BYTES = 1 << 30
+XB = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
+YB = {"f32": 4, "f16": 2, "bf16": 2, "i8": 4}
+
+
+def out_extent(size, f, s, d, p):
+    return (size + 2 * p - d * (f - 1) - 1) // s + 1
+
+
+def work(wl):
+    """(algorithmic bytes, flops, OH, OW) of one forward pass."""
+    OH = out_extent(wl.H, wl.FH, wl.stride, wl.dilation, wl.pad)
+    OW = out_extent(wl.W, wl.FW, wl.stride, wl.dilation, wl.pad)
+    xb = wl.N * wl.H * wl.W * wl.C * XB[wl.dtype]
+    wb = wl.FH * wl.FW * wl.C * XB[wl.dtype]
+    bb = wl.C * 4 if wl.b_dist is not None else 0
+    yb = wl.N * OH * OW * wl.C * YB[wl.dtype]
+    flops = 2 * wl.N * OH * OW * wl.C * wl.FH * wl.FW
+    return xb + wb + bb + yb, flops, OH, OW
+
+
+def kernel_sources_hash():
+    """Hash of the library sources; counter figures stored under profiles/
+    are reported only while it matches the hash they were taken with."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "depthwise_convolution_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload, variant):
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{workload}/{variant}")
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("sources") != kernel_sources_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, x, w, b, budget_s=20.0):
+    """The CPU oracle (test infrastructure, untuned) on this host's cores.
+    Sample: whole images of the same workload, as many as fit the budget
+    after a one-image probe."""
+    import oracle
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    oracle.fwd(x[:1], w, b, wl.stride, wl.dilation, wl.pad, wl.dtype, threads=1)
+    per_image_1t = time.perf_counter() - t0
+    n = int(max(1, min(wl.N, budget_s * threads / max(per_image_1t, 1e-6))))
+    n = max(min(n, wl.N), min(threads, wl.N))
+    t0 = time.perf_counter()
+    oracle.fwd(x[:n], w, b, wl.stride, wl.dilation, wl.pad, wl.dtype, threads=threads)
+    dt = time.perf_counter() - t0
+    sub = type(wl)(**{**wl.__dict__, "N": n})
+    nbytes, flops, _, _ = work(sub)
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} of {wl.N} images of {wl.name} (fp64/int64 loop nest, "
+                      f"{dt:.2f} s, {flops / dt / 1e9:.2f} GFLOP/s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--variant", default="auto")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (shard over the batch: one process per GPU, no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import depthwise_convolution_amd as dw
+    from synth import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    nbytes, flops, OH, OW = work(wl)
+    print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    x, w, b = make_inputs(wl)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a, fmt):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if fmt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    ydt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+           "i8": torch.int32}[wl.dtype]
+    set_bytes = nbytes
+    sets = max(2, -(-MALL_FLUSH_BYTES // set_bytes))
+    xd0 = to_dev(x, wl.dtype)
+    xs = [xd0] + [xd0.clone() for _ in range(sets - 1)]
+    ys = [torch.empty((wl.N, OH, OW, wl.C), dtype=ydt, device=dev) for _ in range(sets)]
+    wd = to_dev(w, wl.dtype)
+    bd = to_dev(b, "f32" if wl.dtype != "i8" else "i8")
+    torch.cuda.synchronize()
+
+    h = dw.dwconv_create_variant(wl.N, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride,
+                                 wl.dilation, wl.pad, wl.dtype, args.variant)
+    variant = dw.dwconv_plan_variant(h)
+    desc = dw.dwconv_plan_describe(h)
+    stream = torch.cuda.current_stream(dev)
+    print(f"[bench] plan: {desc}; {sets} buffer sets of {set_bytes / 1e6:.1f} MB",
+          file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        dw.dwconv_fwd(h, xs[i % sets], wd, bd, ys[i % sets], stream)
+    K = args.steps
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        ev0[i].record(stream)
+        dw.dwconv_fwd(h, xs[i % sets], wd, bd, ys[i % sets], stream)
+        ev1[i].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    total_ms = start.elapsed_time(end)
+    kern_ms = np.array([a.elapsed_time(z) for a, z in zip(ev0, ev1)])
+    dw.dwconv_destroy(h)
+
+    ms_per_step = total_ms / K
+    kavg_ms = float(kern_ms.mean())
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (kavg_ms * 1e-3) / 1e9
+    traffic = stored_traffic(wl.name, variant)
+    print(f"[bench] kernel avg {kavg_ms * 1e3:.2f} us (median "
+          f"{np.median(kern_ms) * 1e3:.2f}, min {kern_ms.min() * 1e3:.2f}); step "
+          f"{ms_per_step * 1e3:.2f} us; host wall {t_wall * 1e3 / K:.2f} us/step",
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, x, w, b)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "N": wl.N, "H": wl.H, "W": wl.W, "C": wl.C,
+                   "FH": wl.FH, "FW": wl.FW, "stride": wl.stride,
+                   "dilation": wl.dilation, "pad": wl.pad, "bias": wl.b_dist is not None,
+                   "layout": "NHWC", "parallelism": "single GPU"},
+        "gflops": round(flops / (ms_per_step * 1e-3) / 1e9, 2),
+        "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes": nbytes,
+        "flops": flops,
+        "kernel": {"variant": variant, "plan": desc,
+                   "avg_us": round(kavg_ms * 1e3, 3),
+                   "median_us": round(float(np.median(kern_ms)) * 1e3, 3),
+                   "min_us": round(float(kern_ms.min()) * 1e3, 3),
+                   "buffer_sets": sets},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

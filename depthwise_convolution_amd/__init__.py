@@ -1,0 +1,198 @@
+"""Python binding of libdwconv.so, the gfx950 forward depthwise convolution.
+
+The functions carry the C ABI's names (``include/dwconv.h``) and only marshal
+arguments: every step of the computation runs in the HIP kernels.  Torch is
+used for device memory and streams.  There is no CPU path: if the library is
+missing, importing this package fails.
+
+    h = dwconv_create(N, H, W, C, FH, FW, stride, dilation, pad, "f16")
+    dwconv_fwd(h, x, w, bias, y)          # torch tensors on the GPU, or raw ints
+    dwconv_destroy(h)
+
+or, with allocation of the output:
+
+    conv = DepthwiseConv2d(N, H, W, C, FH, FW, stride, dilation, pad, "f16")
+    y = conv(x, w, bias)
+"""
+import ctypes
+import os
+
+# torch carries its own HIP and HSA runtimes (same sonames as /opt/rocm's).
+# Loading it first makes libdwconv.so bind to those copies, so the process
+# holds one HIP runtime and torch's device pointers and streams are valid in
+# the library.  Loaded the other way round, two runtimes would share the GPU.
+import torch  # noqa: E402,F401
+
+__all__ = [
+    "DWCONV_F32", "DWCONV_F16", "DWCONV_BF16", "DWCONV_I8",
+    "VARIANTS", "DwconvError", "DepthwiseConv2d", "library_path",
+    "dwconv_create", "dwconv_create_variant", "dwconv_fwd", "dwconv_destroy",
+    "dwconv_output_dims", "dwconv_plan_variant", "dwconv_plan_describe",
+    "dwconv_status_string",
+]
+
+DWCONV_F32, DWCONV_F16, DWCONV_BF16, DWCONV_I8 = 0, 1, 2, 3
+VARIANTS = {"auto": 0, "direct": 1, "rowwin": 2, "ldstile": 3, "mfma": 4}
+_VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
+_DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libdwconv.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(
+        f"{library_path} is missing: build it with "
+        "`python -m depthwise_convolution_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(library_path)
+_H = ctypes.c_void_p
+_I = ctypes.c_int
+_lib.dwconv_create.argtypes = [ctypes.POINTER(_H)] + [_I] * 10
+_lib.dwconv_create.restype = _I
+_lib.dwconv_create_variant.argtypes = [ctypes.POINTER(_H)] + [_I] * 11
+_lib.dwconv_create_variant.restype = _I
+_lib.dwconv_fwd.argtypes = [_H, _H, _H, _H, _H, _H]
+_lib.dwconv_fwd.restype = _I
+_lib.dwconv_destroy.argtypes = [_H]
+_lib.dwconv_destroy.restype = _I
+_lib.dwconv_output_dims.argtypes = [_H, ctypes.POINTER(_I), ctypes.POINTER(_I)]
+_lib.dwconv_output_dims.restype = _I
+_lib.dwconv_plan_variant.argtypes = [_H]
+_lib.dwconv_plan_variant.restype = _I
+_lib.dwconv_plan_describe.argtypes = [_H]
+_lib.dwconv_plan_describe.restype = ctypes.c_char_p
+_lib.dwconv_status_string.argtypes = [_I]
+_lib.dwconv_status_string.restype = ctypes.c_char_p
+
+
+class DwconvError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {dwconv_status_string(status)} (status {status})")
+
+
+def dwconv_status_string(status: int) -> str:
+    return _lib.dwconv_status_string(int(status)).decode()
+
+
+def _dtype_code(dtype):
+    if isinstance(dtype, int):
+        return dtype
+    if isinstance(dtype, str):
+        if dtype not in _DTYPE_CODES:
+            raise ValueError(f"unknown dtype {dtype!r}")
+        return _DTYPE_CODES[dtype]
+    import torch
+    m = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.int8: 3}
+    if dtype not in m:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return m[dtype]
+
+
+def dwconv_create_variant(N, H, W, C, FH, FW, stride, dilation, pad, dtype, variant):
+    """Returns an opaque handle (int); raises DwconvError on a bad shape."""
+    h = _H()
+    v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    rc = _lib.dwconv_create_variant(ctypes.byref(h), N, H, W, C, FH, FW, stride,
+                                    dilation, pad, _dtype_code(dtype), v)
+    if rc != 0:
+        raise DwconvError(rc, "dwconv_create")
+    return h.value
+
+
+def dwconv_create(N, H, W, C, FH, FW, stride, dilation, pad, dtype):
+    return dwconv_create_variant(N, H, W, C, FH, FW, stride, dilation, pad, dtype, 0)
+
+
+def dwconv_destroy(h) -> None:
+    _lib.dwconv_destroy(h)
+
+
+def dwconv_output_dims(h):
+    oh, ow = _I(), _I()
+    rc = _lib.dwconv_output_dims(h, ctypes.byref(oh), ctypes.byref(ow))
+    if rc != 0:
+        raise DwconvError(rc, "dwconv_output_dims")
+    return oh.value, ow.value
+
+
+def dwconv_plan_variant(h) -> str:
+    return _VARIANT_NAMES.get(_lib.dwconv_plan_variant(h), "?")
+
+
+def dwconv_plan_describe(h) -> str:
+    return _lib.dwconv_plan_describe(h).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous (channel-last as laid out)")
+    return t.data_ptr()
+
+
+def _stream(stream, like):
+    if stream is None:
+        import torch
+        dev = like.device if hasattr(like, "device") else None
+        return torch.cuda.current_stream(dev).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dwconv_fwd(h, x, w, bias, y, stream=None) -> None:
+    """Enqueues the forward pass.  x, w, bias, y: GPU tensors (or raw device
+    pointers as ints); bias may be None.  ``stream``: torch stream, raw
+    hipStream_t int, or None for torch's current stream."""
+    rc = _lib.dwconv_fwd(h, _ptr(x), _ptr(w), _ptr(bias), _ptr(y), _stream(stream, x))
+    if rc != 0:
+        raise DwconvError(rc, "dwconv_fwd")
+
+
+class DepthwiseConv2d:
+    """Owns a plan; ``conv(x, w, bias)`` allocates y with torch and runs the
+    kernel.  x: N x H x W x C, w: FH x FW x C, bias: C (fp32, or int32 for
+    int8) or None."""
+
+    _TORCH_Y = {0: "float32", 1: "float16", 2: "bfloat16", 3: "int32"}
+
+    def __init__(self, N, H, W, C, FH, FW, stride=1, dilation=1, pad=0, dtype="f32",
+                 variant="auto"):
+        self.shape = (N, H, W, C, FH, FW, stride, dilation, pad)
+        self.dtype = _dtype_code(dtype)
+        self.handle = dwconv_create_variant(N, H, W, C, FH, FW, stride, dilation, pad,
+                                            self.dtype, variant)
+        self.OH, self.OW = dwconv_output_dims(self.handle)
+
+    @property
+    def variant(self):
+        return dwconv_plan_variant(self.handle)
+
+    def describe(self):
+        return dwconv_plan_describe(self.handle)
+
+    def __call__(self, x, w, bias=None, y=None, stream=None):
+        import torch
+        N, _, _, C = self.shape[:4]
+        if y is None:
+            y = torch.empty((N, self.OH, self.OW, C), device=x.device,
+                            dtype=getattr(torch, self._TORCH_Y[self.dtype]))
+        dwconv_fwd(self.handle, x, w, bias, y, stream)
+        return y
+
+    def close(self):
+        if self.handle:
+            dwconv_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

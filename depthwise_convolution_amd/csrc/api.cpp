@@ -1,0 +1,82 @@
+// api.cpp -- the extern "C" entry points declared in include/dwconv.h.
+#include <new>
+#include <stdint.h>
+
+#include "../../include/dwconv.h"
+#include "plan.h"
+
+struct dwconv_plan {
+    dw::Plan p;
+};
+
+extern "C" {
+
+dwconv_status_t dwconv_create_variant(dwconv_handle_t *out, int N, int H, int W, int C,
+                                      int FH, int FW, int stride, int dilation, int pad,
+                                      dwconv_dtype_t dtype, dwconv_variant_t variant) {
+    if (!out) return DWCONV_ERR_INVALID_ARG;
+    *out = nullptr;
+    dwconv_plan *h = new (std::nothrow) dwconv_plan;
+    if (!h) return DWCONV_ERR_ALLOC;
+    int rc = dw::make_plan(h->p, N, H, W, C, FH, FW, stride, dilation, pad, (int)dtype,
+                           (int)variant);
+    if (rc != DWCONV_OK) {
+        delete h;
+        return (dwconv_status_t)rc;
+    }
+    *out = h;
+    return DWCONV_OK;
+}
+
+dwconv_status_t dwconv_create(dwconv_handle_t *out, int N, int H, int W, int C, int FH,
+                              int FW, int stride, int dilation, int pad,
+                              dwconv_dtype_t dtype) {
+    return dwconv_create_variant(out, N, H, W, C, FH, FW, stride, dilation, pad, dtype,
+                                 DWCONV_VARIANT_AUTO);
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
+                           const void *bias, void *y, hipStream_t stream) {
+    if (!h || !x || !w || !y) return DWCONV_ERR_INVALID_ARG;
+    const dw::Plan &p = h->p;
+    // The vectorised families need 16-byte aligned tensors; anything else
+    // runs on the direct family, which takes any alignment.
+    bool ok_align = aligned16(x) && aligned16(w) && aligned16(y) &&
+                    (bias == nullptr || aligned16(bias));
+    dw::LaunchFn fn = ok_align ? p.launch : p.fallback;
+    hipError_t e = fn(p, x, w, bias, y, stream);
+    return e == hipSuccess ? DWCONV_OK : DWCONV_ERR_HIP;
+}
+
+dwconv_status_t dwconv_destroy(dwconv_handle_t h) {
+    delete h;
+    return DWCONV_OK;
+}
+
+dwconv_status_t dwconv_output_dims(dwconv_handle_t h, int *OH, int *OW) {
+    if (!h || !OH || !OW) return DWCONV_ERR_INVALID_ARG;
+    *OH = h->p.s.OH;
+    *OW = h->p.s.OW;
+    return DWCONV_OK;
+}
+
+dwconv_variant_t dwconv_plan_variant(dwconv_handle_t h) {
+    return h ? (dwconv_variant_t)h->p.variant : DWCONV_VARIANT_AUTO;
+}
+
+const char *dwconv_plan_describe(dwconv_handle_t h) { return h ? h->p.desc : ""; }
+
+const char *dwconv_status_string(dwconv_status_t s) {
+    switch (s) {
+        case DWCONV_OK: return "ok";
+        case DWCONV_ERR_INVALID_ARG: return "invalid argument";
+        case DWCONV_ERR_UNSUPPORTED: return "unsupported";
+        case DWCONV_ERR_HIP: return "HIP runtime error";
+        case DWCONV_ERR_ALLOC: return "out of host memory";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// dw_common.h -- shapes, element-type traits and small device helpers shared
+// by the gfx950 depthwise-convolution kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dw {
+
+// Operation shape.  Names follow "Flash-DWC: Making Depthwise Convolution
+// Compute-Efficient on GPUs", section 2.1 (N, H = IH, W = IW, C = IC = OC,
+// FH, FW, OH, OW) plus stride S, dilation D and padding P.
+struct Shape {
+    int N, H, W, C;
+    int FH, FW;
+    int S, D, P;
+    int OH, OW;
+};
+
+// ---------------------------------------------------------------------------
+// Element-type traits.  X: stored input/filter element; Acc: accumulator;
+// Bias: bias element (always the accumulator type); Y: stored output.
+// ---------------------------------------------------------------------------
+struct F32 {
+    using X = float;
+    using Acc = float;
+    using Bias = float;
+    using Y = float;
+    static __device__ __forceinline__ float widen(float v) { return v; }
+    static __device__ __forceinline__ float narrow(float a) { return a; }
+};
+
+struct F16 {
+    using X = _Float16;
+    using Acc = float;
+    using Bias = float;
+    using Y = _Float16;
+    static __device__ __forceinline__ float widen(_Float16 v) { return (float)v; }
+    // v_cvt_f16_f32 rounds to nearest even in the default rounding mode
+    static __device__ __forceinline__ _Float16 narrow(float a) { return (_Float16)a; }
+};
+
+struct BF16 {
+    using X = uint16_t;  // bfloat16 bit pattern
+    using Acc = float;
+    using Bias = float;
+    using Y = uint16_t;
+    static __device__ __forceinline__ float widen(uint16_t v) {
+        return __uint_as_float((uint32_t)v << 16);
+    }
+    // fp32 -> bf16, round to nearest even on the dropped 16 bits; NaN stays NaN
+    static __device__ __forceinline__ uint16_t narrow(float a) {
+        uint32_t u = __float_as_uint(a);
+        if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+        u += 0x7fffu + ((u >> 16) & 1u);
+        return (uint16_t)(u >> 16);
+    }
+};
+
+struct I8 {
+    using X = int8_t;
+    using Acc = int32_t;
+    using Bias = int32_t;
+    using Y = int32_t;
+    static __device__ __forceinline__ int32_t widen(int8_t v) { return (int32_t)v; }
+    static __device__ __forceinline__ int32_t narrow(int32_t a) { return a; }
+};
+
+template <class A>
+__device__ __forceinline__ A mac(A acc, A a, A b);
+template <>
+__device__ __forceinline__ float mac<float>(float acc, float a, float b) {
+    return __builtin_fmaf(a, b, acc);
+}
+template <>
+__device__ __forceinline__ int32_t mac<int32_t>(int32_t acc, int32_t a, int32_t b) {
+    return acc + a * b;
+}
+
+// Workgroups are handed to the 8 XCDs of the chip round-robin, and each XCD
+// has its own L2.  Renumber them so that a contiguous range of logical tiles
+// (which share halo rows) lands on one XCD.  A bijection on [0, nb).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb) {
+    constexpr uint32_t NX = 8;
+    uint32_t q = nb / NX, rem = nb % NX;
+    uint32_t xcd = b % NX, k = b / NX;
+    return xcd < rem ? xcd * (q + 1) + k : rem * (q + 1) + (xcd - rem) * q + k;
+}
+
+}  // namespace dw

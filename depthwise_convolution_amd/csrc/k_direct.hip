@@ -1,0 +1,85 @@
+// k_direct.hip -- the "direct" kernel family: one lane per output element.
+//
+// Runs every shape, dtype and alignment, so it is the fallback for pointers
+// that are not 16-byte aligned and for channel counts whose pixel is not a
+// whole number of 16-byte vectors.  Consecutive lanes take consecutive
+// channels of one output pixel, so each tap's loads are contiguous along C
+// (channel-last layout, "Flash-DWC: Making Depthwise Convolution
+// Compute-Efficient on GPUs", section 2.3).
+//
+// Each filter row is summed into its own fresh partial, which is then added
+// to the running sum; the bias seeds that sum once, and nothing is rounded
+// to the storage type before the final store ("Tiles, halos and partial
+// sums", section "Partition tensors to fit storage"; "Flash-DWC", section
+// 3.3 decomposes the 2-D filter into FH one-dimensional rows).
+#include "plan.h"
+
+#include <stdio.h>
+
+namespace dw {
+
+template <class DT>
+__global__ void __launch_bounds__(256)
+k_direct(const typename DT::X *__restrict__ x, const typename DT::X *__restrict__ w,
+         const typename DT::Bias *__restrict__ bias, typename DT::Y *__restrict__ y,
+         Shape s, long long total) {
+    using Acc = typename DT::Acc;
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    for (long long o = (long long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+         o += stride) {
+        int c = (int)(o % s.C);
+        long long r = o / s.C;
+        int ow = (int)(r % s.OW);
+        r /= s.OW;
+        int oh = (int)(r % s.OH);
+        long long n = r / s.OH;
+        Acc acc = bias ? bias[c] : Acc(0);
+        for (int fh = 0; fh < s.FH; ++fh) {
+            int ih = oh * s.S - s.P + fh * s.D;
+            if ((unsigned)ih >= (unsigned)s.H) continue;  // generated zero rows
+            const typename DT::X *xr = x + ((n * s.H + ih) * (long long)s.W) * s.C + c;
+            const typename DT::X *wr = w + (long long)fh * s.FW * s.C + c;
+            Acc row = Acc(0);
+            for (int fw = 0; fw < s.FW; ++fw) {
+                int iw = ow * s.S - s.P + fw * s.D;
+                if ((unsigned)iw >= (unsigned)s.W) continue;  // generated zeros
+                row = mac<Acc>(row, DT::widen(xr[(long long)iw * s.C]),
+                               DT::widen(wr[(long long)fw * s.C]));
+            }
+            acc += row;
+        }
+        y[o] = DT::narrow(acc);
+    }
+}
+
+template <class DT>
+static hipError_t launch_direct(const Plan &p, const void *x, const void *w,
+                                const void *bias, void *y, hipStream_t st) {
+    long long total = (long long)p.s.N * p.s.OH * p.s.OW * p.s.C;
+    hipLaunchKernelGGL(k_direct<DT>, dim3(p.grid), dim3(p.block), 0, st,
+                       (const typename DT::X *)x, (const typename DT::X *)w,
+                       (const typename DT::Bias *)bias, (typename DT::Y *)y, p.s, total);
+    return hipGetLastError();
+}
+
+bool plan_direct(Plan &p) {
+    long long total = (long long)p.s.N * p.s.OH * p.s.OW * p.s.C;
+    p.variant = V_DIRECT;
+    p.block = 256;
+    long long blocks = (total + 255) / 256;
+    // grid-stride beyond 2^20 workgroups: plenty to fill 256 CUs
+    p.grid = (uint32_t)(blocks < (1LL << 20) ? blocks : (1LL << 20));
+    p.vec = 1;
+    p.tm = 1;
+    switch (p.dtype) {
+        case DT_F32: p.launch = launch_direct<F32>; break;
+        case DT_F16: p.launch = launch_direct<F16>; break;
+        case DT_BF16: p.launch = launch_direct<BF16>; break;
+        case DT_I8: p.launch = launch_direct<I8>; break;
+        default: return false;
+    }
+    snprintf(p.desc, sizeof(p.desc), "direct: 1 output/lane, %u x %d", p.grid, p.block);
+    return true;
+}
+
+}  // namespace dw

@@ -1,0 +1,75 @@
+// plan.cpp -- validation, output extent and kernel-family choice.  Host only;
+// makes no HIP calls.
+#include "plan.h"
+
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/dwconv.h"
+
+namespace dw {
+
+// The input span of an output extent O is (O-1)S + (F-1)D + 1 ("Tiles, halos
+// and partial sums", section "Partition tensors to fit storage"); the output
+// extent is the largest O whose span fits the zero-padded input in + 2p.
+int out_extent(int in, int f, int s, int d, int p) {
+    if (in < 1 || f < 1 || s < 1 || d < 1 || p < 0) return 0;
+    long long room = (long long)in + 2LL * p - (long long)(f - 1) * d - 1;
+    if (room < 0) return 0;
+    long long o = room / s + 1;
+    return o > 0x7fffffffLL ? 0 : (int)o;
+}
+
+static int elem_bytes_of(int dtype) {
+    switch (dtype) {
+        case DT_F32: return 4;
+        case DT_F16: return 2;
+        case DT_BF16: return 2;
+        case DT_I8: return 1;
+    }
+    return 0;
+}
+
+int make_plan(Plan &p, int N, int H, int W, int C, int FH, int FW, int S, int D,
+              int P, int dtype, int variant) {
+    memset(&p, 0, sizeof(p));
+    if (N < 1 || H < 1 || W < 1 || C < 1 || FH < 1 || FW < 1 || S < 1 || D < 1 || P < 0)
+        return DWCONV_ERR_INVALID_ARG;
+    int eb = elem_bytes_of(dtype);
+    if (eb == 0) return DWCONV_ERR_INVALID_ARG;
+    if (variant < V_AUTO || variant > V_MFMA) return DWCONV_ERR_INVALID_ARG;
+    int OH = out_extent(H, FH, S, D, P);
+    int OW = out_extent(W, FW, S, D, P);
+    if (OH < 1 || OW < 1) return DWCONV_ERR_INVALID_ARG;
+    const long long lim = 1LL << 31;
+    if ((long long)N * H * W * C >= lim || (long long)N * OH * OW * C >= lim ||
+        (long long)FH * FW * C >= lim)
+        return DWCONV_ERR_INVALID_ARG;
+    if (dtype == DT_I8 && (long long)FH * FW > 131071) return DWCONV_ERR_INVALID_ARG;
+
+    p.s = Shape{N, H, W, C, FH, FW, S, D, P, OH, OW};
+    p.dtype = dtype;
+    p.elem_bytes = eb;
+
+    // The direct family runs every shape and alignment; it is also the
+    // fallback for pointers that are not 16-byte aligned.
+    Plan d = p;
+    if (!plan_direct(d)) return DWCONV_ERR_UNSUPPORTED;
+
+    bool ok = false;
+    switch (variant) {
+        case V_DIRECT: p = d; ok = true; break;
+        case V_ROWWIN: ok = plan_rowwin(p); break;
+        case V_LDSTILE: ok = plan_ldstile(p); break;
+        case V_MFMA: ok = plan_mfma(p); break;
+        case V_AUTO:
+            ok = plan_mfma(p) || plan_ldstile(p) || plan_rowwin(p);
+            if (!ok) { p = d; ok = true; }
+            break;
+    }
+    if (!ok) return DWCONV_ERR_UNSUPPORTED;
+    p.fallback = d.launch;
+    return DWCONV_OK;
+}
+
+}  // namespace dw

@@ -1,0 +1,52 @@
+// plan.h -- host-side plan of one forward depthwise convolution: validated
+// shape, output extent and the kernel family / tiling chosen for it.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "dw_common.h"
+
+namespace dw {
+
+enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 };
+enum Variant { V_AUTO = 0, V_DIRECT = 1, V_ROWWIN = 2, V_LDSTILE = 3, V_MFMA = 4 };
+
+struct Plan;
+using LaunchFn = hipError_t (*)(const Plan &, const void *x, const void *w,
+                                const void *bias, void *y, hipStream_t);
+
+struct Plan {
+    Shape s;
+    int dtype;
+    int variant;          // family launched for aligned pointers
+    int elem_bytes;       // bytes of one stored x / w element
+    // kernel-specific tiling (meaning depends on the family)
+    int vec;              // channels per lane (one 4/8/16-byte vector)
+    int tm;               // consecutive outputs along width per lane
+    int th;               // output rows per lane / tile
+    int cs;               // channels per tile
+    int lds_bytes;        // dynamic LDS per workgroup
+    int block;            // threads per workgroup
+    uint32_t grid;        // workgroups
+    int aux0, aux1;       // family-specific extra launch parameters
+    LaunchFn launch;      // launcher for `variant`
+    LaunchFn fallback;    // launcher for misaligned pointers (direct family)
+    char desc[192];
+};
+
+// Output extent along one axis; 0 when not even one output fits.
+int out_extent(int in, int f, int s, int d, int p);
+
+// Validates and fills `p`.  Returns a dwconv_status_t value.
+int make_plan(Plan &p, int N, int H, int W, int C, int FH, int FW, int S, int D,
+              int P, int dtype, int variant);
+
+// Per-family planners, defined next to their kernels.  Each returns true and
+// fills the tiling and launcher when it can run the shape.
+bool plan_direct(Plan &p);
+bool plan_rowwin(Plan &p);
+bool plan_ldstile(Plan &p);
+bool plan_mfma(Plan &p);
+
+}  // namespace dw

@@ -1,0 +1,126 @@
+/*
+ * dwconv.h -- C ABI of the MI355X (gfx950) forward depthwise 2-D convolution.
+ *
+ * Operation ("Flash-DWC: Making Depthwise Convolution Compute-Efficient on
+ * GPUs", sections 2.1 and 2.3; "Tiles, halos and partial sums", section
+ * "Partition tensors to fit storage"):
+ *
+ *   Y[n,oh,ow,c] = bias[c] + sum_{fh<FH, fw<FW}
+ *                   X[n, oh*S - P + fh*D, ow*S - P + fw*D, c] * Wt[fh,fw,c]
+ *
+ * Every channel is filtered by its own FH x FW filter (input channels =
+ * output channels = C).  The filter is applied as a correlation (not
+ * flipped).  Input positions outside the image read as zero (padding is
+ * generated, never fetched).  OH = floor((H + 2P - D(FH-1) - 1)/S) + 1, the
+ * largest output extent whose input span (OH-1)S + (FH-1)D + 1 fits the
+ * padded height; OW likewise.  Stride S, dilation D and padding P apply to
+ * both axes; FH and FW may differ.
+ *
+ * Layouts (dense, row-major, channel last):
+ *   x    N  x H  x W  x C
+ *   w    FH x FW x C          (the filter re-laid channel-last)
+ *   bias C                    (may be NULL: no bias)
+ *   y    N  x OH x OW x C
+ *
+ * Element types per dtype:
+ *   DWCONV_F32   x, w float     bias float   y float    accumulate fp32
+ *   DWCONV_F16   x, w fp16      bias float   y fp16     accumulate fp32
+ *   DWCONV_BF16  x, w bf16      bias float   y bf16     accumulate fp32
+ *   DWCONV_I8    x, w int8      bias int32   y int32    accumulate int32 (exact)
+ * The bias is in the accumulator type and is added once; partial sums are
+ * never rounded to the storage type before the end; fp16/bf16 outputs are
+ * rounded once, to nearest even, from the fp32 sum.
+ *
+ * Ownership: the caller allocates and owns every buffer (device memory).  The
+ * library allocates no device memory.  A handle holds host-side plan data
+ * only, is immutable after creation, and may be used from several host
+ * threads and on several streams at once.
+ *
+ * Errors: every function returns a status and never throws.  Nothing here
+ * synchronises the device.
+ */
+#ifndef DWCONV_H
+#define DWCONV_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DWCONV_F32 = 0,
+    DWCONV_F16 = 1,
+    DWCONV_BF16 = 2,
+    DWCONV_I8 = 3
+} dwconv_dtype_t;
+
+typedef enum {
+    DWCONV_OK = 0,
+    DWCONV_ERR_INVALID_ARG = 1,  /* bad shape, dtype, pointer or variant       */
+    DWCONV_ERR_UNSUPPORTED = 2,  /* valid operation this build cannot run      */
+    DWCONV_ERR_HIP = 3,          /* the HIP runtime reported an error          */
+    DWCONV_ERR_ALLOC = 4         /* host memory for the plan could not be had  */
+} dwconv_status_t;
+
+/* Kernel families.  AUTO lets the planner choose; the others force one (for
+ * testing and A/B timing) and make dwconv_create fail with
+ * DWCONV_ERR_UNSUPPORTED when that family cannot run the shape. */
+typedef enum {
+    DWCONV_VARIANT_AUTO = 0,
+    DWCONV_VARIANT_DIRECT = 1,   /* one lane per output element; any shape      */
+    DWCONV_VARIANT_ROWWIN = 2,   /* width-first register window, 16-B vectors   */
+    DWCONV_VARIANT_LDSTILE = 3,  /* LDS halo tile + register window             */
+    DWCONV_VARIANT_MFMA = 4      /* banded-filter GEMM on the matrix cores      */
+} dwconv_variant_t;
+
+typedef struct dwconv_plan *dwconv_handle_t;
+
+/* Validates the operation and builds a plan.  Touches no GPU state.
+ * Rejects (DWCONV_ERR_INVALID_ARG): out == NULL; N, H, W, C, FH, FW, stride
+ * or dilation < 1; pad < 0; an empty output (OH < 1 or OW < 1); an unknown
+ * dtype; tensors with 2^31 or more elements; for DWCONV_I8 a filter of more
+ * than 131071 taps (FH*FW*128*128 would no longer fit int32).  With DWCONV_I8
+ * the caller keeps bias + products inside int32; past it the sum wraps (two's
+ * complement).  On failure *out is set to NULL. */
+dwconv_status_t dwconv_create(dwconv_handle_t *out, int N, int H, int W, int C,
+                              int FH, int FW, int stride, int dilation, int pad,
+                              dwconv_dtype_t dtype);
+
+/* As dwconv_create, with the kernel family forced (DWCONV_VARIANT_AUTO is the
+ * same as dwconv_create). */
+dwconv_status_t dwconv_create_variant(dwconv_handle_t *out, int N, int H, int W,
+                                      int C, int FH, int FW, int stride,
+                                      int dilation, int pad, dwconv_dtype_t dtype,
+                                      dwconv_variant_t variant);
+
+/* Enqueues the forward pass on `stream` (0 = the null stream) and returns
+ * without waiting.  x, w, y: device pointers to the layouts above; bias:
+ * device pointer or NULL.  y must not overlap x, w or bias.  Any alignment is
+ * accepted (pointers that are not 16-byte aligned, or rows whose byte length
+ * is not a multiple of 16, make the planner fall back to a slower kernel
+ * family, never to an error).  Returns DWCONV_ERR_INVALID_ARG for a NULL
+ * handle, x, w or y, and DWCONV_ERR_HIP if the launch fails. */
+dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
+                           const void *bias, void *y, hipStream_t stream);
+
+/* Frees the plan.  NULL is a no-op. */
+dwconv_status_t dwconv_destroy(dwconv_handle_t h);
+
+/* Output extent of a plan. */
+dwconv_status_t dwconv_output_dims(dwconv_handle_t h, int *OH, int *OW);
+
+/* Kernel family the plan will launch for 16-byte aligned pointers, and a
+ * one-line description of its tiling (static strings owned by the library or
+ * the plan; valid until dwconv_destroy). */
+dwconv_variant_t dwconv_plan_variant(dwconv_handle_t h);
+const char *dwconv_plan_describe(dwconv_handle_t h);
+
+/* Static, human-readable name of a status. */
+const char *dwconv_status_string(dwconv_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DWCONV_H */

@@ -1,0 +1,125 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports every entry
+point the header declares, and validates arguments before touching the GPU.
+No test here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import depthwise_convolution_amd as dw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(dwconv_\w+)\s*\(", text))
+    return names
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert {"dwconv_create", "dwconv_fwd", "dwconv_destroy"} <= names
+    lib = ctypes.CDLL(dw.library_path)
+    for n in sorted(names):
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+        assert hasattr(dw, n), f"{n} has no Python binding of the same name"
+
+
+def test_status_strings():
+    assert dw.dwconv_status_string(0) == "ok"
+    assert dw.dwconv_status_string(1) == "invalid argument"
+    assert dw.dwconv_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("args", [
+    (0, 8, 8, 4, 3, 3, 1, 1, 1),     # N < 1
+    (1, 0, 8, 4, 3, 3, 1, 1, 1),     # H < 1
+    (1, 8, 8, 0, 3, 3, 1, 1, 1),     # C < 1
+    (1, 8, 8, 4, 0, 3, 1, 1, 1),     # FH < 1
+    (1, 8, 8, 4, 3, 3, 0, 1, 1),     # stride < 1
+    (1, 8, 8, 4, 3, 3, 1, 0, 1),     # dilation < 1
+    (1, 8, 8, 4, 3, 3, 1, 1, -1),    # pad < 0
+    (1, 2, 8, 4, 5, 3, 1, 1, 0),     # empty output (filter taller than input)
+    (1, 8, 8, 4, 3, 3, 1, 4, 0),     # dilated span exceeds the input
+    (65536, 256, 256, 64, 3, 3, 1, 1, 1),  # 2^38 elements
+])
+def test_create_rejects(args):
+    with pytest.raises(dw.DwconvError) as e:
+        dw.dwconv_create(*args, "f32")
+    assert e.value.status == 1
+
+
+def test_create_rejects_dtype_and_variant():
+    for bad in (4, -1, 17):
+        with pytest.raises(dw.DwconvError) as e:
+            dw.dwconv_create(1, 8, 8, 4, 3, 3, 1, 1, 1, bad)
+        assert e.value.status == 1
+    with pytest.raises(dw.DwconvError) as e:
+        dw.dwconv_create_variant(1, 8, 8, 4, 3, 3, 1, 1, 1, "f32", 9)
+    assert e.value.status == 1
+    # int8 filters whose products alone could overflow int32
+    with pytest.raises(dw.DwconvError):
+        dw.dwconv_create(1, 400, 400, 1, 363, 363, 1, 1, 181, "i8")
+
+
+def test_create_null_out_pointer():
+    lib = ctypes.CDLL(dw.library_path)
+    lib.dwconv_create.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 10
+    assert lib.dwconv_create(None, 1, 8, 8, 4, 3, 3, 1, 1, 1, 0) == 1
+
+
+def test_output_dims_and_plan():
+    h = dw.dwconv_create(16, 112, 112, 61, 5, 5, 2, 2, 4, "i8")
+    try:
+        assert dw.dwconv_output_dims(h) == (56, 56)
+        assert dw.dwconv_plan_variant(h) in dw.VARIANTS
+        assert dw.dwconv_plan_describe(h)
+    finally:
+        dw.dwconv_destroy(h)
+    h = dw.dwconv_create(1, 16, 16, 8, 3, 3, 1, 1, 1, "f32")
+    assert dw.dwconv_output_dims(h) == (16, 16)
+    dw.dwconv_destroy(h)
+    dw.dwconv_destroy(None)          # no-op
+
+
+def test_forced_variants():
+    # the direct family takes every shape
+    h = dw.dwconv_create_variant(2, 9, 7, 5, 4, 2, 3, 2, 1, "bf16", "direct")
+    assert dw.dwconv_plan_variant(h) == "direct"
+    dw.dwconv_destroy(h)
+    # a family that cannot run the shape is reported, not substituted
+    with pytest.raises(dw.DwconvError) as e:
+        dw.dwconv_create_variant(2, 9, 7, 5, 4, 2, 3, 2, 1, "bf16", "rowwin")
+    assert e.value.status == 2
+
+
+def test_fwd_argument_errors_before_any_launch():
+    lib = ctypes.CDLL(dw.library_path)
+    V = ctypes.c_void_p
+    lib.dwconv_fwd.argtypes = [V] * 6
+    h = dw.dwconv_create(1, 8, 8, 4, 3, 3, 1, 1, 1, "f32")
+    try:
+        fake = 0x1000
+        assert lib.dwconv_fwd(None, fake, fake, None, fake, None) == 1
+        assert lib.dwconv_fwd(h, None, fake, None, fake, None) == 1
+        assert lib.dwconv_fwd(h, fake, None, None, fake, None) == 1
+        assert lib.dwconv_fwd(h, fake, fake, None, None, None) == 1
+        lib.dwconv_output_dims.argtypes = [V, V, V]
+        assert lib.dwconv_output_dims(None, None, None) == 1
+    finally:
+        dw.dwconv_destroy(h)
+
+
+def test_one_hip_runtime_in_process():
+    """The library binds to the HIP/HSA runtime torch loaded: one copy of
+    each in the process, so torch's pointers and streams are valid in it."""
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {l.split()[-1] for l in maps if "libamdhip64" in l}
+    hsa = {l.split()[-1] for l in maps if "libhsa-runtime64" in l}
+    assert len(hip) == 1 and len(hsa) == 1, (hip, hsa)

@@ -1,0 +1,227 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Floating point must satisfy the elementwise bound |y - y_exact| <=
+1e-5 * sum|x*w| + 1e-6 on the value before the one final rounding to the
+output format (oracle/check.py); int8 -> int32 must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import depthwise_convolution_amd as dw
+import oracle
+from oracle import check
+import synth
+from synth import WORKLOADS, make_inputs
+
+from gpu_helpers import run, assert_matches_oracle, shape_of, say, DEV
+
+pytestmark = pytest.mark.gpu
+
+FAMILIES = ["auto", "direct", "rowwin", "ldstile", "mfma"]
+
+
+def supported(shape, fmt, variant):
+    try:
+        h = dw.dwconv_create_variant(*shape, fmt, variant)
+    except dw.DwconvError as e:
+        if e.status == 2:
+            return False
+        raise
+    dw.dwconv_destroy(h)
+    return True
+
+
+# ------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("name", ["tiny_f32_3x3", "mobilenet_f32_3x3", "convnext_f16_7x7",
+                                  "strided_i8_5x5"])
+def test_workload_full(name):
+    wl = WORKLOADS[name]
+    x, w, b = make_inputs(wl)
+    shape = shape_of(wl)
+    for fam in FAMILIES:
+        if fam != "auto" and not supported(shape, wl.dtype, fam):
+            continue
+        say(f"[gpu] workload {name} family {fam} shape {shape}")
+        y, used = run(x, w, b, shape, wl.dtype, fam, guard=4096)
+        rep = assert_matches_oracle(y, x, w, b, shape, wl.dtype, f"{name}/{fam}({used})")
+        say(f"      ok ({used}) {rep}")
+
+
+def test_workload_largekernel_sampled():
+    """32x56x56x128 bf16, 31x31: every output of the first and last image's
+    border rows and columns, plus 60000 random outputs, one by one."""
+    wl = WORKLOADS["largekernel_bf16_31x31"]
+    x, w, b = make_inputs(wl)
+    shape = shape_of(wl)
+    N, OH, OW, C = wl.N, 56, 56, wl.C
+    rng = np.random.default_rng(44)
+    idx = [rng.integers(0, N * OH * OW * C, size=60000)]
+    for n in (0, N - 1):
+        for oh in range(OH):
+            for ow in (0, 1, 14, 15, 16, 40, OW - 2, OW - 1):
+                idx.append(((n * OH + oh) * OW + ow) * C + np.arange(C))
+        for ow in range(OW):
+            for oh in (0, 15, OH - 1):
+                idx.append(((n * OH + oh) * OW + ow) * C + np.arange(C))
+    idx = np.unique(np.concatenate(idx))
+    ye, scale = oracle.points(x, w, b, wl.stride, wl.dilation, wl.pad, "bf16", idx)
+    for fam in FAMILIES:
+        if fam == "direct":
+            continue  # 12 G MACs one output per lane: slow, covered by the small cases
+        if fam != "auto" and not supported(shape, "bf16", fam):
+            continue
+        say(f"[gpu] largekernel family {fam}")
+        y, used = run(x, w, b, shape, "bf16", fam, guard=4096)
+        rep = check.assert_float(y.ravel()[idx], "bf16", ye, scale, f"largekernel/{used}")
+        say(f"      ok ({used}) {rep}")
+
+
+# ------------------------------------------------------- random small shapes
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16", "i8"])
+def test_random_small(fmt):
+    rng = np.random.default_rng({"f32": 1, "f16": 2, "bf16": 3, "i8": 4}[fmt])
+    for i in range(40):
+        wl = synth.random_small(rng, fmt)
+        x, w, b = make_inputs(wl)
+        shape = shape_of(wl)
+        for fam in FAMILIES:
+            if fam != "auto" and not supported(shape, fmt, fam):
+                continue
+            say(f"[gpu] random {fmt} #{i} {fam} shape {shape} bias={b is not None}")
+            y, used = run(x, w, b, shape, fmt, fam, guard=64)
+            assert_matches_oracle(y, x, w, b, shape, fmt, f"random {fmt} #{i} {used}")
+
+
+# Shapes that reach each family's fast path with ragged tails: widths that
+# are not multiples of any tile, channel counts one vector over a tile, one
+# output row/column, filters larger than the image, heavy padding.
+EDGE = [
+    (1, 16, 16, 8, 3, 3, 1, 1, 1),
+    (2, 9, 57, 132, 3, 3, 1, 1, 1),
+    (1, 5, 5, 128, 3, 3, 1, 1, 0),        # 3x3 output
+    (1, 1, 1, 64, 3, 3, 1, 1, 1),         # 1x1 image
+    (1, 3, 3, 32, 7, 7, 1, 1, 3),         # filter larger than the image
+    (2, 23, 17, 96, 7, 7, 1, 1, 3),
+    (1, 40, 70, 104, 7, 7, 1, 1, 3),
+    (1, 20, 20, 16, 31, 31, 1, 1, 15),
+    (1, 64, 61, 24, 31, 31, 1, 1, 15),
+    (2, 33, 35, 64, 5, 5, 2, 2, 4),
+    (1, 30, 30, 32, 3, 3, 2, 1, 1),
+    (1, 8, 8, 16, 3, 3, 1, 1, 6),         # padding wider than the filter
+    (3, 14, 14, 48, 5, 5, 1, 1, 2),
+]
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16", "i8"])
+def test_edge_shapes(fmt):
+    rng = np.random.default_rng(5)
+    for shape in EDGE:
+        N, H, W, C, FH, FW, S, D, P = shape
+        wl = synth.Workload("edge", fmt, N, H, W, C, FH, FW, S, D, P,
+                            ("int", -128, 127) if fmt == "i8" else ("normal", 0.0, 1.0),
+                            ("int", -128, 127) if fmt == "i8" else ("normal", 0.0, 1.0 / (FH * FW)),
+                            ("int", -2**15, 2**15) if fmt == "i8" else ("uniform", -0.1, 0.1),
+                            int(rng.integers(0, 2**31)))
+        x, w, b = make_inputs(wl)
+        for fam in FAMILIES:
+            if fam != "auto" and not supported(shape, fmt, fam):
+                continue
+            say(f"[gpu] edge {fmt} {fam} shape {shape}")
+            y, used = run(x, w, b, shape, fmt, fam, guard=256)
+            assert_matches_oracle(y, x, w, b, shape, fmt, f"edge {fmt} {shape} {used}")
+
+
+# ----------------------------------------------------- exact special cases
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16", "i8"])
+def test_delta_identity_bit_exact(fmt):
+    """A centred one-hot filter with unit stride and same padding copies x to
+    y exactly (no bias), in every family and dtype."""
+    rng = np.random.default_rng(6)
+    for F in (3, 5, 7, 31):
+        shape = (2, 19, 23, 64, F, F, 1, 1, F // 2)
+        wl = synth.Workload("delta", fmt, 2, 19, 23, 64, F, F, 1, 1, F // 2,
+                            ("int", -128, 127) if fmt == "i8" else ("normal", 0.0, 1.0),
+                            ("ones",), None, int(rng.integers(0, 2**31)))
+        x, _, _ = make_inputs(wl)
+        w = np.zeros((F, F, 64), x.dtype)
+        w[F // 2, F // 2, :] = 1 if fmt == "i8" else synth.to_storage(np.ones(64), fmt)
+        for fam in FAMILIES:
+            if fam != "auto" and not supported(shape, fmt, fam):
+                continue
+            say(f"[gpu] delta {fmt} F={F} {fam}")
+            y, used = run(x, w, None, shape, fmt, fam)
+            want = x.astype(np.int32) if fmt == "i8" else x
+            assert np.array_equal(y.view(np.uint8), np.ascontiguousarray(want).view(np.uint8)), \
+                f"delta {fmt} F={F} {used}"
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16", "i8"])
+def test_box_counts_exact(fmt):
+    """x = 1, w = 1, no bias: each output is the number of taps inside the
+    image, exactly (rounded once to the output format: 961 -> 960 in bf16)."""
+    for shape in [(1, 16, 16, 8, 3, 3, 1, 1, 1), (2, 40, 37, 64, 31, 31, 1, 1, 15),
+                  (1, 56, 56, 96, 7, 7, 1, 1, 3), (1, 33, 31, 16, 5, 5, 2, 2, 4)]:
+        N, H, W, C, FH, FW, S, D, P = shape
+        one = np.int8(1) if fmt == "i8" else synth.to_storage(np.ones(1), fmt)[0]
+        x = np.full((N, H, W, C), one)
+        w = np.full((FH, FW, C), one)
+        OH = oracle.out_dim(H, FH, S, D, P)
+        OW = oracle.out_dim(W, FW, S, D, P)
+        cnt_h = np.array([sum(0 <= o * S - P + f * D < H for f in range(FH)) for o in range(OH)])
+        cnt_w = np.array([sum(0 <= o * S - P + f * D < W for f in range(FW)) for o in range(OW)])
+        cnt = (cnt_h[:, None] * cnt_w[None, :]).astype(np.float64)
+        want = np.broadcast_to(cnt[None, :, :, None], (N, OH, OW, C))
+        want = want.astype(np.int32) if fmt == "i8" else synth.to_storage(want, fmt)
+        for fam in FAMILIES:
+            if fam != "auto" and not supported(shape, fmt, fam):
+                continue
+            say(f"[gpu] box {fmt} {shape} {fam}")
+            y, used = run(x, w, None, shape, fmt, fam)
+            assert np.array_equal(y.view(np.uint8), np.ascontiguousarray(want).view(np.uint8)), \
+                f"box {fmt} {shape} {used}"
+
+
+# ------------------------------------------------ alignment, streams, repeats
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "i8"])
+def test_misaligned_pointers_fall_back(fmt):
+    """Tensors that start one element past a 16-byte boundary still give the
+    right answer (the direct family runs them)."""
+    shape = (2, 12, 13, 64, 3, 3, 1, 1, 1)
+    wl = synth.Workload("mis", fmt, *shape,
+                        ("int", -128, 127) if fmt == "i8" else ("normal", 0.0, 1.0),
+                        ("int", -128, 127) if fmt == "i8" else ("normal", 0.0, 1 / 9),
+                        ("int", -100, 100) if fmt == "i8" else ("uniform", -0.1, 0.1), 77)
+    x, w, b = make_inputs(wl)
+    from gpu_helpers import to_dev, y_torch_dtype, y_to_host
+    xd = to_dev(np.concatenate([x.ravel()[:1], x.ravel()]), fmt)[1:]
+    wd = to_dev(np.concatenate([w.ravel()[:1], w.ravel()]), fmt)[1:]
+    bd = to_dev(np.concatenate([b[:1], b]), "f32")[1:]
+    h = dw.dwconv_create(*shape, fmt)
+    try:
+        OH, OW = dw.dwconv_output_dims(h)
+        yb = torch.empty(2 * OH * OW * 64 + 1, dtype=y_torch_dtype(fmt), device=DEV)
+        y = yb[1:]
+        say(f"[gpu] misaligned {fmt}")
+        dw.dwconv_fwd(h, xd.data_ptr(), wd.data_ptr(), bd.data_ptr(), y.data_ptr(), None)
+        torch.cuda.synchronize()
+        yh = y_to_host(y, fmt).reshape(2, OH, OW, 64)
+    finally:
+        dw.dwconv_destroy(h)
+    assert_matches_oracle(yh, x, w, b, shape, fmt, f"misaligned {fmt}")
+
+
+def test_repeat_runs_bitwise_identical_and_stream():
+    wl = WORKLOADS["convnext_f16_7x7"]
+    x, w, b = make_inputs(wl, n=4)
+    shape = (4,) + shape_of(wl)[1:]
+    say("[gpu] repeat determinism on a side stream")
+    y1, _ = run(x, w, b, shape, "f16")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y2, _ = run(x, w, b, shape, "f16")
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
