@@ -11,10 +11,13 @@ from an earlier step, the bench keeps several copies of x and y, at least
 1 GiB in all, and steps walk through them in turn.
 
 Prints one JSON line:
-  value           algorithmic GB/s of the whole timed region (bytes / wall time)
-  roofline        the kernel's own duration (HIP events around each launch,
-                  averaged) against MI355X's 8 TB/s HBM, plus the HBM traffic
-                  the rocprofv3 counters measured for this kernel (or null)
+  value           algorithmic GB/s of K back-to-back steps (bytes / time per step)
+  roofline        the kernel's own duration (a second pass of K steps with HIP
+                  events around each launch, averaged) against MI355X's 8 TB/s
+                  HBM, plus the HBM bytes per launch that the rocprofv3
+                  FETCH_SIZE / WRITE_SIZE counters measured for this kernel,
+                  scaled by what they read for a plain copy of known size
+                  (profiles/counters.json; null once the sources changed)
   cpu_baseline    the CPU oracle timed on this host's cores on a sample
 Algorithmic bytes count x, w, bias and y once each; halo re-reads and
 padding are not counted.  FLOPs are 2 per tap per output.
@@ -79,6 +82,31 @@ def stored_traffic(workload, variant):
     return rec.get("hbm_bytes_per_launch")
 
 
+def copy_ceiling(torch, dev, stream, nbytes, sets, K, warmup):
+    """A plain device-to-device copy that reads nbytes/2 and writes nbytes/2
+    (the same total as one forward pass), over the same number of rotating
+    buffer sets, timed the same way.  It is the practical HBM ceiling on this
+    GPU, and the known-size kernel that calibrates the traffic counters."""
+    half = nbytes // 2
+    src = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(sets)]
+    dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(sets)]
+    for t in src:
+        t.fill_(1)
+    for i in range(warmup):
+        dst[i % sets].copy_(src[i % sets])
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev0[i].record(stream)
+        dst[i % sets].copy_(src[i % sets])
+        ev1[i].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(z) for a, z in zip(ev0, ev1)]))
+    return {"gbs": round(2 * half / (ms * 1e-3) / 1e9, 2), "avg_us": round(ms * 1e3, 3),
+            "bytes": 2 * half, "kind": "torch copy_ (device to device)"}
+
+
 def cpu_baseline(wl, x, w, b, budget_s=20.0):
     """The CPU oracle (test infrastructure, untuned) on this host's cores.
     Sample: whole images of the same workload, as many as fit the budget
@@ -109,6 +137,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--variant", default="auto")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-copy", action="store_true",
+                    help="skip the device-to-device copy ceiling measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
@@ -158,21 +188,29 @@ def main():
     for i in range(args.warmup):
         dw.dwconv_fwd(h, xs[i % sets], wd, bd, ys[i % sets], stream)
     K = args.steps
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    # pass 1: K steps back to back, bracketed by synchronisation (one GPU:
+    # no barrier needed) -> whole-job throughput
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
-        ev0[i].record(stream)
         dw.dwconv_fwd(h, xs[i % sets], wd, bd, ys[i % sets], stream)
-        ev1[i].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     total_ms = start.elapsed_time(end)
+    # pass 2: the same K steps with a HIP event pair around every launch, on
+    # the launch stream -> the kernel's own average duration
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev0[i].record(stream)
+        dw.dwconv_fwd(h, xs[i % sets], wd, bd, ys[i % sets], stream)
+        ev1[i].record(stream)
+    torch.cuda.synchronize()
     kern_ms = np.array([a.elapsed_time(z) for a, z in zip(ev0, ev1)])
     dw.dwconv_destroy(h)
 
@@ -185,6 +223,14 @@ def main():
           f"{np.median(kern_ms) * 1e3:.2f}, min {kern_ms.min() * 1e3:.2f}); step "
           f"{ms_per_step * 1e3:.2f} us; host wall {t_wall * 1e3 / K:.2f} us/step",
           file=sys.stderr, flush=True)
+
+    copy = None
+    if not args.no_copy:
+        copy = copy_ceiling(torch, dev, stream, nbytes, sets, K, args.warmup)
+        print(f"[bench] copy ceiling: {copy['gbs']:.0f} GB/s "
+              f"({copy['avg_us']:.2f} us per {nbytes / 2e6:.1f} MB read + write)",
+              file=sys.stderr, flush=True)
+    del xs, ys
 
     cpu = None
     if not args.no_cpu:
@@ -217,6 +263,8 @@ def main():
                    "median_us": round(float(np.median(kern_ms)) * 1e3, 3),
                    "min_us": round(float(kern_ms.min()) * 1e3, 3),
                    "buffer_sets": sets},
+        "copy_ceiling": copy,
+        "frac_of_copy": None if copy is None else round(achieved / copy["gbs"], 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -23,6 +23,8 @@
 #include "plan.h"
 
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 namespace dw {
 
@@ -62,6 +64,51 @@ __device__ __forceinline__ void store_vec(E *dst, const E (&src)[VEC]) {
     }
 }
 
+// Loads the NWIN-pixel input run of one row starting at column iw0 and widens
+// it to the accumulator type.  Columns outside the image read as zero: their
+// address is clamped to column 0 (always inside the row, so the load is in
+// bounds and branch-free) and the value is replaced by zero.
+template <class DT, int VEC, int NWIN>
+__device__ __forceinline__ void load_window(typename DT::Acc (&xw)[NWIN][VEC],
+                                            const typename DT::X *xr, int iw0, int W,
+                                            int C) {
+    using X = typename DT::X;
+    X e[NWIN][VEC];
+#pragma unroll
+    for (int j = 0; j < NWIN; ++j) {
+        const int iw = iw0 + j;
+        const int iwc = (unsigned)iw < (unsigned)W ? iw : 0;
+        load_vec<X, VEC>(e[j], xr + (long long)iwc * C);
+    }
+#pragma unroll
+    for (int j = 0; j < NWIN; ++j) {
+        const bool ok = (unsigned)(iw0 + j) < (unsigned)W;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) xw[j][v] = ok ? DT::widen(e[j][v]) : typename DT::Acc(0);
+    }
+}
+
+template <class Y, int VEC, bool NT>
+__device__ __forceinline__ void store_out(Y *dst, const Y (&o)[VEC]) {
+    if constexpr (NT) {
+        // y is never read back by this kernel: stream it past the caches
+        constexpr int B = sizeof(Y) * VEC;
+        static_assert(B % 16 == 0, "whole 16-byte vectors");
+        using V = typename VecT<16>::T;
+#pragma unroll
+        for (int k = 0; k < B / 16; ++k) {
+            V v;
+            __builtin_memcpy(&v, reinterpret_cast<const char *>(o) + 16 * k, 16);
+            __builtin_nontemporal_store(v, reinterpret_cast<V *>(dst) + k);
+        }
+    } else {
+        store_vec<Y, VEC>(dst, o);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row window: one output row per lane, any stride and dilation.
+// ---------------------------------------------------------------------------
 template <class DT, int VEC, int FW, int TM, int S, int D>
 __global__ void __launch_bounds__(256)
 k_rowwin(const typename DT::X *__restrict__ x, const typename DT::X *__restrict__ w,
@@ -100,21 +147,8 @@ k_rowwin(const typename DT::X *__restrict__ x, const typename DT::X *__restrict_
         if ((unsigned)ih >= (unsigned)s.H) continue;  // generated zero rows
         const X *xr = x + ((n * s.H + ih) * (long long)s.W) * s.C + c0;
 
-        // input run of this filter row, widened once
-        Acc xw[NWIN][VEC];
-#pragma unroll
-        for (int j = 0; j < NWIN; ++j) {
-            const int iw = iw0 + j;
-            if ((unsigned)iw < (unsigned)s.W) {
-                X e[VEC];
-                load_vec<X, VEC>(e, xr + (long long)iw * s.C);
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) xw[j][v] = DT::widen(e[v]);
-            } else {
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) xw[j][v] = Acc(0);
-            }
-        }
+        Acc xw[NWIN][VEC];  // input run of this filter row, widened once
+        load_window<DT, VEC, NWIN>(xw, xr, iw0, s.W, s.C);
         Acc wt[FW][VEC];
 #pragma unroll
         for (int fw = 0; fw < FW; ++fw) {
@@ -148,9 +182,181 @@ k_rowwin(const typename DT::X *__restrict__ x, const typename DT::X *__restrict_
             typename DT::Y o[VEC];
 #pragma unroll
             for (int v = 0; v < VEC; ++v) o[v] = DT::narrow(acc[t][v]);
-            store_vec<typename DT::Y, VEC>(yr + (long long)t * s.C, o);
+            store_out<typename DT::Y, VEC, false>(yr + (long long)t * s.C, o);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Column stream (stride 1): each lane walks TH output rows of its TM x VEC
+// strip.  Every input row of the strip's halo -- TH + (FH-1)D rows -- is
+// loaded once; for each filter row fh it feeds output row o = i - fh*D, whose
+// fresh row partial is added to that output's running sum.  Output row o
+// starts at input row i = o (fh = 0, where the bias seeds it) and is complete
+// and stored after input row o + (FH-1)D, so only FH rows of accumulators
+// are live at any time (the loop is fully unrolled, indices are constants).
+// The whole FH x FW x VEC filter slice stays in registers.  Every output is
+// still one bias plus FH unrounded row partials; only the order in which the
+// row partials are added depends on the walk direction.
+//
+// Loads run PF rows ahead of the arithmetic: the raw run of row i + PF is
+// requested before row i is used, so each wavefront keeps PF + 1 rows of
+// loads in flight instead of waiting on every row.  Rows and columns outside
+// the image are fetched from a clamped in-bounds address and zeroed by a
+// select, so the stream has no divergent branches.
+// ---------------------------------------------------------------------------
+template <class E, int VEC>
+__device__ __forceinline__ void load_vec_nt(E (&dst)[VEC], const E *src) {
+    using V = typename VecT<sizeof(E) * VEC>::T;
+    V v = __builtin_nontemporal_load(reinterpret_cast<const V *>(src));
+    __builtin_memcpy(dst, &v, sizeof(V));
+}
+
+template <class X, int VEC, int NWIN, bool NTL>
+__device__ __forceinline__ void fetch_run(X (&e)[NWIN][VEC], const X *xn, int ih, int H,
+                                          int iw0, int W, int C) {
+    const int ihc = (unsigned)ih < (unsigned)H ? ih : 0;
+    const X *xr = xn + (long long)ihc * W * C;
+#pragma unroll
+    for (int j = 0; j < NWIN; ++j) {
+        const int iw = iw0 + j;
+        const int iwc = (unsigned)iw < (unsigned)W ? iw : 0;
+        if constexpr (NTL)
+            load_vec_nt<X, VEC>(e[j], xr + (long long)iwc * C);
+        else
+            load_vec<X, VEC>(e[j], xr + (long long)iwc * C);
+    }
+}
+
+// One strip's walk over its input rows, top-down (UP = false) or bottom-up.
+// Bottom-up visits input row i = NROW-1 .. 0; output row o then receives its
+// filter rows in the order fh = FH-1 .. 0, starts (bias) at fh = FH-1 and is
+// stored after fh = 0.
+template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, bool NTL,
+          bool UP>
+__device__ __forceinline__ void colstream_walk(const typename DT::X *xn,
+                                               const typename DT::Acc (&wt)[FH][FW][VEC],
+                                               const typename DT::Acc (&b0)[VEC],
+                                               typename DT::Y *yn, const Shape &s, int ih0,
+                                               int iw0, int oh0, int ow0) {
+    using X = typename DT::X;
+    using Acc = typename DT::Acc;
+    using Y = typename DT::Y;
+    constexpr int NWIN = TM + (FW - 1) * D;
+    constexpr int NROW = TH + (FH - 1) * D;
+    constexpr int RING = PF + 1;
+    // k-th visited row
+    auto row_of = [](int k) { return UP ? NROW - 1 - k : k; };
+
+    X raw[RING][NWIN][VEC];
+#pragma unroll
+    for (int k = 0; k < PF && k < NROW; ++k)
+        fetch_run<X, VEC, NWIN, NTL>(raw[k % RING], xn, ih0 + row_of(k), s.H, iw0, s.W, s.C);
+
+    Acc acc[TH][TM][VEC];
+#pragma unroll
+    for (int k = 0; k < NROW; ++k) {
+        const int i = row_of(k);
+        if (k + PF < NROW)
+            fetch_run<X, VEC, NWIN, NTL>(raw[(k + PF) % RING], xn, ih0 + row_of(k + PF), s.H, iw0,
+                                    s.W, s.C);
+        const bool row_ok = (unsigned)(ih0 + i) < (unsigned)s.H;
+        Acc xw[NWIN][VEC];
+#pragma unroll
+        for (int j = 0; j < NWIN; ++j) {
+            const bool ok = row_ok && (unsigned)(iw0 + j) < (unsigned)s.W;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v)
+                xw[j][v] = ok ? DT::widen(raw[k % RING][j][v]) : Acc(0);
+        }
+#pragma unroll
+        for (int q = 0; q < FH; ++q) {
+            const int fh = UP ? FH - 1 - q : q;
+            const int o = i - fh * D;
+            if (o < 0 || o >= TH) continue;
+            Acc part[TM][VEC];
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) part[t][v] = Acc(0);
+#pragma unroll
+            for (int fw = 0; fw < FW; ++fw)
+#pragma unroll
+                for (int t = 0; t < TM; ++t)
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v)
+                        part[t][v] = mac<Acc>(part[t][v], xw[t + fw * D][v], wt[fh][fw][v]);
+            const bool first = UP ? fh == FH - 1 : fh == 0;
+            const bool last = UP ? fh == 0 : fh == FH - 1;
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v)
+                    acc[o][t][v] = (first ? b0[v] : acc[o][t][v]) + part[t][v];
+            if (last && oh0 + o < s.OH) {
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    if (ow0 + t < s.OW) {
+                        Y ov[VEC];
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) ov[v] = DT::narrow(acc[o][t][v]);
+                        store_out<Y, VEC, NT>(yn + ((long long)o * s.OW + t) * s.C, ov);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Neighbouring strips share (FH-1)D input rows.  Strips walk in alternating
+// directions, so that the two strips on either side of every boundary reach
+// the shared rows at about the same time (both at the start of their walk, or
+// both at the end) and the second request finds them in L2.
+template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, bool NTL>
+__global__ void __launch_bounds__(256)
+k_colstream(const typename DT::X *__restrict__ x, const typename DT::X *__restrict__ w,
+            const typename DT::Bias *__restrict__ bias, typename DT::Y *__restrict__ y,
+            Shape s, int ncv, int owg_n, int ohg_n, long long total) {
+    using X = typename DT::X;
+    using Acc = typename DT::Acc;
+
+    const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
+    const long long g = (long long)b * blockDim.x + threadIdx.x;
+    if (g >= total) return;
+    const int cv = (int)(g % ncv);
+    long long r = g / ncv;
+    const int owg = (int)(r % owg_n);
+    r /= owg_n;
+    const int ohg = (int)(r % ohg_n);
+    const long long n = r / ohg_n;
+    const int c0 = cv * VEC;
+    const int ow0 = owg * TM;
+    const int oh0 = ohg * TH;
+    const int iw0 = ow0 - s.P;
+    const int ih0 = oh0 - s.P;
+    const X *xn = x + (n * s.H) * (long long)s.W * s.C + c0;
+
+    Acc wt[FH][FW][VEC];
+#pragma unroll
+    for (int fh = 0; fh < FH; ++fh)
+#pragma unroll
+        for (int fw = 0; fw < FW; ++fw) {
+            X e[VEC];
+            load_vec<X, VEC>(e, w + ((long long)fh * FW + fw) * s.C + c0);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) wt[fh][fw][v] = DT::widen(e[v]);
+        }
+    Acc b0[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) b0[v] = bias ? bias[c0 + v] : Acc(0);
+
+    typename DT::Y *yn = y + ((n * s.OH + oh0) * (long long)s.OW + ow0) * s.C + c0;
+    if (ohg & 1)
+        colstream_walk<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL, true>(xn, wt, b0, yn, s, ih0, iw0,
+                                                                  oh0, ow0);
+    else
+        colstream_walk<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL, false>(xn, wt, b0, yn, s, ih0, iw0,
+                                                                   oh0, ow0);
 }
 
 template <class DT, int VEC, int FW, int TM, int S, int D>
@@ -164,15 +370,39 @@ static hipError_t launch_rowwin(const Plan &p, const void *x, const void *w,
     return hipGetLastError();
 }
 
-struct RowwinEntry {
-    int dtype, fw, s, d, vec, tm;
+template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, bool NTL>
+static hipError_t launch_colstream(const Plan &p, const void *x, const void *w,
+                                   const void *bias, void *y, hipStream_t st) {
+    int ohg_n = (p.s.OH + TH - 1) / TH;
+    long long total = (long long)p.aux0 * p.aux1 * ohg_n * p.s.N;
+    hipLaunchKernelGGL((k_colstream<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL>), dim3(p.grid),
+                       dim3(p.block), 0, st, (const typename DT::X *)x,
+                       (const typename DT::X *)w, (const typename DT::Bias *)bias,
+                       (typename DT::Y *)y, p.s, p.aux0, p.aux1, ohg_n, total);
+    return hipGetLastError();
+}
+
+// Compiled tilings.  th == 0: row window (any stride); th > 0: column stream
+// of th rows (stride 1, FH fixed at compile time).  The first entry that
+// matches a shape is the planner's choice; DWCONV_TILE="TMxTH[nt]" picks
+// another compiled entry for the same filter (tuning sweeps).
+struct RegTile {
+    int dtype, fh, fw, s, d, vec, tm, th, pf, nt, ntl;
     LaunchFn fn;
 };
 
 #define RW(DTE, DTT, FW_, S_, D_, VEC_, TM_) \
-    {DTE, FW_, S_, D_, VEC_, TM_, launch_rowwin<DTT, VEC_, FW_, TM_, S_, D_>}
+    {DTE, 0, FW_, S_, D_, VEC_, TM_, 0, 0, 0, 0, launch_rowwin<DTT, VEC_, FW_, TM_, S_, D_>}
+#define CS(DTE, DTT, FH_, FW_, D_, VEC_, TM_, TH_, PF_, NT_, NTL_) \
+    {DTE, FH_, FW_, 1, D_, VEC_, TM_, TH_, PF_, NT_, NTL_,        \
+     launch_colstream<DTT, VEC_, FH_, FW_, TM_, TH_, D_, PF_, NT_, NTL_>}
 
-static const RowwinEntry kRowwin[] = {
+static const RegTile kTiles[] = {
+    CS(DT_F32, F32, 3, 3, 1, 4, 4, 14, 2, 1, 0),
+    CS(DT_F32, F32, 3, 3, 1, 4, 2, 28, 2, 1, 0),
+    CS(DT_F32, F32, 3, 3, 1, 4, 4, 8, 2, 1, 0),
+    CS(DT_F16, F16, 3, 3, 1, 8, 2, 14, 2, 1, 0),
+    CS(DT_BF16, BF16, 3, 3, 1, 8, 2, 14, 2, 1, 0),
     RW(DT_F32, F32, 3, 1, 1, 4, 8),
     RW(DT_F32, F32, 5, 1, 1, 4, 8),
     RW(DT_F32, F32, 7, 1, 1, 4, 4),
@@ -188,32 +418,64 @@ static const RowwinEntry kRowwin[] = {
     RW(DT_I8, I8, 5, 2, 2, 4, 2),
 };
 #undef RW
+#undef CS
+
+static bool tile_matches(const RegTile &k, const Plan &p) {
+    if (k.dtype != p.dtype || k.fw != p.s.FW || k.s != p.s.S || k.d != p.s.D) return false;
+    if (k.th > 0 && k.fh != p.s.FH) return false;
+    return p.s.C % k.vec == 0;  // every pixel a whole number of vectors
+}
 
 bool plan_rowwin(Plan &p) {
-    const RowwinEntry *e = nullptr;
-    for (const auto &k : kRowwin)
-        if (k.dtype == p.dtype && k.fw == p.s.FW && k.s == p.s.S && k.d == p.s.D) {
-            e = &k;
-            break;
+    const RegTile *e = nullptr;
+    // DWCONV_TILE="TMxTH[pPF[flags]]", flags: n = non-temporal y stores,
+    // l = non-temporal x loads (a tuning hook; the table order is the default)
+    int want_tm = 0, want_th = -1, want_pf = -1, want_nt = -1, want_ntl = -1;
+    if (const char *env = getenv("DWCONV_TILE")) {
+        char rest[8] = {0};
+        int got = sscanf(env, "%dx%dp%d%7s", &want_tm, &want_th, &want_pf, rest);
+        if (got < 2) want_th = -1;
+        if (got >= 3) {
+            want_nt = strchr(rest, 'n') != nullptr;
+            want_ntl = strchr(rest, 'l') != nullptr;
         }
+    }
+    for (const auto &k : kTiles) {
+        if (!tile_matches(k, p)) continue;
+        if (want_th >= 0 && (k.tm != want_tm || k.th != want_th)) continue;
+        if (want_pf >= 0 && k.pf != want_pf) continue;
+        if (want_nt >= 0 && k.nt != want_nt) continue;
+        if (want_ntl >= 0 && k.ntl != want_ntl) continue;
+        e = &k;
+        break;
+    }
+    if (!e && want_th >= 0) return false;  // asked for a tiling that is not compiled
     if (!e) return false;
-    if (p.s.C % e->vec != 0) return false;  // every pixel a whole number of vectors
     int ncv = p.s.C / e->vec;
     int owg_n = (p.s.OW + e->tm - 1) / e->tm;
-    long long total = (long long)ncv * owg_n * p.s.N * p.s.OH;
+    long long rows = e->th > 0 ? (long long)(p.s.OH + e->th - 1) / e->th : p.s.OH;
+    long long total = (long long)ncv * owg_n * rows * p.s.N;
     long long blocks = (total + 255) / 256;
     if (blocks >= (1LL << 31)) return false;
     p.variant = V_ROWWIN;
     p.vec = e->vec;
     p.tm = e->tm;
+    p.th = e->th;
     p.block = 256;
     p.grid = (uint32_t)blocks;
     p.aux0 = ncv;
     p.aux1 = owg_n;
     p.launch = e->fn;
-    snprintf(p.desc, sizeof(p.desc),
-             "rowwin: VEC=%d ch/lane, TM=%d outputs/lane, FW=%d S=%d D=%d, %u x %d",
-             e->vec, e->tm, e->fw, e->s, e->d, p.grid, p.block);
+    if (e->th > 0)
+        snprintf(p.desc, sizeof(p.desc),
+                 "colstream: VEC=%d ch/lane, TM=%d x TH=%d outputs/lane, %dx%d D=%d, "
+                 "prefetch %d rows%s%s, %u x %d",
+                 e->vec, e->tm, e->th, e->fh, e->fw, e->d, e->pf,
+                 e->nt ? ", nt stores" : "", e->ntl ? ", nt loads" : "", p.grid, p.block);
+    else
+        snprintf(p.desc, sizeof(p.desc),
+                 "rowwin: VEC=%d ch/lane, TM=%d outputs/lane, FW=%d S=%d D=%d, %u x %d",
+                 e->vec, e->tm, e->fw, e->s, e->d, p.grid, p.block);
     return true;
 }
 

@@ -225,3 +225,37 @@ def test_repeat_runs_bitwise_identical_and_stream():
     with torch.cuda.stream(s):
         y2, _ = run(x, w, b, shape, "f16")
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+# ------------------------------------------------ every compiled tiling
+
+REG_TILES = {
+    "f32": ["4x14p2n", "2x28p2n", "4x8p2n"],
+    "f16": ["2x14p2n"],
+    "bf16": ["2x14p2n"],
+}
+
+
+@pytest.mark.parametrize("fmt", sorted(REG_TILES))
+def test_each_column_stream_tiling(fmt, monkeypatch):
+    """Each compiled column-stream tiling (picked through the DWCONV_TILE
+    tuning hook) against the oracle, on shapes with ragged row and column
+    strips, an image shorter than a strip, and a batch."""
+    rng = np.random.default_rng(9)
+    shapes = [(2, 30, 19, 64, 3, 3, 1, 1, 1), (1, 5, 57, 32, 3, 3, 1, 1, 1),
+              (3, 17, 16, 128, 3, 3, 1, 1, 0), (1, 56, 56, 128, 3, 3, 1, 1, 2)]
+    for tile in REG_TILES[fmt]:
+        monkeypatch.setenv("DWCONV_TILE", tile)
+        for shape in shapes:
+            N, H, W, C, FH, FW, S, D, P = shape
+            wl = synth.Workload("tile", fmt, *shape, ("normal", 0.0, 1.0),
+                                ("normal", 0.0, 1 / 9), ("uniform", -0.1, 0.1),
+                                int(rng.integers(0, 2**31)))
+            x, w, b = make_inputs(wl)
+            say(f"[gpu] tile {tile} {fmt} shape {shape}")
+            y, used = run(x, w, b, shape, fmt, "rowwin", guard=512)
+            assert_matches_oracle(y, x, w, b, shape, fmt, f"tile {tile} {shape}")
+            h = dw.dwconv_create_variant(*shape, fmt, "rowwin")
+            desc = dw.dwconv_plan_describe(h)
+            dw.dwconv_destroy(h)
+            assert desc.startswith("colstream"), desc
