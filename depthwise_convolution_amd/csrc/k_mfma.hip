@@ -1,0 +1,424 @@
+// k_mfma.hip -- the "mfma" kernel family: depthwise convolution as banded GEMMs
+// on the gfx950 matrix cores (fp16 / bf16 in, fp32 accumulate; stride 1,
+// dilation 1).
+//
+// "Flash-DWC: Making Depthwise Convolution Compute-Efficient on GPUs",
+// section 4.2, turns each channel's GEMV into a small dense GEMM: the taps of
+// one filter fragment form a banded (Toeplitz) K x TM matrix whose column t
+// holds the taps starting at row t, and TM consecutive outputs of one row
+// become one length-K input vector; stacking several such vectors gives the
+// left operand.  The pages pack this into NVIDIA's m16n8k16 shape.  Here the
+// shape is gfx950's v_mfma_f32_16x16x32_{f16,bf16}:
+//
+//   D[i][t] += sum_k A[i][k] * B[k][t],   A 16x32, B 32x16, D 16x16 fp32
+//
+//   i  = one of 16 consecutive output rows (the 16 GEMVs)
+//   t  = one of 16 consecutive output columns (TM = 16)
+//   k  = one of 32 consecutive input columns (the input window, K = 32)
+//   B[k][t] = w[fh][16f + k - t] for 0 <= k - t < 16, else 0
+//
+// A filter row of FW taps is cut into ceil(FW/16) fragments of 16 taps
+// (31 taps -> 16 + 15).  Fragment f of output block b reads the input window
+// starting at padded column 16(b+f), so windows are 16-element aligned and
+// the window of (b, f=1) is the window of (b+1, f=0).  Only products inside
+// one channel are formed: every MFMA works on a single channel, as the pages'
+// one-GEMM-per-channel does.
+//
+// Workgroup (4 wavefronts): one image, a strip of 16*NB output columns and
+// CS channels, walked down 16 output rows at a time.  The input a row block
+// needs -- the halo span (16 + FH - 1) rows x 16(NB + NFRAG) columns of
+// "Tiles, halos and partial sums", with padding generated as zeros -- sits in
+// an LDS ring, channel-major, so that one 16-byte LDS read gives a lane its 8
+// consecutive columns of one channel (the A operand); each new block loads
+// only its 16 new rows.  The row pitch is padded by 8 elements, which puts the 16 rows an
+// A read touches on distinct banks.  The filter slice is staged once as
+// padded fragments -- 16 zeros, the fragment's 16 taps, 16 zeros -- so that
+// a lane's 8 entries of B, B[k][t] = tap k - t, are 8 consecutive elements at
+// a fixed per-lane offset, with the band's zeros built in; the lane reads
+// them as five aligned dwords and a 16-bit funnel shift.
+//
+// Filter rows are taken in pairs: the fragments of two filter rows
+// accumulate into a fresh fp32 partial (at most 2 x 32 products per MFMA
+// chain), which is then added to the running sum; the bias seeds that sum
+// once.  Worst-case rounding is then about (64 + FH/2) * 2^-24 * sum|x*w|.  The epilogue rounds once to
+// fp16/bf16 and goes through LDS so that the stores are whole channel
+// vectors of NHWC pixels, masked at the ragged right and bottom edges.
+#include "plan.h"
+
+#include <stdio.h>
+#include <stdlib.h>
+
+namespace dw {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <class DT>
+struct MfmaOp;
+template <>
+struct MfmaOp<F16> {
+    static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+};
+template <>
+struct MfmaOp<BF16> {
+    static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+// LDS geometry of one workgroup strip.
+template <int CS, int NB, int NFRAG>
+struct MfmaTile {
+    static constexpr int XW = 16 * (NB + NFRAG);  // staged input columns
+    static constexpr int PITCH = XW + 8;          // elements per staged row
+    static constexpr int ZLEN = 48;               // padded fragment length
+    static constexpr int NEW = NB + NFRAG;        // tile elements per thread, 16 rows
+};
+
+// Loads (into registers) the 16 padded input rows [R0, R0+16) of the strip:
+// element e = tid + 256u is row R0 + e / XW, column e % XW, CS channels.
+// Rows and columns outside the image are zeros.
+template <int CS, int XW, int NEW>
+__device__ __forceinline__ void strip_fetch(uint16_t (&v)[NEW][CS], const uint16_t *xn,
+                                            const Shape &s, int R0, int ow0, int tid) {
+#pragma unroll
+    for (int u = 0; u < NEW; ++u) {
+        const int e = tid + 256 * u;
+        const int ih = R0 + e / XW - s.P, iw = ow0 - s.P + e % XW;
+        if ((unsigned)ih < (unsigned)s.H && (unsigned)iw < (unsigned)s.W) {
+            const uint16_t *src = xn + ((long long)ih * s.W + iw) * s.C;
+            if constexpr (CS == 8) {
+                u32x4 q = *reinterpret_cast<const u32x4 *>(src);
+                __builtin_memcpy(v[u], &q, 16);
+            } else {
+                static_assert(CS == 4, "channel slice of 4 or 8");
+                uint2 q = *reinterpret_cast<const uint2 *>(src);
+                __builtin_memcpy(v[u], &q, 8);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < CS; ++c) v[u][c] = 0;
+        }
+    }
+}
+
+// Scatters fetched rows into the channel-major ring: padded row R lives in
+// slot R mod XR.
+template <int CS, int XW, int NEW>
+__device__ __forceinline__ void strip_store(const uint16_t (&v)[NEW][CS], uint16_t *xt,
+                                            int XR, int R0, int tid) {
+    constexpr int PITCH = XW + 8;
+#pragma unroll
+    for (int u = 0; u < NEW; ++u) {
+        const int e = tid + 256 * u;
+        int slot = R0 + e / XW;
+        slot -= (slot / XR) * XR;
+        const int L = e % XW;
+#pragma unroll
+        for (int c = 0; c < CS; ++c) xt[(c * XR + slot) * PITCH + L] = v[u][c];
+    }
+}
+
+// Workgroup (4 wavefronts): one image, one strip of 16*NB output columns and
+// CS channels, walking down the image 16 output rows at a time.  The
+// XR = 16 + FH - 1 padded input rows a row block needs sit in an LDS ring;
+// moving to the next block replaces the 16 oldest rows, whose loads are
+// issued before the current block's MFMAs so that their latency is hidden.
+template <class DT, int CS, int NB, int NFRAG>
+__global__ void __launch_bounds__(256)
+k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+       const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int ncs, int nct) {
+    using T = MfmaTile<CS, NB, NFRAG>;
+    constexpr int PITCH = T::PITCH, ZLEN = T::ZLEN, NEW = T::NEW;
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+
+    const int XR = 16 + s.FH - 1;                   // ring rows
+    uint16_t *xt = lds;                             // [CS][XR][PITCH]
+    uint16_t *zt = xt + CS * XR * PITCH;            // [CS][FH][NFRAG][ZLEN]
+    uint16_t *ot = zt + CS * s.FH * NFRAG * ZLEN;   // [16][16*NB][CS]
+
+    // workgroup -> (image, column strip, channel slice); channel slices vary
+    // fastest so that the slices of one strip run together and share the L2
+    // lines of its pixels
+    const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int cs = bid % ncs;
+    const uint32_t r = bid / ncs;
+    const int ct = r % nct;
+    const int n = r / nct;
+    const int c0 = cs * CS;
+    const int ow0 = ct * 16 * NB;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const uint16_t *xn = x + (long long)n * s.H * s.W * s.C + c0;
+    const int nrb = (s.OH + 15) / 16;
+
+    // ---- filter slice as padded fragments: fragment f of filter row fh of
+    // channel c is 16 zeros, its 16 taps (zero past FW), 16 zeros ----
+    {
+        const int zlen = CS * s.FH * NFRAG * ZLEN;
+        for (int e = 8 * tid; e < zlen; e += 8 * 256)   // zlen is a multiple of 8
+            *reinterpret_cast<u32x4 *>(zt + e) = (u32x4){0u, 0u, 0u, 0u};
+        __syncthreads();
+        // thread -> (fw = tid % 32, fh = tid / 32 + 8k): no divisions
+        const int fw = tid & 31;
+        if (fw < s.FW) {
+            const int f = fw >> 4, q = fw & 15;
+            for (int fh = tid >> 5; fh < s.FH; fh += 8) {
+                uint16_t v[CS];
+                const uint16_t *src = w + ((long long)fh * s.FW + fw) * s.C + c0;
+                if constexpr (CS == 8) {
+                    u32x4 t = *reinterpret_cast<const u32x4 *>(src);
+                    __builtin_memcpy(v, &t, 16);
+                } else {
+                    uint2 t = *reinterpret_cast<const uint2 *>(src);
+                    __builtin_memcpy(v, &t, 8);
+                }
+#pragma unroll
+                for (int c = 0; c < CS; ++c)
+                    zt[((c * s.FH + fh) * NFRAG + f) * ZLEN + 16 + q] = v[c];
+            }
+        }
+    }
+    // ---- prologue: padded rows [0, XR) of the first row block ----
+    for (int R0 = 0; R0 < XR; R0 += 16) {
+        uint16_t v[NEW][CS];
+        strip_fetch<CS, T::XW, NEW>(v, xn, s, R0, ow0, tid);
+        // rows past XR of the last chunk belong to the next block: skip them
+#pragma unroll
+        for (int u = 0; u < NEW; ++u) {
+            const int e = tid + 256 * u;
+            const int R = R0 + e / T::XW;
+            if (R < XR) {
+                const int L = e % T::XW;
+#pragma unroll
+                for (int c = 0; c < CS; ++c) xt[(c * XR + R) * PITCH + L] = v[u][c];
+            }
+        }
+    }
+
+    const int g = lane >> 4;    // k group of A/B, row group of D
+    const int t16 = lane & 15;  // row of A, column of B and D
+    // this lane's 8 entries of B are elements 16 + 8g - t16 .. +7 of the
+    // padded fragment: B[k][t] = tap k - t.  They are read from the dword
+    // holding element boff rounded down, shifted right by bsh bits.
+    const int boff = 16 + 8 * g - t16;
+    const int bsh = 16 * (boff & 1);
+    float bv[CS / 4];
+#pragma unroll
+    for (int ci = 0; ci < CS / 4; ++ci) bv[ci] = bias ? bias[c0 + wave + 4 * ci] : 0.0f;
+
+    for (int rb = 0; rb < nrb; ++rb) {
+        __syncthreads();  // ring rows of this block written; output tile free
+        // prefetch the 16 rows the next block adds (the rows this block
+        // needs are in the ring already)
+        const int Rn = 16 * rb + XR;
+        const bool more = rb + 1 < nrb;
+        uint16_t nv[NEW][CS];
+        if (more) strip_fetch<CS, T::XW, NEW>(nv, xn, s, Rn, ow0, tid);
+
+        // The wavefront's CS/4 channels are interleaved, and the operands
+        // of filter row fh+1 are read from LDS before the MFMAs of row fh
+        // issue (two register sets), so LDS latency hides behind MFMAs.
+        constexpr int NCH = CS / 4;
+        constexpr int NWIN = NB + NFRAG - 1;
+        f32x4 acc[NCH][NB];
+        const uint16_t *xc[NCH];
+        const uint16_t *zc[NCH];
+#pragma unroll
+        for (int ci = 0; ci < NCH; ++ci) {
+            const int c = wave + 4 * ci;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[ci][b] = (f32x4){bv[ci], bv[ci], bv[ci], bv[ci]};
+            xc[ci] = xt + c * XR * PITCH + 8 * g;
+            zc[ci] = zt + c * s.FH * NFRAG * ZLEN + (boff & ~1);
+        }
+        int slot0 = 16 * rb + t16;  // ring slot of this lane's row at fh = 0
+        slot0 -= (slot0 / XR) * XR;
+
+        struct Ops {
+            u32x4 A[NCH][NWIN];
+            u32x4 B[NCH][NFRAG];
+        };
+        auto load_ops = [&](Ops &o, int fh) {
+            int slot = slot0 + fh;
+            slot -= slot >= XR ? XR : 0;
+#pragma unroll
+            for (int ci = 0; ci < NCH; ++ci) {
+#pragma unroll
+                for (int f = 0; f < NFRAG; ++f) {
+                    // 8 taps from element boff: five dword-aligned reads, then
+                    // a 16-bit funnel shift when boff is odd (unaligned wide
+                    // LDS reads stall)
+                    const uint32_t *zd = reinterpret_cast<const uint32_t *>(
+                        zc[ci] + (fh * NFRAG + f) * ZLEN);
+                    uint32_t d[5];
+#pragma unroll
+                    for (int q = 0; q < 5; ++q) d[q] = zd[q];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        o.B[ci][f][q] = __builtin_amdgcn_alignbit(d[q + 1], d[q], bsh);
+                }
+                const uint16_t *xr = xc[ci] + slot * PITCH;
+#pragma unroll
+                for (int win = 0; win < NWIN; ++win)
+                    o.A[ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
+            }
+        };
+        auto mfmas = [&](const Ops &o, f32x4 (&part)[NCH][NB]) {
+#pragma unroll
+            for (int f = 0; f < NFRAG; ++f)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int ci = 0; ci < NCH; ++ci)
+                        part[ci][b] = MfmaOp<DT>::run(o.A[ci][b + f], o.B[ci][f], part[ci][b]);
+        };
+
+        // filter rows two at a time: each pair accumulates into a fresh fp32
+        // partial that is then added to the running sum
+        Ops o0, o1;
+        load_ops(o0, 0);
+        for (int fh0 = 0; fh0 < s.FH; fh0 += 2) {
+            f32x4 part[NCH][NB];
+#pragma unroll
+            for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) part[ci][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            const bool two = fh0 + 1 < s.FH;
+            if (two) load_ops(o1, fh0 + 1);
+            mfmas(o0, part);
+            if (fh0 + 2 < s.FH) load_ops(o0, fh0 + 2);
+            if (two) mfmas(o1, part);
+#pragma unroll
+            for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) acc[ci][b] += part[ci][b];
+        }
+        f32x4 (&res)[NCH][NB] = acc;
+
+        // ---- epilogue: round once, regroup through LDS into NHWC vectors ----
+#pragma unroll
+        for (int ci = 0; ci < CS / 4; ++ci) {
+            const int c = wave + 4 * ci;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int row = 4 * g + q, col = 16 * b + t16;
+                    ot[(row * 16 * NB + col) * CS + c] =
+                        __builtin_bit_cast(uint16_t, DT::narrow(res[ci][b][q]));
+                }
+        }
+        __syncthreads();  // block's ring rows consumed; output tile complete
+        const int oh0 = 16 * rb;
+        for (int e = tid; e < 16 * 16 * NB; e += 256) {
+            const int row = e / (16 * NB), col = e % (16 * NB);
+            const int oh = oh0 + row, ow = ow0 + col;
+            if (oh < s.OH && ow < s.OW) {
+                uint16_t *dst = y + (((long long)n * s.OH + oh) * s.OW + ow) * s.C + c0;
+                const uint16_t *src = ot + e * CS;
+                if constexpr (CS == 8)
+                    *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+                else
+                    *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(src);
+            }
+        }
+        if (more) strip_store<CS, T::XW, NEW>(nv, xt, XR, Rn, tid);
+    }
+}
+
+template <class DT, int CS, int NB, int NFRAG>
+static hipError_t launch_mfma(const Plan &p, const void *x, const void *w, const void *bias,
+                              void *y, hipStream_t st) {
+    if (p.lds_bytes > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG>), dim3(p.grid), dim3(256), p.lds_bytes, st,
+                       (const uint16_t *)x, (const uint16_t *)w, (const float *)bias,
+                       (uint16_t *)y, p.s, p.aux0, p.aux1);
+    return hipGetLastError();
+}
+
+template <int CS, int NB, int NFRAG>
+static int mfma_lds_bytes(const Shape &s) {
+    using T = MfmaTile<CS, NB, NFRAG>;
+    const int XR = 16 + s.FH - 1;
+    const int xt = CS * XR * T::PITCH;
+    const int zt = CS * s.FH * NFRAG * T::ZLEN;
+    const int ot = 16 * 16 * NB * CS;
+    return 2 * (xt + zt + ot);
+}
+
+struct MfmaEntry {
+    int dtype, cs, nb, nfrag;
+    LaunchFn fn;
+    int (*lds)(const Shape &);
+};
+
+#define MF(DTE, DTT, CS_, NB_, NF_) \
+    {DTE, CS_, NB_, NF_, launch_mfma<DTT, CS_, NB_, NF_>, mfma_lds_bytes<CS_, NB_, NF_>}
+
+// Wider channel slices first (16-byte loads, more work per tile); the
+// planner falls back to 4 channels when the 8-channel tile exceeds 64 KiB of
+// LDS (tall filters), to keep several workgroups per CU.
+static const MfmaEntry kMfma[] = {
+    MF(DT_F16, F16, 8, 4, 1),   MF(DT_F16, F16, 8, 4, 2),
+    MF(DT_F16, F16, 4, 4, 1),   MF(DT_F16, F16, 4, 4, 2),
+    MF(DT_BF16, BF16, 8, 4, 1), MF(DT_BF16, BF16, 8, 4, 2),
+    MF(DT_BF16, BF16, 4, 4, 1), MF(DT_BF16, BF16, 4, 4, 2),
+};
+#undef MF
+
+bool plan_mfma(Plan &p) {
+    if (p.dtype != DT_F16 && p.dtype != DT_BF16) return false;
+    if (p.s.S != 1 || p.s.D != 1) return false;
+    const int nfrag = (p.s.FW + 15) / 16;
+    // DWCONV_MFMA_CS=4|8 picks the channel slice (a tuning hook)
+    int want_cs = 0;
+    if (const char *env = getenv("DWCONV_MFMA_CS")) want_cs = atoi(env);
+    const MfmaEntry *e = nullptr;
+    int lds = 0;
+    for (const auto &k : kMfma) {
+        if (k.dtype != p.dtype || k.nfrag != nfrag || p.s.C % k.cs != 0) continue;
+        if (want_cs && k.cs != want_cs) continue;
+        const int need = k.lds(p.s);
+        const bool last = k.cs == 4 || want_cs;
+        if (need <= 64 * 1024 || (last && need <= 160 * 1024)) {
+            e = &k;
+            lds = need;
+            break;
+        }
+    }
+    if (!e) return false;  // tall filters: the tile does not fit LDS
+    const int ncs = p.s.C / e->cs;
+    const int nct = (p.s.OW + 16 * e->nb - 1) / (16 * e->nb);
+    const long long blocks = (long long)ncs * nct * p.s.N;
+    if (blocks >= (1LL << 31)) return false;
+    p.variant = V_MFMA;
+    p.cs = e->cs;
+    p.tm = 16;
+    p.th = 16;
+    p.aux0 = ncs;
+    p.aux1 = nct;
+    p.block = 256;
+    p.grid = (uint32_t)blocks;
+    p.lds_bytes = lds;
+    p.launch = e->fn;
+    snprintf(p.desc, sizeof(p.desc),
+             "mfma: 16x16x32 banded GEMM, strips of %d cols x %d ch walked 16 rows at a "
+             "time, %d fragment(s) of 16 taps, LDS %d B, %u x 256",
+             16 * e->nb, e->cs, nfrag, lds, p.grid);
+    return true;
+}
+
+}  // namespace dw

@@ -4,6 +4,5 @@
 namespace dw {
 
 bool plan_ldstile(Plan &) { return false; }
-bool plan_mfma(Plan &) { return false; }
 
 }  // namespace dw

@@ -63,7 +63,9 @@ int make_plan(Plan &p, int N, int H, int W, int C, int FH, int FW, int S, int D,
         case V_LDSTILE: ok = plan_ldstile(p); break;
         case V_MFMA: ok = plan_mfma(p); break;
         case V_AUTO:
-            ok = plan_mfma(p) || plan_ldstile(p) || plan_rowwin(p);
+            // the banded GEMM wastes most of its K window on filters narrower
+            // than 5 taps; there the vector families are preferred
+            ok = (FW >= 5 && plan_mfma(p)) || plan_ldstile(p) || plan_rowwin(p);
             if (!ok) { p = d; ok = true; }
             break;
     }
