@@ -64,8 +64,10 @@ int make_plan(Plan &p, int N, int H, int W, int C, int FH, int FW, int S, int D,
         case V_MFMA: ok = plan_mfma(p); break;
         case V_AUTO:
             // the banded GEMM wastes most of its K window on filters narrower
-            // than 5 taps; there the vector families are preferred
-            ok = (FW >= 5 && plan_mfma(p)) || plan_ldstile(p) || plan_rowwin(p);
+            // than 5 taps; there the vector families are preferred.  The
+            // register families need whole 16-byte channel vectors; the LDS
+            // tile takes any channel count.
+            ok = (FW >= 5 && plan_mfma(p)) || plan_rowwin(p) || plan_ldstile(p);
             if (!ok) { p = d; ok = true; }
             break;
     }
