@@ -13,8 +13,10 @@ from an earlier step, the bench keeps several copies of x and y, at least
 Prints one JSON line:
   value           algorithmic GB/s of K back-to-back steps (bytes / time per step)
   roofline        the kernel's own duration (a second pass of K steps with HIP
-                  events around each launch, averaged) against MI355X's 8 TB/s
-                  HBM, plus the HBM bytes per launch that the rocprofv3
+                  events around each launch, averaged) against the roof that
+                  binds it -- MI355X's 8 TB/s HBM, or for compute-bound
+                  filters the matrix-core / VALU peak of the units it uses --
+                  plus the HBM bytes per launch that the rocprofv3
                   FETCH_SIZE / WRITE_SIZE counters measured for this kernel,
                   scaled by what they read for a plain copy of known size
                   (profiles/counters.json; null once the sources changed)
@@ -37,6 +39,12 @@ sys.path.insert(0, ROOT)
 METRIC = "depthwise-conv fwd GB/s + GFLOP/s and fraction of HBM roofline, 1 MI355X"
 DEFAULT_WORKLOAD = "mobilenet_f32_3x3"
 HBM_PEAK_GBS = 8000.0
+# Published dense peaks of MI355X used for compute-bound kernels.  The VALU
+# figure is the fp32 FMA rate without packed-FP32 instructions (all HIP code
+# here is built with them disabled): 256 CUs x 4 SIMDs x 16 lanes x 2 flop x
+# 2.4 GHz = 78.6 TFLOP/s; int32 multiply-add runs at the same rate.
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
+VALU_PEAK_TFLOPS = 78.6
 MALL_FLUSH_BYTES = 1 << 30
 XB = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
 YB = {"f32": 4, "f16": 2, "bf16": 2, "i8": 4}
@@ -56,6 +64,26 @@ def work(wl):
     yb = wl.N * OH * OW * wl.C * YB[wl.dtype]
     flops = 2 * wl.N * OH * OW * wl.C * wl.FH * wl.FW
     return xb + wb + bb + yb, flops, OH, OW
+
+
+def roofline(wl, variant, nbytes, flops, kernel_s, traffic):
+    """The roof that binds this kernel: HBM unless the arithmetic at the peak
+    of the units the kernel uses (matrix cores for the mfma family, VALU
+    otherwise) takes longer than moving the algorithmic bytes at 8 TB/s."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    if variant == "mfma":
+        bound, peak = "mfma", MFMA_PEAK_TFLOPS[wl.dtype]
+    else:
+        bound, peak = "alu", VALU_PEAK_TFLOPS
+    t_cmp = flops / (peak * 1e12)
+    if t_hbm >= t_cmp:
+        achieved = nbytes / kernel_s / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    achieved = flops / kernel_s / 1e12
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "hbm_gbs": round(nbytes / kernel_s / 1e9, 2)}
 
 
 def kernel_sources_hash():
@@ -265,10 +293,7 @@ def main():
                    "buffer_sets": sets},
         "copy_ceiling": copy,
         "frac_of_copy": None if copy is None else round(achieved / copy["gbs"], 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+        "roofline": roofline(wl, variant, nbytes, flops, kavg_ms * 1e-3, traffic),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
