@@ -37,10 +37,12 @@
 // a fixed per-lane offset, with the band's zeros built in; the lane reads
 // them as five aligned dwords and a 16-bit funnel shift.
 //
-// Filter rows are taken in pairs: the fragments of two filter rows
-// accumulate into a fresh fp32 partial (at most 2 x 32 products per MFMA
-// chain), which is then added to the running sum; the bias seeds that sum
-// once.  Worst-case rounding is then about (64 + FH/2) * 2^-24 * sum|x*w|.  The epilogue rounds once to
+// The partial sums stay fp32 in the MFMA accumulators for the whole filter,
+// seeded once with the bias.  An MFMA adds its 32 products into the
+// accumulator with a single rounding (measured on gfx950: 32 products of
+// 2^-25 added to 1.0 are all kept, and 2^24 + 32 x 1.0 is exact), so a chain
+// of at most 64 MFMAs (FH <= 32, two fragments) has worst-case rounding
+// error below 2 * 64 * 2^-24 * sum|x*w| < 1e-5 * sum|x*w|.  The epilogue rounds once to
 // fp16/bf16 and goes through LDS so that the stores are whole channel
 // vectors of NHWC pixels, masked at the ragged right and bottom edges.
 #include "plan.h"
@@ -78,64 +80,34 @@ struct MfmaTile {
     static constexpr int XW = 16 * (NB + NFRAG);  // staged input columns
     static constexpr int PITCH = XW + 8;          // elements per staged row
     static constexpr int ZLEN = 48;               // padded fragment length
-    static constexpr int NEW = NB + NFRAG;        // tile elements per thread, 16 rows
+    static constexpr int NPAIR = 128 * (NB + NFRAG);   // column pairs in 16 rows
+    static constexpr int NEWP = (NPAIR + 255) / 256;   // column pairs per thread
+    // output tile: pixel stride and row stride (in elements) chosen so that
+    // the regrouping writes of a wavefront hit each LDS bank at most twice
+    static constexpr int OPS = CS == 8 ? 10 : 6;
+    static constexpr int ORS = 16 * NB * OPS + 4;
 };
 
-// Loads (into registers) the 16 padded input rows [R0, R0+16) of the strip:
-// element e = tid + 256u is row R0 + e / XW, column e % XW, CS channels.
-// Rows and columns outside the image are zeros.
-template <int CS, int XW, int NEW>
-__device__ __forceinline__ void strip_fetch(uint16_t (&v)[NEW][CS], const uint16_t *xn,
-                                            const Shape &s, int R0, int ow0, int tid) {
-#pragma unroll
-    for (int u = 0; u < NEW; ++u) {
-        const int e = tid + 256 * u;
-        const int ih = R0 + e / XW - s.P, iw = ow0 - s.P + e % XW;
-        if ((unsigned)ih < (unsigned)s.H && (unsigned)iw < (unsigned)s.W) {
-            const uint16_t *src = xn + ((long long)ih * s.W + iw) * s.C;
-            if constexpr (CS == 8) {
-                u32x4 q = *reinterpret_cast<const u32x4 *>(src);
-                __builtin_memcpy(v[u], &q, 16);
-            } else {
-                static_assert(CS == 4, "channel slice of 4 or 8");
-                uint2 q = *reinterpret_cast<const uint2 *>(src);
-                __builtin_memcpy(v[u], &q, 8);
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < CS; ++c) v[u][c] = 0;
-        }
-    }
-}
-
-// Scatters fetched rows into the channel-major ring: padded row R lives in
-// slot R mod XR.
-template <int CS, int XW, int NEW>
-__device__ __forceinline__ void strip_store(const uint16_t (&v)[NEW][CS], uint16_t *xt,
-                                            int XR, int R0, int tid) {
-    constexpr int PITCH = XW + 8;
-#pragma unroll
-    for (int u = 0; u < NEW; ++u) {
-        const int e = tid + 256 * u;
-        int slot = R0 + e / XW;
-        slot -= (slot / XR) * XR;
-        const int L = e % XW;
-#pragma unroll
-        for (int c = 0; c < CS; ++c) xt[(c * XR + slot) * PITCH + L] = v[u][c];
-    }
-}
-
-// Workgroup (4 wavefronts): one image, one strip of 16*NB output columns and
+// Workgroup (4 wavefronts): one image, a strip of 16*NB output columns and
 // CS channels, walking down the image 16 output rows at a time.  The
 // XR = 16 + FH - 1 padded input rows a row block needs sit in an LDS ring;
 // moving to the next block replaces the 16 oldest rows, whose loads are
 // issued before the current block's MFMAs so that their latency is hidden.
-template <class DT, int CS, int NB, int NFRAG>
+// FHK > 0: filters of at most FHK rows and one fragment keep every B operand
+// of the wavefront's channels in registers for the whole strip.
+template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT>
 __global__ void __launch_bounds__(256)
 k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
        const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int ncs, int nct) {
     using T = MfmaTile<CS, NB, NFRAG>;
-    constexpr int PITCH = T::PITCH, ZLEN = T::ZLEN, NEW = T::NEW;
+    constexpr int XW = T::XW, PITCH = T::PITCH, ZLEN = T::ZLEN;
+    constexpr int NCH = CS / 4;             // channels per wavefront
+    constexpr int NWIN = NB + NFRAG - 1;    // distinct A windows per filter row
+    static_assert(FHK == 0 || NFRAG == 1, "kept B operands: one fragment");
+    static_assert(FHT == 0 || FHK == 0 || FHT <= FHK, "kept B operands cover the filter");
+    // FHT > 0: the filter height is a compile-time constant and the
+    // filter-row loop is fully unrolled, so the accumulators keep fixed
+    // registers (a runtime loop made the compiler rotate them)
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
     const int XR = 16 + s.FH - 1;                   // ring rows
@@ -158,6 +130,69 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const int wave = tid >> 6;
     const uint16_t *xn = x + (long long)n * s.H * s.W * s.C + c0;
     const int nrb = (s.OH + 15) / 16;
+    const int WC = s.W * s.C;  // elements of one image row (< 2^31)
+
+    // Column pair e = tid + 256u of a 16-row chunk is chunk row e / (XW/2),
+    // tile columns 2 (e % (XW/2)) and the next one: the same for every chunk,
+    // so computed once.
+    constexpr int NEWP = T::NEWP, HALFW = XW / 2;
+    int crow[NEWP], ccol[NEWP], cgoff[NEWP];
+    bool cok0[NEWP], cok1[NEWP], cin[NEWP];
+#pragma unroll
+    for (int u = 0; u < NEWP; ++u) {
+        const int e = tid + 256 * u;
+        cin[u] = e < 16 * HALFW;
+        crow[u] = e / HALFW;
+        ccol[u] = 2 * (e % HALFW);
+        const int iw = ow0 - s.P + ccol[u];
+        cok0[u] = cin[u] && (unsigned)iw < (unsigned)s.W;
+        cok1[u] = cin[u] && (unsigned)(iw + 1) < (unsigned)s.W;
+        cgoff[u] = iw * s.C;
+    }
+    auto ld1 = [&](uint16_t(&v)[CS], const uint16_t *src) {
+        if constexpr (CS == 8) {
+            u32x4 q = *reinterpret_cast<const u32x4 *>(src);
+            __builtin_memcpy(v, &q, 16);
+        } else {
+            static_assert(CS == 4, "channel slice of 4 or 8");
+            uint2 q = *reinterpret_cast<const uint2 *>(src);
+            __builtin_memcpy(v, &q, 8);
+        }
+    };
+    // loads of padded input rows [R0, R0 + 16); zeros outside the image
+    auto fetch = [&](uint16_t(&v)[NEWP][2][CS], int R0) {
+#pragma unroll
+        for (int u = 0; u < NEWP; ++u) {
+            const int ih = R0 + crow[u] - s.P;
+            const bool rok = (unsigned)ih < (unsigned)s.H;
+            const uint16_t *src = xn + ih * WC + cgoff[u];
+            if (rok && cok0[u]) ld1(v[u][0], src);
+            else {
+#pragma unroll
+                for (int c = 0; c < CS; ++c) v[u][0][c] = 0;
+            }
+            if (rok && cok1[u]) ld1(v[u][1], src + s.C);
+            else {
+#pragma unroll
+                for (int c = 0; c < CS; ++c) v[u][1][c] = 0;
+            }
+        }
+    };
+    // channel-major scatter into the ring, one dword (two columns) per
+    // channel: padded row R lives in slot R mod XR
+    auto scatter = [&](const uint16_t(&v)[NEWP][2][CS], int R0, int rlimit) {
+        const int r0m = R0 % XR;
+#pragma unroll
+        for (int u = 0; u < NEWP; ++u) {
+            if (!cin[u] || R0 + crow[u] >= rlimit) continue;
+            int slot = r0m + crow[u];
+            slot -= slot >= XR ? XR : 0;
+#pragma unroll
+            for (int c = 0; c < CS; ++c)
+                *reinterpret_cast<uint32_t *>(xt + (c * XR + slot) * PITCH + ccol[u]) =
+                    (uint32_t)v[u][0][c] | ((uint32_t)v[u][1][c] << 16);
+        }
+    };
 
     // ---- filter slice as padded fragments: fragment f of filter row fh of
     // channel c is 16 zeros, its 16 taps (zero past FW), 16 zeros ----
@@ -166,154 +201,217 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         for (int e = 8 * tid; e < zlen; e += 8 * 256)   // zlen is a multiple of 8
             *reinterpret_cast<u32x4 *>(zt + e) = (u32x4){0u, 0u, 0u, 0u};
         __syncthreads();
-        // thread -> (fw = tid % 32, fh = tid / 32 + 8k): no divisions
+        // thread -> (fw = tid % 32, fh = tid / 32 + 8k): no divisions; the
+        // (at most 4) loads of a thread are issued before its LDS writes
         const int fw = tid & 31;
         if (fw < s.FW) {
             const int f = fw >> 4, q = fw & 15;
-            for (int fh = tid >> 5; fh < s.FH; fh += 8) {
-                uint16_t v[CS];
-                const uint16_t *src = w + ((long long)fh * s.FW + fw) * s.C + c0;
-                if constexpr (CS == 8) {
-                    u32x4 t = *reinterpret_cast<const u32x4 *>(src);
-                    __builtin_memcpy(v, &t, 16);
-                } else {
-                    uint2 t = *reinterpret_cast<const uint2 *>(src);
-                    __builtin_memcpy(v, &t, 8);
+            for (int fh0 = tid >> 5; fh0 < s.FH; fh0 += 32) {
+                uint16_t v[4][CS];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int fh = fh0 + 8 * k;
+                    if (fh < s.FH) ld1(v[k], w + ((long long)fh * s.FW + fw) * s.C + c0);
                 }
 #pragma unroll
-                for (int c = 0; c < CS; ++c)
-                    zt[((c * s.FH + fh) * NFRAG + f) * ZLEN + 16 + q] = v[c];
+                for (int k = 0; k < 4; ++k) {
+                    const int fh = fh0 + 8 * k;
+                    if (fh < s.FH) {
+#pragma unroll
+                        for (int c = 0; c < CS; ++c)
+                            zt[((c * s.FH + fh) * NFRAG + f) * ZLEN + 16 + q] = v[k][c];
+                    }
+                }
             }
         }
     }
-    // ---- prologue: padded rows [0, XR) of the first row block ----
-    for (int R0 = 0; R0 < XR; R0 += 16) {
-        uint16_t v[NEW][CS];
-        strip_fetch<CS, T::XW, NEW>(v, xn, s, R0, ow0, tid);
-        // rows past XR of the last chunk belong to the next block: skip them
+    // ---- prologue: padded rows [0, XR) of the first row block; the loads
+    // of up to four 16-row chunks are issued before any of them is written
+    for (int R0 = 0; R0 < XR; R0 += 64) {
+        uint16_t v[4][NEWP][2][CS];
 #pragma unroll
-        for (int u = 0; u < NEW; ++u) {
-            const int e = tid + 256 * u;
-            const int R = R0 + e / T::XW;
-            if (R < XR) {
-                const int L = e % T::XW;
+        for (int k = 0; k < 4; ++k)
+            if (R0 + 16 * k < XR) fetch(v[k], R0 + 16 * k);
 #pragma unroll
-                for (int c = 0; c < CS; ++c) xt[(c * XR + R) * PITCH + L] = v[u][c];
-            }
-        }
+        for (int k = 0; k < 4; ++k)
+            if (R0 + 16 * k < XR) scatter(v[k], R0 + 16 * k, XR);
     }
+    __syncthreads();
 
     const int g = lane >> 4;    // k group of A/B, row group of D
     const int t16 = lane & 15;  // row of A, column of B and D
-    // this lane's 8 entries of B are elements 16 + 8g - t16 .. +7 of the
+    // This lane's 8 entries of B are elements 16 + 8g - t16 .. +7 of the
     // padded fragment: B[k][t] = tap k - t.  They are read from the dword
     // holding element boff rounded down, shifted right by bsh bits.
     const int boff = 16 + 8 * g - t16;
     const int bsh = 16 * (boff & 1);
-    float bv[CS / 4];
+    const uint16_t *xc[NCH];
+    const uint16_t *zc[NCH];
+    float bv[NCH];
 #pragma unroll
-    for (int ci = 0; ci < CS / 4; ++ci) bv[ci] = bias ? bias[c0 + wave + 4 * ci] : 0.0f;
+    for (int ci = 0; ci < NCH; ++ci) {
+        const int c = wave + 4 * ci;
+        xc[ci] = xt + c * XR * PITCH + 8 * g;
+        zc[ci] = zt + c * s.FH * NFRAG * ZLEN + (boff & ~1);
+        bv[ci] = bias ? bias[c0 + c] : 0.0f;
+    }
+    auto load_b = [&](u32x4 &b, int ci, int fh, int f) {
+        const uint32_t *zd =
+            reinterpret_cast<const uint32_t *>(zc[ci] + (fh * NFRAG + f) * ZLEN);
+        uint32_t d[5];
+#pragma unroll
+        for (int q = 0; q < 5; ++q) d[q] = zd[q];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) b[q] = __builtin_amdgcn_alignbit(d[q + 1], d[q], bsh);
+    };
+    constexpr int KB = FHK > 0 ? FHK : 1;
+    u32x4 Bk[NCH][KB];
+    if constexpr (FHK > 0) {
+#pragma unroll
+        for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+            for (int fh = 0; fh < FHK; ++fh)
+                if (fh < s.FH) load_b(Bk[ci][fh], ci, fh, 0);
+    }
 
     for (int rb = 0; rb < nrb; ++rb) {
-        __syncthreads();  // ring rows of this block written; output tile free
+        if (rb) __syncthreads();  // ring rows of this block written; output tile free
         // prefetch the 16 rows the next block adds (the rows this block
         // needs are in the ring already)
         const int Rn = 16 * rb + XR;
         const bool more = rb + 1 < nrb;
-        uint16_t nv[NEW][CS];
-        if (more) strip_fetch<CS, T::XW, NEW>(nv, xn, s, Rn, ow0, tid);
+        uint16_t nv[NEWP][2][CS];
+        if (more) fetch(nv, Rn);
 
-        // The wavefront's CS/4 channels are interleaved, and the operands
-        // of filter row fh+1 are read from LDS before the MFMAs of row fh
-        // issue (two register sets), so LDS latency hides behind MFMAs.
-        constexpr int NCH = CS / 4;
-        constexpr int NWIN = NB + NFRAG - 1;
+        int slot0 = 16 * rb + t16;  // ring slot of this lane's row at fh = 0
+        slot0 %= XR;
+
+        // One fp32 MFMA chain per output tile, seeded with the bias: each
+        // MFMA adds its 32 products with one rounding, so a chain of at most
+        // 2 * 32 MFMAs stays within 1e-5 * sum|x*w| (about 2^-24 per MFMA).
         f32x4 acc[NCH][NB];
-        const uint16_t *xc[NCH];
-        const uint16_t *zc[NCH];
 #pragma unroll
-        for (int ci = 0; ci < NCH; ++ci) {
-            const int c = wave + 4 * ci;
+        for (int ci = 0; ci < NCH; ++ci)
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[ci][b] = (f32x4){bv[ci], bv[ci], bv[ci], bv[ci]};
-            xc[ci] = xt + c * XR * PITCH + 8 * g;
-            zc[ci] = zt + c * s.FH * NFRAG * ZLEN + (boff & ~1);
-        }
-        int slot0 = 16 * rb + t16;  // ring slot of this lane's row at fh = 0
-        slot0 -= (slot0 / XR) * XR;
 
+        // A windows of filter row fh: lane t16 holds row fh + t16 of the row
+        // block.  Row fh+1's windows are row fh's moved down one lane within
+        // each 16-lane row (DPP row_shl:1); only lane 15 reads its new row
+        // from LDS.  B operands (unless kept) and the next windows are
+        // produced before the MFMAs of row fh issue.
         struct Ops {
             u32x4 A[NCH][NWIN];
-            u32x4 B[NCH][NFRAG];
+            u32x4 B[NCH][FHK > 0 ? 1 : NFRAG];
         };
-        auto load_ops = [&](Ops &o, int fh) {
-            int slot = slot0 + fh;
-            slot -= slot >= XR ? XR : 0;
+        auto full_a = [&](Ops &o) {
 #pragma unroll
             for (int ci = 0; ci < NCH; ++ci) {
-#pragma unroll
-                for (int f = 0; f < NFRAG; ++f) {
-                    // 8 taps from element boff: five dword-aligned reads, then
-                    // a 16-bit funnel shift when boff is odd (unaligned wide
-                    // LDS reads stall)
-                    const uint32_t *zd = reinterpret_cast<const uint32_t *>(
-                        zc[ci] + (fh * NFRAG + f) * ZLEN);
-                    uint32_t d[5];
-#pragma unroll
-                    for (int q = 0; q < 5; ++q) d[q] = zd[q];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        o.B[ci][f][q] = __builtin_amdgcn_alignbit(d[q + 1], d[q], bsh);
-                }
-                const uint16_t *xr = xc[ci] + slot * PITCH;
+                const uint16_t *xr = xc[ci] + slot0 * PITCH;
 #pragma unroll
                 for (int win = 0; win < NWIN; ++win)
                     o.A[ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
             }
         };
-        auto mfmas = [&](const Ops &o, f32x4 (&part)[NCH][NB]) {
+        auto next_a = [&](Ops &o, const Ops &prev, int fh) {
+            // this lane's row for filter row fh (only lane 15's is read)
+            int slot = slot0 + fh;
+            slot -= slot >= XR ? XR : 0;
+#pragma unroll
+            for (int ci = 0; ci < NCH; ++ci) {
+#pragma unroll
+                for (int win = 0; win < NWIN; ++win)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        o.A[ci][win][q] = __builtin_amdgcn_update_dpp(
+                            0, (int)prev.A[ci][win][q], 0x101, 0xf, 0xf, true);
+                if (t16 == 15) {
+                    const uint16_t *xr = xc[ci] + slot * PITCH;
+#pragma unroll
+                    for (int win = 0; win < NWIN; ++win)
+                        o.A[ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
+                }
+            }
+        };
+        auto load_bs = [&](Ops &o, int fh) {
+            if constexpr (FHK == 0) {
+#pragma unroll
+                for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+                    for (int f = 0; f < NFRAG; ++f) load_b(o.B[ci][f], ci, fh, f);
+            }
+        };
+        auto mfmas = [&](const Ops &o, int fh) {
 #pragma unroll
             for (int f = 0; f < NFRAG; ++f)
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
-                    for (int ci = 0; ci < NCH; ++ci)
-                        part[ci][b] = MfmaOp<DT>::run(o.A[ci][b + f], o.B[ci][f], part[ci][b]);
+                    for (int ci = 0; ci < NCH; ++ci) {
+                        u32x4 bb;
+                        if constexpr (FHK > 0) {
+                            bb = Bk[ci][0];
+#pragma unroll
+                            for (int k = 1; k < FHK; ++k)
+                                if (fh == k) bb = Bk[ci][k];
+                        } else {
+                            bb = o.B[ci][f];
+                        }
+                        acc[ci][b] = MfmaOp<DT>::run(o.A[ci][b + f], bb, acc[ci][b]);
+                    }
         };
 
-        // filter rows two at a time: each pair accumulates into a fresh fp32
-        // partial that is then added to the running sum
-        Ops o0, o1;
-        load_ops(o0, 0);
-        for (int fh0 = 0; fh0 < s.FH; fh0 += 2) {
-            f32x4 part[NCH][NB];
+        if constexpr (FHT > 0) {
+            Ops o[2];
+            full_a(o[0]);
+            load_bs(o[0], 0);
 #pragma unroll
-            for (int ci = 0; ci < NCH; ++ci)
+            for (int fh = 0; fh < FHT; ++fh) {
+                if (fh + 1 < FHT) {
+                    next_a(o[(fh + 1) & 1], o[fh & 1], fh + 1);
+                    load_bs(o[(fh + 1) & 1], fh + 1);
+                }
+                mfmas(o[fh & 1], fh);
+            }
+        } else if constexpr (FHK > 0) {
+            Ops o[2];
+            full_a(o[0]);
 #pragma unroll
-                for (int b = 0; b < NB; ++b) part[ci][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            const bool two = fh0 + 1 < s.FH;
-            if (two) load_ops(o1, fh0 + 1);
-            mfmas(o0, part);
-            if (fh0 + 2 < s.FH) load_ops(o0, fh0 + 2);
-            if (two) mfmas(o1, part);
-#pragma unroll
-            for (int ci = 0; ci < NCH; ++ci)
-#pragma unroll
-                for (int b = 0; b < NB; ++b) acc[ci][b] += part[ci][b];
+            for (int fh = 0; fh < FHK; ++fh) {
+                if (fh >= s.FH) break;
+                if (fh + 1 < s.FH) next_a(o[(fh + 1) & 1], o[fh & 1], fh + 1);
+                mfmas(o[fh & 1], fh);
+            }
+        } else {
+            Ops o0, o1;
+            full_a(o0);
+            load_bs(o0, 0);
+            int fh = 0;
+            for (; fh + 1 < s.FH; fh += 2) {
+                next_a(o1, o0, fh + 1);
+                load_bs(o1, fh + 1);
+                mfmas(o0, fh);
+                if (fh + 2 < s.FH) {
+                    next_a(o0, o1, fh + 2);
+                    load_bs(o0, fh + 2);
+                }
+                mfmas(o1, fh + 1);
+            }
+            if (fh < s.FH) mfmas(o0, fh);
         }
-        f32x4 (&res)[NCH][NB] = acc;
 
         // ---- epilogue: round once, regroup through LDS into NHWC vectors ----
+        constexpr int OPS = T::OPS, ORS = T::ORS;
 #pragma unroll
-        for (int ci = 0; ci < CS / 4; ++ci) {
+        for (int ci = 0; ci < NCH; ++ci) {
             const int c = wave + 4 * ci;
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int row = 4 * g + q, col = 16 * b + t16;
-                    ot[(row * 16 * NB + col) * CS + c] =
-                        __builtin_bit_cast(uint16_t, DT::narrow(res[ci][b][q]));
+                    ot[row * ORS + col * OPS + c] =
+                        __builtin_bit_cast(uint16_t, DT::narrow(acc[ci][b][q]));
                 }
         }
         __syncthreads();  // block's ring rows consumed; output tile complete
@@ -323,27 +421,28 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
             const int oh = oh0 + row, ow = ow0 + col;
             if (oh < s.OH && ow < s.OW) {
                 uint16_t *dst = y + (((long long)n * s.OH + oh) * s.OW + ow) * s.C + c0;
-                const uint16_t *src = ot + e * CS;
+                const uint32_t *src =
+                    reinterpret_cast<const uint32_t *>(ot + row * ORS + col * OPS);
                 if constexpr (CS == 8)
-                    *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+                    *reinterpret_cast<u32x4 *>(dst) = (u32x4){src[0], src[1], src[2], src[3]};
                 else
-                    *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(src);
+                    *reinterpret_cast<uint2 *>(dst) = (uint2){src[0], src[1]};
             }
         }
-        if (more) strip_store<CS, T::XW, NEW>(nv, xt, XR, Rn, tid);
+        if (more) scatter(nv, Rn, 1 << 30);
     }
 }
 
-template <class DT, int CS, int NB, int NFRAG>
+template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT>
 static hipError_t launch_mfma(const Plan &p, const void *x, const void *w, const void *bias,
                               void *y, hipStream_t st) {
     if (p.lds_bytes > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG>),
+            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, FHT>),
             hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG>), dim3(p.grid), dim3(256), p.lds_bytes, st,
+    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT>), dim3(p.grid), dim3(256), p.lds_bytes, st,
                        (const uint16_t *)x, (const uint16_t *)w, (const float *)bias,
                        (uint16_t *)y, p.s, p.aux0, p.aux1);
     return hipGetLastError();
@@ -355,27 +454,34 @@ static int mfma_lds_bytes(const Shape &s) {
     const int XR = 16 + s.FH - 1;
     const int xt = CS * XR * T::PITCH;
     const int zt = CS * s.FH * NFRAG * T::ZLEN;
-    const int ot = 16 * 16 * NB * CS;
+    const int ot = 16 * T::ORS;
     return 2 * (xt + zt + ot);
 }
 
 struct MfmaEntry {
-    int dtype, cs, nb, nfrag;
+    int dtype, cs, nb, nfrag, fhk, fht;
     LaunchFn fn;
     int (*lds)(const Shape &);
 };
 
-#define MF(DTE, DTT, CS_, NB_, NF_) \
-    {DTE, CS_, NB_, NF_, launch_mfma<DTT, CS_, NB_, NF_>, mfma_lds_bytes<CS_, NB_, NF_>}
+#define MF(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_)                                             \
+    {DTE,     CS_, NB_, NF_, FHK_, FHT_, launch_mfma<DTT, CS_, NB_, NF_, FHK_, FHT_>, \
+     mfma_lds_bytes<CS_, NB_, NF_>}
 
 // Wider channel slices first (16-byte loads, more work per tile); the
 // planner falls back to 4 channels when the 8-channel tile exceeds 64 KiB of
 // LDS (tall filters), to keep several workgroups per CU.
 static const MfmaEntry kMfma[] = {
-    MF(DT_F16, F16, 8, 4, 1),   MF(DT_F16, F16, 8, 4, 2),
-    MF(DT_F16, F16, 4, 4, 1),   MF(DT_F16, F16, 4, 4, 2),
-    MF(DT_BF16, BF16, 8, 4, 1), MF(DT_BF16, BF16, 8, 4, 2),
-    MF(DT_BF16, BF16, 4, 4, 1), MF(DT_BF16, BF16, 4, 4, 2),
+    // compile-time filter heights of the common square filters
+    MF(DT_F16, F16, 8, 4, 1, 8, 7),    MF(DT_BF16, BF16, 8, 4, 1, 8, 7),
+    MF(DT_F16, F16, 4, 4, 2, 0, 31),   MF(DT_BF16, BF16, 4, 4, 2, 0, 31),
+    // any filter height
+    MF(DT_F16, F16, 8, 4, 1, 8, 0),    MF(DT_F16, F16, 8, 4, 1, 0, 0),
+    MF(DT_F16, F16, 8, 4, 2, 0, 0),    MF(DT_F16, F16, 4, 4, 1, 8, 0),
+    MF(DT_F16, F16, 4, 4, 1, 0, 0),    MF(DT_F16, F16, 4, 4, 2, 0, 0),
+    MF(DT_BF16, BF16, 8, 4, 1, 8, 0),  MF(DT_BF16, BF16, 8, 4, 1, 0, 0),
+    MF(DT_BF16, BF16, 8, 4, 2, 0, 0),  MF(DT_BF16, BF16, 4, 4, 1, 8, 0),
+    MF(DT_BF16, BF16, 4, 4, 1, 0, 0),  MF(DT_BF16, BF16, 4, 4, 2, 0, 0),
 };
 #undef MF
 
@@ -390,6 +496,8 @@ bool plan_mfma(Plan &p) {
     int lds = 0;
     for (const auto &k : kMfma) {
         if (k.dtype != p.dtype || k.nfrag != nfrag || p.s.C % k.cs != 0) continue;
+        if (k.fhk && p.s.FH > k.fhk) continue;
+        if (k.fht && p.s.FH != k.fht) continue;
         if (want_cs && k.cs != want_cs) continue;
         const int need = k.lds(p.s);
         const bool last = k.cs == 4 || want_cs;
