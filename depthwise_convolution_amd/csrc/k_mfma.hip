@@ -96,7 +96,7 @@ struct MfmaTile {
 // FHK > 0: filters of at most FHK rows and one fragment keep every B operand
 // of the wavefront's channels in registers for the whole strip.
 template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)  // two waves per SIMD: at most 256 registers
 k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
        const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int ncs, int nct) {
     using T = MfmaTile<CS, NB, NFRAG>;
@@ -110,10 +110,11 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     // registers (a runtime loop made the compiler rotate them)
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
-    const int XR = 16 + s.FH - 1;                   // ring rows
+    const int FH = FHT > 0 ? FHT : s.FH;            // filter height
+    const int XR = 16 + FH - 1;                     // ring rows
     uint16_t *xt = lds;                             // [CS][XR][PITCH]
     uint16_t *zt = xt + CS * XR * PITCH;            // [CS][FH][NFRAG][ZLEN]
-    uint16_t *ot = zt + CS * s.FH * NFRAG * ZLEN;   // [16][16*NB][CS]
+    uint16_t *ot = zt + CS * FH * NFRAG * ZLEN;     // [16][16*NB][CS]
 
     // workgroup -> (image, column strip, channel slice); channel slices vary
     // fastest so that the slices of one strip run together and share the L2
@@ -149,55 +150,46 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         cok1[u] = cin[u] && (unsigned)(iw + 1) < (unsigned)s.W;
         cgoff[u] = iw * s.C;
     }
-    auto ld1 = [&](uint16_t(&v)[CS], const uint16_t *src) {
-        if constexpr (CS == 8) {
-            u32x4 q = *reinterpret_cast<const u32x4 *>(src);
-            __builtin_memcpy(v, &q, 16);
-        } else {
-            static_assert(CS == 4, "channel slice of 4 or 8");
-            uint2 q = *reinterpret_cast<const uint2 *>(src);
-            __builtin_memcpy(v, &q, 8);
-        }
-    };
+    // One pixel's CS channels as a packed vector (two channels per dword).
+    typedef uint32_t PixV __attribute__((ext_vector_type(CS / 2)));
+    static_assert(CS == 4 || CS == 8, "channel slice of 4 or 8");
+    auto ld1 = [&](const uint16_t *src) { return *reinterpret_cast<const PixV *>(src); };
     // loads of padded input rows [R0, R0 + 16); zeros outside the image
-    auto fetch = [&](uint16_t(&v)[NEWP][2][CS], int R0) {
+    auto fetch = [&](PixV(&v)[NEWP][2], int R0, int rlimit) {
 #pragma unroll
         for (int u = 0; u < NEWP; ++u) {
             const int ih = R0 + crow[u] - s.P;
-            const bool rok = (unsigned)ih < (unsigned)s.H;
+            const bool rok = (unsigned)ih < (unsigned)s.H && R0 + crow[u] < rlimit;
             const uint16_t *src = xn + ih * WC + cgoff[u];
-            if (rok && cok0[u]) ld1(v[u][0], src);
-            else {
-#pragma unroll
-                for (int c = 0; c < CS; ++c) v[u][0][c] = 0;
-            }
-            if (rok && cok1[u]) ld1(v[u][1], src + s.C);
-            else {
-#pragma unroll
-                for (int c = 0; c < CS; ++c) v[u][1][c] = 0;
-            }
+            v[u][0] = rok && cok0[u] ? ld1(src) : (PixV)0u;
+            v[u][1] = rok && cok1[u] ? ld1(src + s.C) : (PixV)0u;
         }
     };
     // channel-major scatter into the ring, one dword (two columns) per
     // channel: padded row R lives in slot R mod XR
-    auto scatter = [&](const uint16_t(&v)[NEWP][2][CS], int R0, int rlimit) {
+    auto scatter = [&](const PixV(&v)[NEWP][2], int R0, int rlimit) {
         const int r0m = R0 % XR;
 #pragma unroll
         for (int u = 0; u < NEWP; ++u) {
             if (!cin[u] || R0 + crow[u] >= rlimit) continue;
             int slot = r0m + crow[u];
             slot -= slot >= XR ? XR : 0;
+            uint16_t *dst = xt + slot * PITCH + ccol[u];
 #pragma unroll
-            for (int c = 0; c < CS; ++c)
-                *reinterpret_cast<uint32_t *>(xt + (c * XR + slot) * PITCH + ccol[u]) =
-                    (uint32_t)v[u][0][c] | ((uint32_t)v[u][1][c] << 16);
+            for (int k = 0; k < CS / 2; ++k) {
+                const uint32_t a = v[u][0][k], b = v[u][1][k];
+                *reinterpret_cast<uint32_t *>(dst + (2 * k) * XR * PITCH) =
+                    (a & 0xffffu) | (b << 16);
+                *reinterpret_cast<uint32_t *>(dst + (2 * k + 1) * XR * PITCH) =
+                    (a >> 16) | (b & 0xffff0000u);
+            }
         }
     };
 
     // ---- filter slice as padded fragments: fragment f of filter row fh of
     // channel c is 16 zeros, its 16 taps (zero past FW), 16 zeros ----
     {
-        const int zlen = CS * s.FH * NFRAG * ZLEN;
+        const int zlen = CS * FH * NFRAG * ZLEN;
         for (int e = 8 * tid; e < zlen; e += 8 * 256)   // zlen is a multiple of 8
             *reinterpret_cast<u32x4 *>(zt + e) = (u32x4){0u, 0u, 0u, 0u};
         __syncthreads();
@@ -206,20 +198,21 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         const int fw = tid & 31;
         if (fw < s.FW) {
             const int f = fw >> 4, q = fw & 15;
-            for (int fh0 = tid >> 5; fh0 < s.FH; fh0 += 32) {
-                uint16_t v[4][CS];
+            for (int fh0 = tid >> 5; fh0 < FH; fh0 += 32) {
+                PixV v[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int fh = fh0 + 8 * k;
-                    if (fh < s.FH) ld1(v[k], w + ((long long)fh * s.FW + fw) * s.C + c0);
+                    if (fh < FH) v[k] = ld1(w + ((long long)fh * s.FW + fw) * s.C + c0);
                 }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int fh = fh0 + 8 * k;
-                    if (fh < s.FH) {
+                    if (fh < FH) {
 #pragma unroll
                         for (int c = 0; c < CS; ++c)
-                            zt[((c * s.FH + fh) * NFRAG + f) * ZLEN + 16 + q] = v[k][c];
+                            zt[((c * FH + fh) * NFRAG + f) * ZLEN + 16 + q] =
+                                (uint16_t)(v[k][c / 2] >> (16 * (c & 1)));
                     }
                 }
             }
@@ -228,10 +221,10 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     // ---- prologue: padded rows [0, XR) of the first row block; the loads
     // of up to four 16-row chunks are issued before any of them is written
     for (int R0 = 0; R0 < XR; R0 += 64) {
-        uint16_t v[4][NEWP][2][CS];
+        PixV v[4][NEWP][2];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            if (R0 + 16 * k < XR) fetch(v[k], R0 + 16 * k);
+            if (R0 + 16 * k < XR) fetch(v[k], R0 + 16 * k, XR);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (R0 + 16 * k < XR) scatter(v[k], R0 + 16 * k, XR);
@@ -252,7 +245,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     for (int ci = 0; ci < NCH; ++ci) {
         const int c = wave + 4 * ci;
         xc[ci] = xt + c * XR * PITCH + 8 * g;
-        zc[ci] = zt + c * s.FH * NFRAG * ZLEN + (boff & ~1);
+        zc[ci] = zt + c * FH * NFRAG * ZLEN + (boff & ~1);
         bv[ci] = bias ? bias[c0 + c] : 0.0f;
     }
     auto load_b = [&](u32x4 &b, int ci, int fh, int f) {
@@ -264,14 +257,14 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
 #pragma unroll
         for (int q = 0; q < 4; ++q) b[q] = __builtin_amdgcn_alignbit(d[q + 1], d[q], bsh);
     };
-    constexpr int KB = FHK > 0 ? FHK : 1;
+    constexpr int KB = FHT > 0 && FHK > 0 ? FHT : FHK > 0 ? FHK : 1;
     u32x4 Bk[NCH][KB];
     if constexpr (FHK > 0) {
 #pragma unroll
         for (int ci = 0; ci < NCH; ++ci)
 #pragma unroll
-            for (int fh = 0; fh < FHK; ++fh)
-                if (fh < s.FH) load_b(Bk[ci][fh], ci, fh, 0);
+            for (int fh = 0; fh < KB; ++fh)
+                if (fh < FH) load_b(Bk[ci][fh], ci, fh, 0);
     }
 
     for (int rb = 0; rb < nrb; ++rb) {
@@ -280,8 +273,8 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         // needs are in the ring already)
         const int Rn = 16 * rb + XR;
         const bool more = rb + 1 < nrb;
-        uint16_t nv[NEWP][2][CS];
-        if (more) fetch(nv, Rn);
+        PixV nv[NEWP][2];
+        if (more) fetch(nv, Rn, 1 << 30);
 
         int slot0 = 16 * rb + t16;  // ring slot of this lane's row at fh = 0
         slot0 %= XR;
@@ -352,7 +345,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                         if constexpr (FHK > 0) {
                             bb = Bk[ci][0];
 #pragma unroll
-                            for (int k = 1; k < FHK; ++k)
+                            for (int k = 1; k < KB; ++k)
                                 if (fh == k) bb = Bk[ci][k];
                         } else {
                             bb = o.B[ci][f];
@@ -372,14 +365,17 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     load_bs(o[(fh + 1) & 1], fh + 1);
                 }
                 mfmas(o[fh & 1], fh);
+                // keep the scheduler from hoisting later rows' operands
+                // (and their registers) above this row's MFMAs
+                __builtin_amdgcn_sched_barrier(0);
             }
         } else if constexpr (FHK > 0) {
             Ops o[2];
             full_a(o[0]);
 #pragma unroll
             for (int fh = 0; fh < FHK; ++fh) {
-                if (fh >= s.FH) break;
-                if (fh + 1 < s.FH) next_a(o[(fh + 1) & 1], o[fh & 1], fh + 1);
+                if (fh >= FH) break;
+                if (fh + 1 < FH) next_a(o[(fh + 1) & 1], o[fh & 1], fh + 1);
                 mfmas(o[fh & 1], fh);
             }
         } else {
@@ -387,17 +383,17 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
             full_a(o0);
             load_bs(o0, 0);
             int fh = 0;
-            for (; fh + 1 < s.FH; fh += 2) {
+            for (; fh + 1 < FH; fh += 2) {
                 next_a(o1, o0, fh + 1);
                 load_bs(o1, fh + 1);
                 mfmas(o0, fh);
-                if (fh + 2 < s.FH) {
+                if (fh + 2 < FH) {
                     next_a(o0, o1, fh + 2);
                     load_bs(o0, fh + 2);
                 }
                 mfmas(o1, fh + 1);
             }
-            if (fh < s.FH) mfmas(o0, fh);
+            if (fh < FH) mfmas(o0, fh);
         }
 
         // ---- epilogue: round once, regroup through LDS into NHWC vectors ----
@@ -415,21 +411,34 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                 }
         }
         __syncthreads();  // block's ring rows consumed; output tile complete
+        // The next block's rows go into the ring first: their loads were
+        // issued before this block's MFMAs, and waiting for them here, with
+        // no global stores outstanding yet, does not also wait for this
+        // block's stores to be acknowledged.
+        if (more) scatter(nv, Rn, 1 << 30);
+        // Every output pixel vector of the tile is read from LDS before the
+        // first store is issued, so the LDS latency is paid once.
+        constexpr int NOUT = 16 * 16 * NB / 256;
+        static_assert(16 * 16 * NB % 256 == 0, "whole output vectors per thread");
+        PixV ov[NOUT];
+#pragma unroll
+        for (int k = 0; k < NOUT; ++k) {
+            const int e = tid + 256 * k;
+            const int row = e / (16 * NB), col = e % (16 * NB);
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(ot + row * ORS + col * OPS);
+#pragma unroll
+            for (int q = 0; q < CS / 2; ++q) ov[k][q] = src[q];
+        }
         const int oh0 = 16 * rb;
-        for (int e = tid; e < 16 * 16 * NB; e += 256) {
+#pragma unroll
+        for (int k = 0; k < NOUT; ++k) {
+            const int e = tid + 256 * k;
             const int row = e / (16 * NB), col = e % (16 * NB);
             const int oh = oh0 + row, ow = ow0 + col;
-            if (oh < s.OH && ow < s.OW) {
-                uint16_t *dst = y + (((long long)n * s.OH + oh) * s.OW + ow) * s.C + c0;
-                const uint32_t *src =
-                    reinterpret_cast<const uint32_t *>(ot + row * ORS + col * OPS);
-                if constexpr (CS == 8)
-                    *reinterpret_cast<u32x4 *>(dst) = (u32x4){src[0], src[1], src[2], src[3]};
-                else
-                    *reinterpret_cast<uint2 *>(dst) = (uint2){src[0], src[1]};
-            }
+            if (oh < s.OH && ow < s.OW)
+                *reinterpret_cast<PixV *>(y + (((long long)n * s.OH + oh) * s.OW + ow) * s.C + c0) =
+                    ov[k];
         }
-        if (more) scatter(nv, Rn, 1 << 30);
     }
 }
 
