@@ -267,6 +267,27 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                 if (fh < FH) load_b(Bk[ci][fh], ci, fh, 0);
     }
 
+    // Output vectors of the previous row block.  A store reads its data
+    // registers after issue, so a register it still holds cannot be
+    // rewritten before the store has drained; keeping these registers out of
+    // the allocator's hands until the next epilogue means no refill or MFMA
+    // operand of the next block has to wait for the previous block's stores.
+    // Thread tid stores NOUT consecutive pixels of output row tid / OTPR of
+    // the block with buffer stores: one 32-bit lane offset, the pixel step
+    // as a uniform offset, and the image's output range checked by the
+    // buffer resource.
+    constexpr int NOUT = 16 * 16 * NB / 256;
+    constexpr int OTPR = 256 / 16;  // threads per output row
+    static_assert(16 * 16 * NB == 256 * NOUT && NOUT * OTPR == 16 * NB, "output tile mapping");
+    const int orow = tid / OTPR, ocol0 = NOUT * (tid % OTPR);
+    PixV ov[NOUT];
+#pragma unroll
+    for (int k = 0; k < NOUT; ++k) ov[k] = (PixV)0u;
+    uint32_t yoff = 0;
+    const long long yimg = (long long)s.OH * s.OW * s.C;  // elements per image (< 2^31)
+    const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+        y + n * yimg + c0, (short)0, (int)(uint32_t)(2 * (yimg - c0)), 0x00020000);
+
     for (int rb = 0; rb < nrb; ++rb) {
         if (rb) __syncthreads();  // ring rows of this block written; output tile free
         // prefetch the 16 rows the next block adds (the rows this block
@@ -416,28 +437,33 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         // no global stores outstanding yet, does not also wait for this
         // block's stores to be acknowledged.
         if (more) scatter(nv, Rn, 1 << 30);
+        // The refill loads are consumed and the previous block's stores are
+        // long done: say so on every path (vmcnt 0, other counters
+        // untouched), so that later register reuse needs no wait.
+        __builtin_amdgcn_s_waitcnt(0x0f70);
         // Every output pixel vector of the tile is read from LDS before the
         // first store is issued, so the LDS latency is paid once.
-        constexpr int NOUT = 16 * 16 * NB / 256;
-        static_assert(16 * 16 * NB % 256 == 0, "whole output vectors per thread");
-        PixV ov[NOUT];
+#pragma unroll
+        for (int k = 0; k < NOUT; ++k) asm volatile("" : "+v"(ov[k]));
+        asm volatile("" : "+v"(yoff));
 #pragma unroll
         for (int k = 0; k < NOUT; ++k) {
-            const int e = tid + 256 * k;
-            const int row = e / (16 * NB), col = e % (16 * NB);
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(ot + row * ORS + col * OPS);
+            const uint32_t *src =
+                reinterpret_cast<const uint32_t *>(ot + orow * ORS + (ocol0 + k) * OPS);
 #pragma unroll
             for (int q = 0; q < CS / 2; ++q) ov[k][q] = src[q];
         }
-        const int oh0 = 16 * rb;
+        const int oh = 16 * rb + orow, ow = ow0 + ocol0;
+        yoff = 2u * (uint32_t)((oh * s.OW + ow) * s.C);
+        if (oh < s.OH) {
 #pragma unroll
-        for (int k = 0; k < NOUT; ++k) {
-            const int e = tid + 256 * k;
-            const int row = e / (16 * NB), col = e % (16 * NB);
-            const int oh = oh0 + row, ow = ow0 + col;
-            if (oh < s.OH && ow < s.OW)
-                *reinterpret_cast<PixV *>(y + (((long long)n * s.OH + oh) * s.OW + ow) * s.C + c0) =
-                    ov[k];
+            for (int k = 0; k < NOUT; ++k)
+                if (ow + k < s.OW) {
+                    if constexpr (CS == 8)
+                        __builtin_amdgcn_raw_buffer_store_b128(ov[k], yrs, (int)yoff, 2 * k * s.C, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b64(ov[k], yrs, (int)yoff, 2 * k * s.C, 0);
+                }
         }
     }
 }

@@ -93,12 +93,13 @@ __device__ __forceinline__ void store_out(Y *dst, const Y (&o)[VEC]) {
     if constexpr (NT) {
         // y is never read back by this kernel: stream it past the caches
         constexpr int B = sizeof(Y) * VEC;
-        static_assert(B % 16 == 0, "whole 16-byte vectors");
-        using V = typename VecT<16>::T;
+        constexpr int VB = B < 16 ? B : 16;  // bytes per store
+        static_assert(B % VB == 0, "whole vectors");
+        using V = typename VecT<VB>::T;
 #pragma unroll
-        for (int k = 0; k < B / 16; ++k) {
+        for (int k = 0; k < B / VB; ++k) {
             V v;
-            __builtin_memcpy(&v, reinterpret_cast<const char *>(o) + 16 * k, 16);
+            __builtin_memcpy(&v, reinterpret_cast<const char *>(o) + VB * k, VB);
             __builtin_nontemporal_store(v, reinterpret_cast<V *>(dst) + k);
         }
     } else {
