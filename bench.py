@@ -12,14 +12,18 @@ from an earlier step, the bench keeps several copies of x and y, at least
 
 Prints one JSON line:
   value           algorithmic GB/s of K back-to-back steps (bytes / time per step)
-  roofline        the kernel's own duration (a second pass of K steps with HIP
-                  events around each launch, averaged) against the roof that
+  roofline        the kernel's average duration (HIP events around the K
+                  back-to-back steps, one launch each) against the roof that
                   binds it -- MI355X's 8 TB/s HBM, or for compute-bound
                   filters the matrix-core / VALU peak of the units it uses --
                   plus the HBM bytes per launch that the rocprofv3
                   FETCH_SIZE / WRITE_SIZE counters measured for this kernel,
                   scaled by what they read for a plain copy of known size
                   (profiles/counters.json; null once the sources changed)
+  kernel          plan, average, and the spread of single launches (a second
+                  pass with an event pair around each launch: mean, median,
+                  min, p90; each pair adds the event packets' own time)
+  copy_ceiling    torch's device copy of the same byte count, back to back
   cpu_baseline    the CPU oracle timed on this host's cores on a sample
 Algorithmic bytes count x, w, bias and y once each; halo re-reads and
 padding are not counted.  FLOPs are 2 per tap per output.
@@ -86,12 +90,18 @@ def roofline(wl, variant, nbytes, flops, kernel_s, traffic):
             "hbm_gbs": round(nbytes / kernel_s / 1e9, 2)}
 
 
-def kernel_sources_hash():
-    """Hash of the library sources; counter figures stored under profiles/
-    are reported only while it matches the hash they were taken with."""
+# the source file each kernel family is compiled from
+FAMILY_SOURCES = {"direct": "k_direct.hip", "rowwin": "k_rowwin.hip",
+                  "ldstile": "k_ldstile.hip", "mfma": "k_mfma.hip"}
+
+
+def kernel_sources_hash(variant):
+    """Hash of one kernel family's source file and the headers every family
+    includes; counter figures stored under profiles/ are reported only while
+    it matches the hash they were taken with."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "depthwise_convolution_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ("dw_common.h", "plan.h", FAMILY_SOURCES[variant]):
         h.update(f.encode())
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
@@ -105,7 +115,7 @@ def stored_traffic(workload, variant):
         rec = json.load(open(path)).get(f"{workload}/{variant}")
     except (ValueError, OSError):
         return None
-    if not rec or rec.get("sources") != kernel_sources_hash():
+    if not rec or rec.get("sources") != kernel_sources_hash(variant):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -122,17 +132,17 @@ def copy_ceiling(torch, dev, stream, nbytes, sets, K, warmup):
         t.fill_(1)
     for i in range(warmup):
         dst[i % sets].copy_(src[i % sets])
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    e0.record(stream)
     for i in range(K):
-        ev0[i].record(stream)
         dst[i % sets].copy_(src[i % sets])
-        ev1[i].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(z) for a, z in zip(ev0, ev1)]))
+    ms = e0.elapsed_time(e1) / K
     return {"gbs": round(2 * half / (ms * 1e-3) / 1e9, 2), "avg_us": round(ms * 1e3, 3),
-            "bytes": 2 * half, "kind": "torch copy_ (device to device)"}
+            "bytes": 2 * half, "kind": "torch copy_ (device to device), back to back"}
 
 
 def cpu_baseline(wl, x, w, b, budget_s=20.0):
@@ -230,7 +240,8 @@ def main():
     t_wall = time.perf_counter() - t_wall0
     total_ms = start.elapsed_time(end)
     # pass 2: the same K steps with a HIP event pair around every launch, on
-    # the launch stream -> the kernel's own average duration
+    # the launch stream: the spread of single launches (each pair adds the
+    # event packets' own time, so these run a little above pass 1's average)
     ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()
@@ -242,14 +253,17 @@ def main():
     kern_ms = np.array([a.elapsed_time(z) for a, z in zip(ev0, ev1)])
     dw.dwconv_destroy(h)
 
+    # one launch per step: the kernel's average duration is the timed
+    # region's average
     ms_per_step = total_ms / K
-    kavg_ms = float(kern_ms.mean())
+    kavg_ms = ms_per_step
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kavg_ms * 1e-3) / 1e9
     traffic = stored_traffic(wl.name, variant)
-    print(f"[bench] kernel avg {kavg_ms * 1e3:.2f} us (median "
-          f"{np.median(kern_ms) * 1e3:.2f}, min {kern_ms.min() * 1e3:.2f}); step "
-          f"{ms_per_step * 1e3:.2f} us; host wall {t_wall * 1e3 / K:.2f} us/step",
+    print(f"[bench] kernel avg {kavg_ms * 1e3:.2f} us over the timed region; single "
+          f"launches with events: mean {kern_ms.mean() * 1e3:.2f}, median "
+          f"{np.median(kern_ms) * 1e3:.2f}, min {kern_ms.min() * 1e3:.2f}, p90 "
+          f"{np.percentile(kern_ms, 90) * 1e3:.2f} us; host wall {t_wall * 1e3 / K:.2f} us/step",
           file=sys.stderr, flush=True)
 
     copy = None
@@ -288,8 +302,11 @@ def main():
         "flops": flops,
         "kernel": {"variant": variant, "plan": desc,
                    "avg_us": round(kavg_ms * 1e3, 3),
-                   "median_us": round(float(np.median(kern_ms)) * 1e3, 3),
-                   "min_us": round(float(kern_ms.min()) * 1e3, 3),
+                   "single_launch_us": {
+                       "mean": round(float(kern_ms.mean()) * 1e3, 3),
+                       "median": round(float(np.median(kern_ms)) * 1e3, 3),
+                       "min": round(float(kern_ms.min()) * 1e3, 3),
+                       "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3)},
                    "buffer_sets": sets},
         "copy_ceiling": copy,
         "frac_of_copy": None if copy is None else round(achieved / copy["gbs"], 4),
