@@ -72,10 +72,15 @@ template <>
 __device__ __forceinline__ float mac<float>(float acc, float a, float b) {
     return __builtin_fmaf(a, b, acc);
 }
+// int8 operands widened to int32 fit 24 bits: a 24-bit multiply-add is
+// exact and runs at full rate (a 32-bit multiply is quarter rate)
 template <>
 __device__ __forceinline__ int32_t mac<int32_t>(int32_t acc, int32_t a, int32_t b) {
-    return acc + a * b;
+    return acc + __mul24(a, b);
 }
+
+// Greatest common divisor (compile-time or host use).
+__host__ __device__ constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
 // Workgroups are handed to the 8 XCDs of the chip round-robin, and each XCD
 // has its own L2.  Renumber them so that a contiguous range of logical tiles

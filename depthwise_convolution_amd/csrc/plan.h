@@ -29,7 +29,7 @@ struct Plan {
     int lds_bytes;        // dynamic LDS per workgroup
     int block;            // threads per workgroup
     uint32_t grid;        // workgroups
-    int aux0, aux1, aux2; // family-specific extra launch parameters
+    int aux0, aux1, aux2, aux3;  // family-specific extra launch parameters
     LaunchFn launch;      // launcher for `variant`
     LaunchFn fallback;    // launcher for misaligned pointers (direct family)
     char desc[192];

@@ -259,3 +259,54 @@ def test_each_column_stream_tiling(fmt, monkeypatch):
             desc = dw.dwconv_plan_describe(h)
             dw.dwconv_destroy(h)
             assert desc.startswith("colstream"), desc
+
+
+# The compiled LDS-tile entries, (dtype, F, S, D): int8 with D dividing S
+# runs the tap-packed kernel, the rest the flat-row kernel.
+LDS_ENTRIES = [("i8", 5, 2, 2), ("i8", 3, 1, 1), ("i8", 5, 1, 1), ("i8", 7, 1, 1),
+               ("i8", 3, 2, 1), ("i8", 3, 2, 2),
+               ("f32", 5, 2, 2), ("f32", 3, 1, 1), ("f32", 7, 1, 1),
+               ("f16", 5, 2, 2), ("f16", 3, 1, 1), ("f16", 7, 1, 1),
+               ("bf16", 5, 2, 2), ("bf16", 3, 1, 1), ("bf16", 7, 1, 1)]
+
+
+@pytest.mark.parametrize("entry", LDS_ENTRIES, ids=lambda e: "%s-%dx%d-s%d-d%d" % (e[0], e[1], e[1], e[2], e[3]))
+def test_each_lds_tile_entry(entry, monkeypatch):
+    """Each compiled LDS-tile kernel against the oracle: channel counts of
+    one, a ragged odd count, exactly one 64-lane group, one more than that and
+    several groups; images narrower and shorter than a tile; paddings of
+    zero, half the span and a full span; tile heights 1, 3 and the planner's."""
+    fmt, F, S, D = entry
+    rng = np.random.default_rng(17)
+    span = (F - 1) * D
+    shapes = [(1, 9, 13, 1, F, F, S, D, span // 2),
+              (2, 17, 23, 61, F, F, S, D, span // 2),
+              (1, 20, 19, 64, F, F, S, D, 0),
+              (1, 12, 40, 65, F, F, S, D, span),
+              (1, 30, 7, 130, F, F, S, D, 1)]
+    for tb in ("", "1", "3"):
+        if tb:
+            monkeypatch.setenv("DWCONV_LDS_TB", tb)
+        else:
+            monkeypatch.delenv("DWCONV_LDS_TB", raising=False)
+        for shape in shapes:
+            N, H, W, C, FH, FW, S_, D_, P = shape
+            if (H + 2 * P - D * (F - 1) - 1) < 0 or (W + 2 * P - D * (F - 1) - 1) < 0:
+                continue
+            if fmt == "i8":
+                dist, wdist, bd = ("int", -128, 127), ("int", -128, 127), ("int", -2**15, 2**15)
+            else:
+                dist, wdist, bd = ("normal", 0.0, 1.0), ("normal", 0.0, 1.0 / F), ("uniform", -0.1, 0.1)
+            wl = synth.Workload("lds", fmt, *shape, dist, wdist, bd, int(rng.integers(0, 2**31)))
+            x, w, b = make_inputs(wl)
+            if not supported(shape, fmt, "ldstile"):
+                continue
+            h = dw.dwconv_create_variant(*shape, fmt, "ldstile")
+            desc = dw.dwconv_plan_describe(h)
+            dw.dwconv_destroy(h)
+            say(f"[gpu] lds entry {entry} TB={tb or 'auto'} shape {shape}: {desc[:60]}")
+            y, used = run(x, w, b, shape, fmt, "ldstile", guard=512)
+            assert used == "ldstile", used
+            assert_matches_oracle(y, x, w, b, shape, fmt, f"lds {entry} tb={tb} {shape}")
+            if fmt == "i8" and S % D == 0:
+                assert "tap-packed" in desc, desc
