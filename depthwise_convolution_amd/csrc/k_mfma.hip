@@ -24,9 +24,9 @@
 // one channel are formed: every MFMA works on a single channel, as the pages'
 // one-GEMM-per-channel does.
 //
-// Workgroup (4 wavefronts): one image, a strip of 16*NB output columns and
-// CS channels, walked down 16 output rows at a time.  The input a row block
-// needs -- the halo span (16 + FH - 1) rows x 16(NB + NFRAG) columns of
+// Workgroup (4 wavefronts, 8 for 16-channel slices): one image, a strip of
+// 16*NB output columns and CS channels, walked down 16 output rows at a
+// time.  The input a row block needs -- the halo span (16 + FH - 1) rows x 16(NB + NFRAG) columns of
 // "Tiles, halos and partial sums", with padding generated as zeros -- sits in
 // an LDS ring, channel-major, so that one 16-byte LDS read gives a lane its 8
 // consecutive columns of one channel (the A operand); each new block loads
@@ -80,28 +80,34 @@ struct MfmaTile {
     static constexpr int XW = 16 * (NB + NFRAG);  // staged input columns
     static constexpr int PITCH = XW + 8;          // elements per staged row
     static constexpr int ZLEN = 48;               // padded fragment length
+    static constexpr int NW = CS >= 16 ? 8 : 4;       // wavefronts per workgroup
+    static constexpr int NT = 64 * NW;                 // threads per workgroup
     static constexpr int NPAIR = 128 * (NB + NFRAG);   // column pairs in 16 rows
-    static constexpr int NEWP = (NPAIR + 255) / 256;   // column pairs per thread
-    // output tile: pixel stride and row stride (in elements) chosen so that
-    // the regrouping writes of a wavefront hit each LDS bank at most twice
-    static constexpr int OPS = CS == 8 ? 10 : 6;
+    static constexpr int NEWP = (NPAIR + NT - 1) / NT; // column pairs per thread
+    // output tile: pixel stride (an odd number of dwords) and row stride (4
+    // mod 16 elements) chosen so that the regrouping writes of a wavefront
+    // hit each LDS bank at most twice
+    static constexpr int OPS = CS + 2;
     static constexpr int ORS = 16 * NB * OPS + 4;
 };
 
-// Workgroup (4 wavefronts): one image, a strip of 16*NB output columns and
-// CS channels, walking down the image 16 output rows at a time.  The
+// Workgroup (4 wavefronts, 8 for 16-channel slices): one image, a strip of
+// 16*NB output columns and CS channels, walking down the image 16 output rows
+// at a time.  The
 // XR = 16 + FH - 1 padded input rows a row block needs sit in an LDS ring;
 // moving to the next block replaces the 16 oldest rows, whose loads are
 // issued before the current block's MFMAs so that their latency is hidden.
 // FHK > 0: filters of at most FHK rows and one fragment keep every B operand
 // of the wavefront's channels in registers for the whole strip.
 template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT>
-__global__ void __launch_bounds__(256, 2)  // two waves per SIMD: at most 256 registers
+__global__ void __launch_bounds__(CS >= 16 ? 512 : 256, 2)  // at most 256 registers
 k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
        const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int ncs, int nct) {
     using T = MfmaTile<CS, NB, NFRAG>;
     constexpr int XW = T::XW, PITCH = T::PITCH, ZLEN = T::ZLEN;
-    constexpr int NCH = CS / 4;             // channels per wavefront
+    constexpr int NW = T::NW, NT = T::NT;
+    static_assert(NT == (CS >= 16 ? 512 : 256), "launch bounds match the tile");
+    constexpr int NCH = CS / NW;            // channels per wavefront
     constexpr int NWIN = NB + NFRAG - 1;    // distinct A windows per filter row
     static_assert(FHK == 0 || NFRAG == 1, "kept B operands: one fragment");
     static_assert(FHT == 0 || FHK == 0 || FHT <= FHK, "kept B operands cover the filter");
@@ -133,7 +139,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const int nrb = (s.OH + 15) / 16;
     const int WC = s.W * s.C;  // elements of one image row (< 2^31)
 
-    // Column pair e = tid + 256u of a 16-row chunk is chunk row e / (XW/2),
+    // Column pair e = tid + NT*u of a 16-row chunk is chunk row e / (XW/2),
     // tile columns 2 (e % (XW/2)) and the next one: the same for every chunk,
     // so computed once.
     constexpr int NEWP = T::NEWP, HALFW = XW / 2;
@@ -141,7 +147,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     bool cok0[NEWP], cok1[NEWP], cin[NEWP];
 #pragma unroll
     for (int u = 0; u < NEWP; ++u) {
-        const int e = tid + 256 * u;
+        const int e = tid + NT * u;
         cin[u] = e < 16 * HALFW;
         crow[u] = e / HALFW;
         ccol[u] = 2 * (e % HALFW);
@@ -152,7 +158,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     }
     // One pixel's CS channels as a packed vector (two channels per dword).
     typedef uint32_t PixV __attribute__((ext_vector_type(CS / 2)));
-    static_assert(CS == 4 || CS == 8, "channel slice of 4 or 8");
+    static_assert(CS == 4 || CS == 8 || CS == 16, "channel slice of 4, 8 or 16");
     auto ld1 = [&](const uint16_t *src) { return *reinterpret_cast<const PixV *>(src); };
     // loads of padded input rows [R0, R0 + 16); zeros outside the image
     auto fetch = [&](PixV(&v)[NEWP][2], int R0, int rlimit) {
@@ -190,24 +196,25 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     // channel c is 16 zeros, its 16 taps (zero past FW), 16 zeros ----
     {
         const int zlen = CS * FH * NFRAG * ZLEN;
-        for (int e = 8 * tid; e < zlen; e += 8 * 256)   // zlen is a multiple of 8
+        for (int e = 8 * tid; e < zlen; e += 8 * NT)   // zlen is a multiple of 8
             *reinterpret_cast<u32x4 *>(zt + e) = (u32x4){0u, 0u, 0u, 0u};
         __syncthreads();
-        // thread -> (fw = tid % 32, fh = tid / 32 + 8k): no divisions; the
-        // (at most 4) loads of a thread are issued before its LDS writes
+        // thread -> (fw = tid % 32, fh = tid / 32 + RPP*k): no divisions;
+        // the (at most 4) loads of a thread are issued before its LDS writes
+        constexpr int RPP = NT / 32;  // filter rows per pass of the workgroup
         const int fw = tid & 31;
         if (fw < s.FW) {
             const int f = fw >> 4, q = fw & 15;
-            for (int fh0 = tid >> 5; fh0 < FH; fh0 += 32) {
+            for (int fh0 = tid >> 5; fh0 < FH; fh0 += 4 * RPP) {
                 PixV v[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const int fh = fh0 + 8 * k;
+                    const int fh = fh0 + RPP * k;
                     if (fh < FH) v[k] = ld1(w + ((long long)fh * s.FW + fw) * s.C + c0);
                 }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const int fh = fh0 + 8 * k;
+                    const int fh = fh0 + RPP * k;
                     if (fh < FH) {
 #pragma unroll
                         for (int c = 0; c < CS; ++c)
@@ -243,7 +250,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     float bv[NCH];
 #pragma unroll
     for (int ci = 0; ci < NCH; ++ci) {
-        const int c = wave + 4 * ci;
+        const int c = wave + NW * ci;
         xc[ci] = xt + c * XR * PITCH + 8 * g;
         zc[ci] = zt + c * FH * NFRAG * ZLEN + (boff & ~1);
         bv[ci] = bias ? bias[c0 + c] : 0.0f;
@@ -276,9 +283,9 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     // the block with buffer stores: one 32-bit lane offset, the pixel step
     // as a uniform offset, and the image's output range checked by the
     // buffer resource.
-    constexpr int NOUT = 16 * 16 * NB / 256;
-    constexpr int OTPR = 256 / 16;  // threads per output row
-    static_assert(16 * 16 * NB == 256 * NOUT && NOUT * OTPR == 16 * NB, "output tile mapping");
+    constexpr int NOUT = 16 * 16 * NB / NT;
+    constexpr int OTPR = NT / 16;  // threads per output row
+    static_assert(16 * 16 * NB == NT * NOUT && NOUT * OTPR == 16 * NB, "output tile mapping");
     const int orow = tid / OTPR, ocol0 = NOUT * (tid % OTPR);
     PixV ov[NOUT];
 #pragma unroll
@@ -421,7 +428,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         constexpr int OPS = T::OPS, ORS = T::ORS;
 #pragma unroll
         for (int ci = 0; ci < NCH; ++ci) {
-            const int c = wave + 4 * ci;
+            const int c = wave + NW * ci;
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -459,10 +466,15 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
 #pragma unroll
             for (int k = 0; k < NOUT; ++k)
                 if (ow + k < s.OW) {
-                    if constexpr (CS == 8)
+                    if constexpr (CS == 16) {
+                        __builtin_amdgcn_raw_buffer_store_b128(ov[k].lo, yrs, (int)yoff, 2 * k * s.C, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(ov[k].hi, yrs, (int)yoff,
+                                                               2 * k * s.C + 16, 0);
+                    } else if constexpr (CS == 8) {
                         __builtin_amdgcn_raw_buffer_store_b128(ov[k], yrs, (int)yoff, 2 * k * s.C, 0);
-                    else
+                    } else {
                         __builtin_amdgcn_raw_buffer_store_b64(ov[k], yrs, (int)yoff, 2 * k * s.C, 0);
+                    }
                 }
         }
     }
@@ -477,7 +489,8 @@ static hipError_t launch_mfma(const Plan &p, const void *x, const void *w, const
             hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT>), dim3(p.grid), dim3(256), p.lds_bytes, st,
+    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT>), dim3(p.grid),
+                       dim3(MfmaTile<CS, NB, NFRAG>::NT), p.lds_bytes, st,
                        (const uint16_t *)x, (const uint16_t *)w, (const float *)bias,
                        (uint16_t *)y, p.s, p.aux0, p.aux1);
     return hipGetLastError();
@@ -509,6 +522,9 @@ struct MfmaEntry {
 static const MfmaEntry kMfma[] = {
     // compile-time filter heights of the common square filters
     MF(DT_F16, F16, 8, 4, 1, 8, 7),    MF(DT_BF16, BF16, 8, 4, 1, 8, 7),
+    // 32-byte pixel slices, 8 wavefronts (measured slower on 7x7: kept for
+    // DWCONV_MFMA_CS=16)
+    MF(DT_F16, F16, 16, 4, 1, 8, 7),   MF(DT_BF16, BF16, 16, 4, 1, 8, 7),
     MF(DT_F16, F16, 4, 4, 2, 0, 31),   MF(DT_BF16, BF16, 4, 4, 2, 0, 31),
     // any filter height
     MF(DT_F16, F16, 8, 4, 1, 8, 0),    MF(DT_F16, F16, 8, 4, 1, 0, 0),
@@ -524,7 +540,7 @@ bool plan_mfma(Plan &p) {
     if (p.dtype != DT_F16 && p.dtype != DT_BF16) return false;
     if (p.s.S != 1 || p.s.D != 1) return false;
     const int nfrag = (p.s.FW + 15) / 16;
-    // DWCONV_MFMA_CS=4|8 picks the channel slice (a tuning hook)
+    // DWCONV_MFMA_CS=4|8|16 picks the channel slice (a tuning hook)
     int want_cs = 0;
     if (const char *env = getenv("DWCONV_MFMA_CS")) want_cs = atoi(env);
     const MfmaEntry *e = nullptr;
@@ -535,8 +551,11 @@ bool plan_mfma(Plan &p) {
         if (k.fht && p.s.FH != k.fht) continue;
         if (want_cs && k.cs != want_cs) continue;
         const int need = k.lds(p.s);
+        // 16-channel slices run one 8-wavefront workgroup per CU; narrower
+        // ones aim for at least two per CU unless nothing else fits
         const bool last = k.cs == 4 || want_cs;
-        if (need <= 64 * 1024 || (last && need <= 160 * 1024)) {
+        const int cap = k.cs == 16 || last ? 160 * 1024 : 64 * 1024;
+        if (need <= cap) {
             e = &k;
             lds = need;
             break;
@@ -553,14 +572,14 @@ bool plan_mfma(Plan &p) {
     p.th = 16;
     p.aux0 = ncs;
     p.aux1 = nct;
-    p.block = 256;
+    p.block = e->cs >= 16 ? 512 : 256;
     p.grid = (uint32_t)blocks;
     p.lds_bytes = lds;
     p.launch = e->fn;
     snprintf(p.desc, sizeof(p.desc),
              "mfma: 16x16x32 banded GEMM, strips of %d cols x %d ch walked 16 rows at a "
-             "time, %d fragment(s) of 16 taps, LDS %d B, %u x 256",
-             16 * e->nb, e->cs, nfrag, lds, p.grid);
+             "time, %d fragment(s) of 16 taps, LDS %d B, %u x %d",
+             16 * e->nb, e->cs, nfrag, lds, p.grid, p.block);
     return true;
 }
 

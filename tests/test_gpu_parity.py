@@ -310,3 +310,36 @@ def test_each_lds_tile_entry(entry, monkeypatch):
             assert_matches_oracle(y, x, w, b, shape, fmt, f"lds {entry} tb={tb} {shape}")
             if fmt == "i8" and S % D == 0:
                 assert "tap-packed" in desc, desc
+
+
+MFMA_SLICES = {  # channel slice -> (dtype, F) combinations it is compiled for
+    4: [("f16", 31), ("bf16", 31), ("f16", 5), ("bf16", 9)],
+    8: [("f16", 7), ("bf16", 7), ("f16", 5), ("bf16", 17)],
+    16: [("f16", 7), ("bf16", 7)],
+}
+
+
+@pytest.mark.parametrize("cs", sorted(MFMA_SLICES))
+def test_each_mfma_channel_slice(cs, monkeypatch):
+    """Each MFMA channel slice (picked through the DWCONV_MFMA_CS tuning
+    hook) against the oracle: compiled and runtime filter heights, one and two
+    16-tap fragments, ragged strips, a short image and several slices."""
+    monkeypatch.setenv("DWCONV_MFMA_CS", str(cs))
+    rng = np.random.default_rng(31 + cs)
+    for fmt, F in MFMA_SLICES[cs]:
+        for (N, H, W, C) in [(1, 23, 37, 2 * cs), (2, 9, 70, cs), (1, 40, 17, 3 * cs)]:
+            shape = (N, H, W, C, F, F, 1, 1, F // 2)
+            if not supported(shape, fmt, "mfma"):
+                continue
+            wl = synth.Workload("mfma", fmt, *shape, ("normal", 0.0, 1.0),
+                                ("normal", 0.0, 1.0 / F), ("uniform", -0.1, 0.1),
+                                int(rng.integers(0, 2**31)))
+            x, w, b = make_inputs(wl)
+            h = dw.dwconv_create_variant(*shape, fmt, "mfma")
+            desc = dw.dwconv_plan_describe(h)
+            dw.dwconv_destroy(h)
+            assert f"x {cs} ch" in desc, desc
+            say(f"[gpu] mfma cs {cs} {fmt} shape {shape}")
+            y, used = run(x, w, b, shape, fmt, "mfma", guard=512)
+            assert used == "mfma", used
+            assert_matches_oracle(y, x, w, b, shape, fmt, f"mfma cs{cs} {shape}")
