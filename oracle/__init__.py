@@ -1,4 +1,4 @@
-"""CPU oracle for the forward depthwise 2-D convolution.
+"""CPU oracle for the depthwise 2-D convolution (forward and backward data).
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
 bench's ``cpu_baseline`` leg import this package.  The product path (the HIP
@@ -10,6 +10,8 @@ module only marshals numpy arrays into it:
 
 * ``fwd``     -- the whole output, plus sum|x*w| per output for float dtypes;
 * ``points``  -- selected outputs only (for shapes too large for a full pass);
+* ``bwd_data`` -- the gradient with respect to the input (float dtypes), plus
+  sum|dy*w| per input element;
 * ``decode``  -- widens stored fp32 / fp16 / bf16 values to float64 exactly.
 
 Storage formats (the same ones the library takes): ``"f32"`` float32,
@@ -47,6 +49,8 @@ def bind(path):
     lib.dwref_points_f64.restype = I
     lib.dwref_points_i8.argtypes = [P, P, P, P, ctypes.c_int64, P] + [I] * 9
     lib.dwref_points_i8.restype = I
+    lib.dwref_bwd_data_f64.argtypes = [P, P, P, P] + [I] * 11
+    lib.dwref_bwd_data_f64.restype = I
     return lib
 
 
@@ -160,3 +164,39 @@ def points(x, w, bias, stride, dilation, pad, dtype, idx, lib=None):
     if rc:
         raise ValueError("oracle rejected the shape or an index")
     return y, scale
+
+
+def bwd_data(dy, w, shape, dtype, threads=1, lib=None):
+    """Gradient with respect to the input, from its definition (the adjoint
+    of the forward pass; "Flash-DWC", section 5.1).  ``shape`` is the forward
+    operation (N, H, W, C, FH, FW, stride, dilation, pad); dy is
+    N x OH x OW x C in ``dtype`` (a float format).  Returns ``(dx, scale)`` in
+    fp64, dx N x H x W x C and scale the sum of |dy*w| per dx element."""
+    if dtype not in ("f32", "f16", "bf16"):
+        raise ValueError("backward data is defined here for float dtypes")
+    N, H, W, C, FH, FW, S, D, P = shape
+    lib = lib or _load()
+    OH = out_dim(H, FH, S, D, P, lib)
+    OW = out_dim(W, FW, S, D, P, lib)
+    if OH < 1 or OW < 1:
+        raise ValueError("no output: the filter span exceeds the padded input")
+    gg = np.ascontiguousarray(decode(dy, dtype))
+    ww = np.ascontiguousarray(decode(w, dtype))
+    if gg.shape != (N, OH, OW, C) or ww.shape != (FH, FW, C):
+        raise ValueError("dy must be N x OH x OW x C and w FH x FW x C")
+    dx = np.empty((N, H, W, C), np.float64)
+    scale = np.empty((N, H, W, C), np.float64)
+
+    def run(n0, n1):
+        return lib.dwref_bwd_data_f64(_ptr(gg), _ptr(ww), _ptr(dx), _ptr(scale),
+                                      N, H, W, C, FH, FW, S, D, P, n0, n1)
+    threads = max(1, min(int(threads), N))
+    if threads == 1:
+        rcs = [run(0, N)]
+    else:
+        bounds = np.linspace(0, N, threads + 1).astype(int)
+        with ThreadPoolExecutor(threads) as ex:
+            rcs = list(ex.map(run, bounds[:-1], bounds[1:]))
+    if any(rcs):
+        raise ValueError("oracle rejected the shape")
+    return dx, scale

@@ -199,3 +199,50 @@ int dwref_points_i8(const int8_t *x, const int8_t *w, const int32_t *bias,
     }
     return 0;
 }
+
+/* Backward data (the gradient with respect to the input), from its
+ * definition: the forward pass is linear in X, and its adjoint sends every
+ * output gradient dY[n,oh,ow,c] back along the taps that produced Y:
+ *
+ *   dX[n,ih,iw,c] = sum over (oh, ow, fh, fw) with oh*S - P + fh*D = ih and
+ *                   ow*S - P + fw*D = iw of dY[n,oh,ow,c] * W[fh,fw,c]
+ *
+ * ("Flash-DWC: Making Depthwise Convolution Compute-Efficient on GPUs",
+ * section 5.1: the input gradient of a depthwise convolution; for stride 1
+ * the same sum is a depthwise convolution of dY with the filter rotated by
+ * 180 degrees.)  Written here as the plain scatter over the forward's taps,
+ * for any stride, dilation and padding.  dy: N*OH*OW*C, w: FH*FW*C,
+ * dx and scale: N*H*W*C (scale = sum |dy*w| per dx element, may be NULL).
+ * Images [n0, n1) only.  Returns 0, or -1 on a bad shape. */
+int dwref_bwd_data_f64(const double *dy, const double *w, double *dx, double *scale,
+                       int N, int H, int W, int C, int FH, int FW, int S, int D, int P,
+                       int n0, int n1)
+{
+    int OH, OW;
+    if (!shape_ok(N, H, W, C, FH, FW, S, D, P, &OH, &OW)) return -1;
+    if (n0 < 0 || n1 > N || n0 > n1) return -1;
+    for (long long n = n0; n < n1; ++n)
+        for (long long i = (n * H) * (long long)W * C; i < ((n + 1) * H) * (long long)W * C; ++i) {
+            dx[i] = 0.0;
+            if (scale) scale[i] = 0.0;
+        }
+    for (long long n = n0; n < n1; ++n)
+        for (int oh = 0; oh < OH; ++oh)
+            for (int ow = 0; ow < OW; ++ow)
+                for (int c = 0; c < C; ++c) {
+                    double g = dy[((n * OH + oh) * (long long)OW + ow) * C + c];
+                    for (int fh = 0; fh < FH; ++fh) {
+                        int ih = oh * S - P + fh * D;
+                        if (ih < 0 || ih >= H) continue;  /* a padding tap: no input */
+                        for (int fw = 0; fw < FW; ++fw) {
+                            int iw = ow * S - P + fw * D;
+                            if (iw < 0 || iw >= W) continue;
+                            double prod = g * w[((long long)fh * FW + fw) * C + c];
+                            long long i = ((n * H + ih) * (long long)W + iw) * C + c;
+                            dx[i] += prod;
+                            if (scale) scale[i] += fabs(prod);
+                        }
+                    }
+                }
+    return 0;
+}
