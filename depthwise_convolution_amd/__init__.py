@@ -63,6 +63,12 @@ _lib.dwconv_plan_describe.argtypes = [_H]
 _lib.dwconv_plan_describe.restype = ctypes.c_char_p
 _lib.dwconv_status_string.argtypes = [_I]
 _lib.dwconv_status_string.restype = ctypes.c_char_p
+_lib.dwconv_bwd_data.argtypes = [_H, _H, _H, _H, _H]
+_lib.dwconv_bwd_data.restype = _I
+_lib.dwconv_bwd_data_supported.argtypes = [_H]
+_lib.dwconv_bwd_data_supported.restype = _I
+_lib.dwconv_bwd_data_describe.argtypes = [_H]
+_lib.dwconv_bwd_data_describe.restype = ctypes.c_char_p
 
 
 class DwconvError(RuntimeError):
@@ -155,6 +161,24 @@ def dwconv_fwd(h, x, w, bias, y, stream=None) -> None:
         raise DwconvError(rc, "dwconv_fwd")
 
 
+def dwconv_bwd_data(h, dy, w, dx, stream=None) -> None:
+    """Enqueues the backward-data pass: dx (N x H x W x C) from dy
+    (N x OH x OW x C) and the forward filter w.  Tensors or raw device
+    pointers; ``stream`` as for ``dwconv_fwd``.  Raises DwconvError
+    (unsupported) where the plan has no backward-data pass."""
+    rc = _lib.dwconv_bwd_data(h, _ptr(dy), _ptr(w), _ptr(dx), _stream(stream, dy))
+    if rc != 0:
+        raise DwconvError(rc, "dwconv_bwd_data")
+
+
+def dwconv_bwd_data_supported(h) -> bool:
+    return bool(_lib.dwconv_bwd_data_supported(h))
+
+
+def dwconv_bwd_data_describe(h) -> str:
+    return _lib.dwconv_bwd_data_describe(h).decode()
+
+
 class DepthwiseConv2d:
     """Owns a plan; ``conv(x, w, bias)`` allocates y with torch and runs the
     kernel.  x: N x H x W x C, w: FH x FW x C, bias: C (fp32, or int32 for
@@ -185,6 +209,15 @@ class DepthwiseConv2d:
                             dtype=getattr(torch, self._TORCH_Y[self.dtype]))
         dwconv_fwd(self.handle, x, w, bias, y, stream)
         return y
+
+    def backward_data(self, dy, w, dx=None, stream=None):
+        """dx = the input gradient for output gradient dy (dtype of x)."""
+        import torch
+        N, H, W, C = self.shape[:4]
+        if dx is None:
+            dx = torch.empty((N, H, W, C), device=dy.device, dtype=dy.dtype)
+        dwconv_bwd_data(self.handle, dy, w, dx, stream)
+        return dx
 
     def close(self):
         if self.handle:

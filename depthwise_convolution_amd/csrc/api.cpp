@@ -6,8 +6,29 @@
 #include "plan.h"
 
 struct dwconv_plan {
-    dw::Plan p;
+    dw::Plan p;      // forward
+    dw::Plan bwd;    // backward data, when has_bwd
+    bool has_bwd;
 };
+
+// Backward data at stride 1 is a forward pass over dY (N x OH x OW x C) with
+// the filter rotated by 180 degrees and padding D(F-1) - P, whose output is
+// exactly H x W ("Flash-DWC: Making Depthwise Convolution Compute-Efficient
+// on GPUs", section 5.1).  One padding serves both axes only for square
+// filters.  Float dtypes only.
+static bool plan_bwd_data(dw::Plan &b, const dw::Plan &f, int variant) {
+    const dw::Shape &s = f.s;
+    if (f.dtype == dw::DT_I8 || s.S != 1 || s.FH != s.FW) return false;
+    const int P2 = s.D * (s.FH - 1) - s.P;
+    if (P2 < 0) return false;
+    int rc = dw::make_plan(b, s.N, s.OH, s.OW, s.C, s.FH, s.FW, 1, s.D, P2, f.dtype, variant);
+    if (rc != DWCONV_OK && variant != dw::V_AUTO)
+        rc = dw::make_plan(b, s.N, s.OH, s.OW, s.C, s.FH, s.FW, 1, s.D, P2, f.dtype,
+                           dw::V_AUTO);
+    if (rc != DWCONV_OK || b.s.OH != s.H || b.s.OW != s.W) return false;
+    b.s.flip = 1;
+    return true;
+}
 
 extern "C" {
 
@@ -24,6 +45,7 @@ dwconv_status_t dwconv_create_variant(dwconv_handle_t *out, int N, int H, int W,
         delete h;
         return (dwconv_status_t)rc;
     }
+    h->has_bwd = plan_bwd_data(h->bwd, h->p, (int)variant);
     *out = h;
     return DWCONV_OK;
 }
@@ -48,6 +70,23 @@ dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
     dw::LaunchFn fn = ok_align ? p.launch : p.fallback;
     hipError_t e = fn(p, x, w, bias, y, stream);
     return e == hipSuccess ? DWCONV_OK : DWCONV_ERR_HIP;
+}
+
+dwconv_status_t dwconv_bwd_data(dwconv_handle_t h, const void *dy, const void *w, void *dx,
+                                hipStream_t stream) {
+    if (!h || !dy || !w || !dx) return DWCONV_ERR_INVALID_ARG;
+    if (!h->has_bwd) return DWCONV_ERR_UNSUPPORTED;
+    const dw::Plan &b = h->bwd;
+    bool ok_align = aligned16(dy) && aligned16(w) && aligned16(dx);
+    dw::LaunchFn fn = ok_align ? b.launch : b.fallback;
+    hipError_t e = fn(b, dy, w, nullptr, dx, stream);
+    return e == hipSuccess ? DWCONV_OK : DWCONV_ERR_HIP;
+}
+
+int dwconv_bwd_data_supported(dwconv_handle_t h) { return h && h->has_bwd ? 1 : 0; }
+
+const char *dwconv_bwd_data_describe(dwconv_handle_t h) {
+    return h && h->has_bwd ? h->bwd.desc : "";
 }
 
 dwconv_status_t dwconv_destroy(dwconv_handle_t h) {

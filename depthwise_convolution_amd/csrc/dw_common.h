@@ -15,7 +15,16 @@ struct Shape {
     int FH, FW;
     int S, D, P;
     int OH, OW;
+    int flip;  // 1: the filter is read rotated by 180 degrees (backward data)
 };
+
+// Offset (in taps) of filter tap (fh, fw) in the FH x FW x C filter.  The
+// backward-data pass is the forward pass with the filter rotated by 180
+// degrees ("Flash-DWC: Making Depthwise Convolution Compute-Efficient on
+// GPUs", section 5.1), read here in place instead of from a rotated copy.
+__host__ __device__ __forceinline__ int tap_index(const Shape &s, int fh, int fw) {
+    return s.flip ? (s.FH - 1 - fh) * s.FW + (s.FW - 1 - fw) : fh * s.FW + fw;
+}
 
 // ---------------------------------------------------------------------------
 // Element-type traits.  X: stored input/filter element; Acc: accumulator;

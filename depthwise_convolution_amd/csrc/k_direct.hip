@@ -38,13 +38,13 @@ k_direct(const typename DT::X *__restrict__ x, const typename DT::X *__restrict_
             int ih = oh * s.S - s.P + fh * s.D;
             if ((unsigned)ih >= (unsigned)s.H) continue;  // generated zero rows
             const typename DT::X *xr = x + ((n * s.H + ih) * (long long)s.W) * s.C + c;
-            const typename DT::X *wr = w + (long long)fh * s.FW * s.C + c;
+            const typename DT::X *wc = w + c;
             Acc row = Acc(0);
             for (int fw = 0; fw < s.FW; ++fw) {
                 int iw = ow * s.S - s.P + fw * s.D;
                 if ((unsigned)iw >= (unsigned)s.W) continue;  // generated zeros
                 row = mac<Acc>(row, DT::widen(xr[(long long)iw * s.C]),
-                               DT::widen(wr[(long long)fw * s.C]));
+                               DT::widen(wc[(long long)tap_index(s, fh, fw) * s.C]));
             }
             acc += row;
         }

@@ -121,7 +121,7 @@ k_ldstile(const typename DT::X *__restrict__ x, const typename DT::X *__restrict
         for (int fh = 0; fh < FH; ++fh)
 #pragma unroll
             for (int fw = 0; fw < FW; ++fw)
-                wt[fh][fw] = DT::widen(w[((long long)fh * FW + fw) * s.C + c]);
+                wt[fh][fw] = DT::widen(w[(long long)tap_index(s, fh, fw) * s.C + c]);
     };
     if (lane < s.C) load_filter(lane);
 
@@ -238,7 +238,7 @@ k_i8tap(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
         for (int fh = 0; fh < FH; ++fh)
 #pragma unroll
             for (int fw = 0; fw < 4 * NQ; ++fw)
-                t8[fh][fw] = fw < FW ? wc[(fh * FW + fw) * s.C] : (int8_t)0;
+                t8[fh][fw] = fw < FW ? wc[tap_index(s, fh, fw) * s.C] : (int8_t)0;
         bv = bias ? bias[c] : 0;
     };
     auto pack_filter = [&]() {

@@ -210,7 +210,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int fh = fh0 + RPP * k;
-                    if (fh < FH) v[k] = ld1(w + ((long long)fh * s.FW + fw) * s.C + c0);
+                    if (fh < FH) v[k] = ld1(w + (long long)tap_index(s, fh, fw) * s.C + c0);
                 }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {

@@ -154,7 +154,7 @@ k_rowwin(const typename DT::X *__restrict__ x, const typename DT::X *__restrict_
 #pragma unroll
         for (int fw = 0; fw < FW; ++fw) {
             X e[VEC];
-            load_vec<X, VEC>(e, w + ((long long)fh * FW + fw) * s.C + c0);
+            load_vec<X, VEC>(e, w + (long long)tap_index(s, fh, fw) * s.C + c0);
 #pragma unroll
             for (int v = 0; v < VEC; ++v) wt[fw][v] = DT::widen(e[v]);
         }
@@ -343,7 +343,7 @@ k_colstream(const typename DT::X *__restrict__ x, const typename DT::X *__restri
 #pragma unroll
         for (int fw = 0; fw < FW; ++fw) {
             X e[VEC];
-            load_vec<X, VEC>(e, w + ((long long)fh * FW + fw) * s.C + c0);
+            load_vec<X, VEC>(e, w + (long long)tap_index(s, fh, fw) * s.C + c0);
 #pragma unroll
             for (int v = 0; v < VEC; ++v) wt[fh][fw][v] = DT::widen(e[v]);
         }

@@ -1,5 +1,6 @@
 /*
- * dwconv.h -- C ABI of the MI355X (gfx950) forward depthwise 2-D convolution.
+ * dwconv.h -- C ABI of the MI355X (gfx950) depthwise 2-D convolution: the
+ * forward pass and its backward-data pass.
  *
  * Operation ("Flash-DWC: Making Depthwise Convolution Compute-Efficient on
  * GPUs", sections 2.1 and 2.3; "Tiles, halos and partial sums", section
@@ -103,6 +104,33 @@ dwconv_status_t dwconv_create_variant(dwconv_handle_t *out, int N, int H, int W,
  * handle, x, w or y, and DWCONV_ERR_HIP if the launch fails. */
 dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
                            const void *bias, void *y, hipStream_t stream);
+
+/* Backward data: the gradient with respect to the input of the forward
+ * operation the handle plans ("Flash-DWC: Making Depthwise Convolution
+ * Compute-Efficient on GPUs", section 5.1):
+ *
+ *   dX[n,ih,iw,c] = sum over (oh, ow, fh, fw) with oh*S - P + fh*D = ih and
+ *                   ow*S - P + fw*D = iw of dY[n,oh,ow,c] * Wt[fh,fw,c]
+ *
+ * At stride 1 this is a forward pass over dY with the filter rotated by 180
+ * degrees and padding D(F-1) - P, run here by the forward kernels reading
+ * the filter rotated in place (no copy is made).
+ *   dy  N x OH x OW x C   (float / fp16 / bf16, as y)
+ *   w   FH x FW x C       (the forward filter, not rotated)
+ *   dx  N x H  x W  x C   (as x; overwritten)
+ * Partial sums are fp32; fp16/bf16 dx is rounded once.  Enqueued on `stream`
+ * without waiting; dx must not overlap dy or w; any alignment is accepted.
+ * Returns DWCONV_ERR_INVALID_ARG for a NULL handle, dy, w or dx,
+ * DWCONV_ERR_UNSUPPORTED when the plan has no backward-data pass (int8; a
+ * stride other than 1; FH != FW; padding larger than D(F-1)), and
+ * DWCONV_ERR_HIP if the launch fails. */
+dwconv_status_t dwconv_bwd_data(dwconv_handle_t h, const void *dy, const void *w,
+                                void *dx, hipStream_t stream);
+
+/* 1 when dwconv_bwd_data can run the handle's operation, else 0 (also for
+ * NULL); and a one-line description of the kernel it launches ("" if none). */
+int dwconv_bwd_data_supported(dwconv_handle_t h);
+const char *dwconv_bwd_data_describe(dwconv_handle_t h);
 
 /* Frees the plan.  NULL is a no-op. */
 dwconv_status_t dwconv_destroy(dwconv_handle_t h);

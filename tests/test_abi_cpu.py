@@ -123,3 +123,41 @@ def test_one_hip_runtime_in_process():
     hip = {l.split()[-1] for l in maps if "libamdhip64" in l}
     hsa = {l.split()[-1] for l in maps if "libhsa-runtime64" in l}
     assert len(hip) == 1 and len(hsa) == 1, (hip, hsa)
+
+
+def test_bwd_data_support_matrix():
+    """Which forward plans carry a backward-data pass (host only, no GPU)."""
+    cases = [((2, 9, 9, 8, 3, 3, 1, 1, 1, "f32"), True),
+             ((2, 9, 9, 8, 7, 7, 1, 1, 3, "f16"), True),
+             ((1, 20, 20, 16, 31, 31, 1, 1, 15, "bf16"), True),
+             ((2, 9, 9, 8, 3, 3, 1, 2, 0, "f32"), True),     # dilated, no padding
+             ((2, 9, 9, 8, 3, 3, 2, 1, 1, "f32"), False),    # stride 2
+             ((2, 9, 9, 8, 3, 5, 1, 1, 1, "f32"), False),    # not square
+             ((2, 9, 9, 8, 3, 3, 1, 1, 3, "f32"), False),    # pad > D(F-1)
+             ((2, 9, 9, 8, 3, 3, 1, 1, 1, "i8"), False)]     # int8
+    for (N, H, W, C, FH, FW, S, D, P, dt), want in cases:
+        h = dw.dwconv_create(N, H, W, C, FH, FW, S, D, P, dt)
+        try:
+            assert dw.dwconv_bwd_data_supported(h) == want, (N, H, W, C, FH, FW, S, D, P, dt)
+            assert bool(dw.dwconv_bwd_data_describe(h)) == want
+        finally:
+            dw.dwconv_destroy(h)
+
+
+def test_bwd_data_argument_errors():
+    """NULL arguments and unsupported plans are refused before any launch."""
+    lib = dw._lib
+    h = dw.dwconv_create(1, 8, 8, 4, 3, 3, 2, 1, 1, "f32")   # stride 2: no bwd pass
+    g = dw.dwconv_create(1, 8, 8, 4, 3, 3, 1, 1, 1, "f32")
+    try:
+        fake = 1 << 40   # never dereferenced: every path below returns first
+        assert lib.dwconv_bwd_data(None, fake, fake, fake, None) == 1
+        assert lib.dwconv_bwd_data(g, None, fake, fake, None) == 1
+        assert lib.dwconv_bwd_data(g, fake, None, fake, None) == 1
+        assert lib.dwconv_bwd_data(g, fake, fake, None, None) == 1
+        assert lib.dwconv_bwd_data(h, fake, fake, fake, None) == 2
+        assert dw.dwconv_bwd_data_supported(None) is False
+        assert dw.dwconv_bwd_data_describe(None) == ""
+    finally:
+        dw.dwconv_destroy(h)
+        dw.dwconv_destroy(g)

@@ -1,0 +1,141 @@
+"""GPU parity of the backward-data pass through the C ABI against the CPU
+oracle's scatter form (oracle.bwd_data): the same elementwise bound as the
+forward pass, |dx - dx_exact| <= 1e-5 * sum|dy*w| + 1e-6 on the value before
+the one final rounding."""
+import numpy as np
+import pytest
+import torch
+
+import depthwise_convolution_amd as dw
+import oracle
+from oracle import check
+import synth
+from synth import WORKLOADS, make_inputs
+
+from gpu_helpers import to_dev, y_torch_dtype, say, DEV
+
+pytestmark = pytest.mark.gpu
+
+FAMILIES = ["auto", "direct", "rowwin", "ldstile", "mfma"]
+
+
+def run_bwd(dy, w, shape, fmt, variant="auto", guard=512):
+    """dx on the host; dx sits inside a NaN-filled buffer whose guard bands
+    are checked for stray writes."""
+    N, H, W, C, FH, FW, S, D, P = shape
+    h = dw.dwconv_create_variant(N, H, W, C, FH, FW, S, D, P, fmt, variant)
+    try:
+        assert dw.dwconv_bwd_data_supported(h)
+        desc = dw.dwconv_bwd_data_describe(h)
+        n_x = N * H * W * C
+        buf = torch.full((n_x + 2 * guard,), float("nan"), dtype=y_torch_dtype(fmt), device=DEV)
+        dx = buf[guard:guard + n_x]
+        dw.dwconv_bwd_data(h, to_dev(dy, fmt), to_dev(w, fmt), dx)
+        torch.cuda.synchronize()
+        host = (buf.view(torch.int16).cpu().numpy().view(np.uint16) if fmt == "bf16"
+                else buf.cpu().numpy())
+        band = np.concatenate([host[:guard], host[guard + n_x:]])
+        if fmt == "bf16":
+            assert np.all(band == band[0]) and band[0] & 0x7f80 == 0x7f80, "write outside dx"
+        else:
+            assert np.all(np.isnan(band)), "write outside dx"
+        return host[guard:guard + n_x].reshape(N, H, W, C), desc
+    finally:
+        dw.dwconv_destroy(h)
+
+
+def check_bwd(dx, dy, w, shape, fmt, what):
+    ref, scale = oracle.bwd_data(dy, w, shape, fmt, threads=8)
+    return check.assert_float(dx, fmt, ref, scale, what)
+
+
+def supported(shape, fmt, variant):
+    try:
+        h = dw.dwconv_create_variant(*shape, fmt, variant)
+    except dw.DwconvError as e:
+        if e.status == 2:
+            return False
+        raise
+    ok = dw.dwconv_bwd_data_supported(h)
+    dw.dwconv_destroy(h)
+    return ok
+
+
+def grads(shape, fmt, seed):
+    """A seeded output gradient and filter of the forward shape's sizes."""
+    N, H, W, C, FH, FW, S, D, P = shape
+    OH, OW = oracle.out_dim(H, FH, S, D, P), oracle.out_dim(W, FW, S, D, P)
+    wl = synth.Workload("bwd", fmt, N, OH, OW, C, FH, FW, 1, 1, 0, ("normal", 0.0, 1.0),
+                        ("normal", 0.0, 1.0 / (FH * FW) ** 0.5), None, seed)
+    dy, w, _ = make_inputs(wl)
+    return dy, w
+
+
+@pytest.mark.parametrize("name", ["mobilenet_f32_3x3", "convnext_f16_7x7"])
+def test_workload_bwd(name):
+    wl = WORKLOADS[name]
+    shape = (wl.N, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
+    dy, w = grads(shape, wl.dtype, 100 + wl.seed)
+    for fam in FAMILIES:
+        if fam != "auto" and not supported(shape, wl.dtype, fam):
+            continue
+        say(f"[gpu] bwd {name} family {fam}")
+        dx, desc = run_bwd(dy, w, shape, wl.dtype, fam)
+        rep = check_bwd(dx, dy, w, shape, wl.dtype, f"bwd {name}/{fam}")
+        say(f"      ok ({desc[:50]}) {rep}")
+
+
+def test_largekernel_bwd_two_images():
+    """The 31x31 bf16 layer's shape on two images (the oracle's full pass over
+    all 32 would take minutes)."""
+    wl = WORKLOADS["largekernel_bf16_31x31"]
+    shape = (2, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
+    dy, w = grads(shape, wl.dtype, 104)
+    say(f"[gpu] bwd largekernel x2")
+    dx, desc = run_bwd(dy, w, shape, wl.dtype)
+    check_bwd(dx, dy, w, shape, wl.dtype, "bwd largekernel")
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_bwd_random_small(fmt):
+    rng = np.random.default_rng({"f32": 61, "f16": 62, "bf16": 63}[fmt])
+    done = 0
+    while done < 30:
+        F = int(rng.choice([1, 3, 5, 7, 9, 17, 31]))
+        D = int(rng.integers(1, 3))
+        P = int(rng.integers(0, D * (F - 1) + 1))
+        H, W = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+        C = int(rng.choice([1, 3, 8, 16, 24, 64, 96]))
+        N = int(rng.integers(1, 3))
+        shape = (N, H, W, C, F, F, 1, D, P)
+        if oracle.out_dim(H, F, 1, D, P) < 1 or oracle.out_dim(W, F, 1, D, P) < 1:
+            continue
+        dy, w = grads(shape, fmt, int(rng.integers(0, 2**31)))
+        for fam in FAMILIES:
+            if fam != "auto" and not supported(shape, fmt, fam):
+                continue
+            say(f"[gpu] bwd {fmt} {shape} {fam}")
+            dx, _ = run_bwd(dy, w, shape, fmt, fam)
+            check_bwd(dx, dy, w, shape, fmt, f"bwd {shape}/{fam}")
+        done += 1
+
+
+def test_bwd_is_adjoint_of_fwd_on_gpu():
+    """<fwd(x), dy> = <x, bwd(dy)> with both passes on the GPU (fp32, small
+    integers: every product and sum is exact)."""
+    rng = np.random.default_rng(64)
+    for shape in [(2, 17, 13, 8, 3, 3, 1, 1, 1), (1, 30, 30, 16, 5, 5, 1, 2, 3),
+                  (1, 12, 21, 4, 7, 7, 1, 1, 6)]:
+        N, H, W, C, FH, FW, S, D, P = shape
+        OH, OW = oracle.out_dim(H, FH, S, D, P), oracle.out_dim(W, FW, S, D, P)
+        x = rng.integers(-4, 5, size=(N, H, W, C)).astype(np.float32)
+        w = rng.integers(-4, 5, size=(FH, FW, C)).astype(np.float32)
+        dy = rng.integers(-4, 5, size=(N, OH, OW, C)).astype(np.float32)
+        conv = dw.DepthwiseConv2d(*shape, dtype="f32")
+        y = conv(torch.from_numpy(x).to(DEV), torch.from_numpy(w).to(DEV))
+        dx = conv.backward_data(torch.from_numpy(dy).to(DEV), torch.from_numpy(w).to(DEV))
+        torch.cuda.synchronize()
+        conv.close()
+        lhs = float(np.sum(y.cpu().numpy().astype(np.float64) * dy))
+        rhs = float(np.sum(x.astype(np.float64) * dx.cpu().numpy()))
+        assert lhs == rhs, (shape, lhs, rhs)
