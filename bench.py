@@ -2,7 +2,8 @@
 """Throughput of the forward depthwise convolution on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--variant auto|direct|rowwin|ldstile|mfma] [--no-cpu]
+                    [--variant auto|direct|rowwin|ldstile|mfma] [--op fwd|bwd_data]
+                    [--no-cpu] [--no-copy]
 
 A step is one forward pass (one launch of the library's kernel) over one batch
 of seeded synthetic input.  The inputs are copied to HBM before timing.  So
@@ -41,6 +42,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "depthwise-conv fwd GB/s + GFLOP/s and fraction of HBM roofline, 1 MI355X"
+METRIC_BWD = ("depthwise-conv bwd-data GB/s + GFLOP/s and fraction of HBM roofline, "
+              "1 MI355X")
 DEFAULT_WORKLOAD = "mobilenet_f32_3x3"
 HBM_PEAK_GBS = 8000.0
 # Published dense peaks of MI355X used for compute-bound kernels.  The VALU
@@ -145,25 +148,35 @@ def copy_ceiling(torch, dev, stream, nbytes, sets, K, warmup):
             "bytes": 2 * half, "kind": "torch copy_ (device to device), back to back"}
 
 
-def cpu_baseline(wl, x, w, b, budget_s=20.0):
+def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd"):
     """The CPU oracle (test infrastructure, untuned) on this host's cores.
     Sample: whole images of the same workload, as many as fit the budget
-    after a one-image probe."""
+    after a one-image probe.  For the backward-data pass x holds dy."""
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
+
+    def run(n, t):
+        if op == "bwd_data":
+            shape = (n, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
+            oracle.bwd_data(x[:n], w, shape, wl.dtype, threads=t)
+        else:
+            oracle.fwd(x[:n], w, b, wl.stride, wl.dilation, wl.pad, wl.dtype, threads=t)
     t0 = time.perf_counter()
-    oracle.fwd(x[:1], w, b, wl.stride, wl.dilation, wl.pad, wl.dtype, threads=1)
+    run(1, 1)
     per_image_1t = time.perf_counter() - t0
     n = int(max(1, min(wl.N, budget_s * threads / max(per_image_1t, 1e-6))))
     n = max(min(n, wl.N), min(threads, wl.N))
     t0 = time.perf_counter()
-    oracle.fwd(x[:n], w, b, wl.stride, wl.dilation, wl.pad, wl.dtype, threads=threads)
+    run(n, threads)
     dt = time.perf_counter() - t0
     sub = type(wl)(**{**wl.__dict__, "N": n})
-    nbytes, flops, _, _ = work(sub)
+    nbytes, flops, OH, OW = work(sub)
+    if op == "bwd_data":
+        nbytes = (n * OH * OW + n * wl.H * wl.W) * wl.C * XB[wl.dtype] + \
+            wl.FH * wl.FW * wl.C * XB[wl.dtype]
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n} of {wl.N} images of {wl.name} (fp64/int64 loop nest, "
+            "sample": f"{n} of {wl.N} images of {wl.name} ({op}; fp64/int64 loop nest, "
                       f"{dt:.2f} s, {flops / dt / 1e9:.2f} GFLOP/s)"}
 
 
@@ -174,6 +187,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--variant", default="auto")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd_data"],
+                    help="the forward pass (default) or the backward-data pass")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-copy", action="store_true",
                     help="skip the device-to-device copy ceiling measurement")
@@ -190,8 +205,17 @@ def main():
 
     wl = WORKLOADS[args.workload]
     nbytes, flops, OH, OW = work(wl)
-    print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    bwd = args.op == "bwd_data"
+    print(f"[bench] {wl.name} ({args.op}): generating inputs", file=sys.stderr, flush=True)
     x, w, b = make_inputs(wl)
+    if bwd:
+        # the pass reads dy (N x OH x OW x C, drawn like x) and w, writes dx
+        # (N x H x W x C); no bias
+        x, _, _ = make_inputs(type(wl)(**{**wl.__dict__, "H": OH, "W": OW, "b_dist": None,
+                                           "seed": wl.seed + 100}))
+        b = None
+        nbytes = (wl.N * OH * OW + wl.N * wl.H * wl.W) * wl.C * XB[wl.dtype] + \
+            wl.FH * wl.FW * wl.C * XB[wl.dtype]
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -210,21 +234,38 @@ def main():
     sets = max(2, -(-MALL_FLUSH_BYTES // set_bytes))
     xd0 = to_dev(x, wl.dtype)
     xs = [xd0] + [xd0.clone() for _ in range(sets - 1)]
-    ys = [torch.empty((wl.N, OH, OW, wl.C), dtype=ydt, device=dev) for _ in range(sets)]
+    yshape = (wl.N, wl.H, wl.W, wl.C) if bwd else (wl.N, OH, OW, wl.C)
+    ys = [torch.empty(yshape, dtype=ydt, device=dev) for _ in range(sets)]
     wd = to_dev(w, wl.dtype)
     bd = to_dev(b, "f32" if wl.dtype != "i8" else "i8")
     torch.cuda.synchronize()
 
     h = dw.dwconv_create_variant(wl.N, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride,
                                  wl.dilation, wl.pad, wl.dtype, args.variant)
-    variant = dw.dwconv_plan_variant(h)
-    desc = dw.dwconv_plan_describe(h)
+    if bwd:
+        if not dw.dwconv_bwd_data_supported(h):
+            print(f"bench.py: {wl.name} has no backward-data pass in this build",
+                  file=sys.stderr)
+            sys.exit(2)
+        desc = dw.dwconv_bwd_data_describe(h)
+        variant = next(v for v in ("mfma", "ldstile", "direct", "rowwin", "colstream")
+                       if desc.startswith(v))
+        variant = "rowwin" if variant == "colstream" else variant
+
+        def step(i):
+            dw.dwconv_bwd_data(h, xs[i % sets], wd, ys[i % sets], stream)
+    else:
+        variant = dw.dwconv_plan_variant(h)
+        desc = dw.dwconv_plan_describe(h)
+
+        def step(i):
+            dw.dwconv_fwd(h, xs[i % sets], wd, bd, ys[i % sets], stream)
     stream = torch.cuda.current_stream(dev)
     print(f"[bench] plan: {desc}; {sets} buffer sets of {set_bytes / 1e6:.1f} MB",
           file=sys.stderr, flush=True)
 
     for i in range(args.warmup):
-        dw.dwconv_fwd(h, xs[i % sets], wd, bd, ys[i % sets], stream)
+        step(i)
     K = args.steps
     # pass 1: K steps back to back, bracketed by synchronisation (one GPU:
     # no barrier needed) -> whole-job throughput
@@ -234,7 +275,7 @@ def main():
     t_wall0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
-        dw.dwconv_fwd(h, xs[i % sets], wd, bd, ys[i % sets], stream)
+        step(i)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
@@ -247,7 +288,7 @@ def main():
     torch.cuda.synchronize()
     for i in range(K):
         ev0[i].record(stream)
-        dw.dwconv_fwd(h, xs[i % sets], wd, bd, ys[i % sets], stream)
+        step(i)
         ev1[i].record(stream)
     torch.cuda.synchronize()
     kern_ms = np.array([a.elapsed_time(z) for a, z in zip(ev0, ev1)])
@@ -259,7 +300,7 @@ def main():
     kavg_ms = ms_per_step
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kavg_ms * 1e-3) / 1e9
-    traffic = stored_traffic(wl.name, variant)
+    traffic = stored_traffic(wl.name + (":bwd_data" if bwd else ""), variant)
     print(f"[bench] kernel avg {kavg_ms * 1e3:.2f} us over the timed region; single "
           f"launches with events: mean {kern_ms.mean() * 1e3:.2f}, median "
           f"{np.median(kern_ms) * 1e3:.2f}, min {kern_ms.min() * 1e3:.2f}, p90 "
@@ -277,10 +318,10 @@ def main():
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, x, w, b)
+        cpu = cpu_baseline(wl, x, w, b, op=args.op)
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if not bwd else METRIC_BWD,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -292,7 +333,7 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "N": wl.N, "H": wl.H, "W": wl.W, "C": wl.C,
+        "config": {"workload": wl.name, "op": args.op, "N": wl.N, "H": wl.H, "W": wl.W, "C": wl.C,
                    "FH": wl.FH, "FW": wl.FW, "stride": wl.stride,
                    "dilation": wl.dilation, "pad": wl.pad, "bias": wl.b_dist is not None,
                    "layout": "NHWC", "parallelism": "single GPU"},
