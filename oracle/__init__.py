@@ -1,4 +1,5 @@
-"""CPU oracle for the depthwise 2-D convolution (forward and backward data).
+"""CPU oracle for the depthwise 2-D convolution (forward, backward data and
+backward filter).
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
 bench's ``cpu_baseline`` leg import this package.  The product path (the HIP
@@ -12,6 +13,8 @@ module only marshals numpy arrays into it:
 * ``points``  -- selected outputs only (for shapes too large for a full pass);
 * ``bwd_data`` -- the gradient with respect to the input (float dtypes), plus
   sum|dy*w| per input element;
+* ``bwd_filter`` -- the gradient with respect to the filter (float dtypes),
+  plus sum|x*dy| per tap;
 * ``decode``  -- widens stored fp32 / fp16 / bf16 values to float64 exactly.
 
 Storage formats (the same ones the library takes): ``"f32"`` float32,
@@ -51,6 +54,8 @@ def bind(path):
     lib.dwref_points_i8.restype = I
     lib.dwref_bwd_data_f64.argtypes = [P, P, P, P] + [I] * 11
     lib.dwref_bwd_data_f64.restype = I
+    lib.dwref_bwd_filter_f64.argtypes = [P, P, P, P] + [I] * 9
+    lib.dwref_bwd_filter_f64.restype = I
     return lib
 
 
@@ -200,3 +205,30 @@ def bwd_data(dy, w, shape, dtype, threads=1, lib=None):
     if any(rcs):
         raise ValueError("oracle rejected the shape")
     return dx, scale
+
+
+def bwd_filter(x, dy, shape, dtype, lib=None):
+    """Gradient with respect to the filter, from its definition ("Flash-DWC",
+    section 5.1).  ``shape`` is the forward operation (N, H, W, C, FH, FW,
+    stride, dilation, pad); x is N x H x W x C and dy N x OH x OW x C in
+    ``dtype`` (a float format).  Returns ``(dw, scale)`` in fp64, FH x FW x C,
+    scale the sum of |x*dy| per tap."""
+    if dtype not in ("f32", "f16", "bf16"):
+        raise ValueError("backward filter is defined here for float dtypes")
+    N, H, W, C, FH, FW, S, D, P = shape
+    lib = lib or _load()
+    OH = out_dim(H, FH, S, D, P, lib)
+    OW = out_dim(W, FW, S, D, P, lib)
+    if OH < 1 or OW < 1:
+        raise ValueError("no output: the filter span exceeds the padded input")
+    xx = np.ascontiguousarray(decode(x, dtype))
+    gg = np.ascontiguousarray(decode(dy, dtype))
+    if xx.shape != (N, H, W, C) or gg.shape != (N, OH, OW, C):
+        raise ValueError("x must be N x H x W x C and dy N x OH x OW x C")
+    dw = np.empty((FH, FW, C), np.float64)
+    scale = np.empty((FH, FW, C), np.float64)
+    rc = lib.dwref_bwd_filter_f64(_ptr(xx), _ptr(gg), _ptr(dw), _ptr(scale),
+                                  N, H, W, C, FH, FW, S, D, P)
+    if rc:
+        raise ValueError("oracle rejected the shape")
+    return dw, scale

@@ -246,3 +246,47 @@ int dwref_bwd_data_f64(const double *dy, const double *w, double *dx, double *sc
                 }
     return 0;
 }
+
+/* Backward filter (the gradient with respect to the filter), from its
+ * definition: the forward pass is linear in W, and the gradient of
+ * sum Y*dY with respect to W[fh,fw,c] is the sum, over every output that
+ * tap touched, of the input it multiplied times that output's gradient:
+ *
+ *   dW[fh,fw,c] = sum_{n, oh, ow} X[n, oh*S - P + fh*D, ow*S - P + fw*D, c]
+ *                                 * dY[n, oh, ow, c]
+ *
+ * with out-of-image X taken as zero ("Flash-DWC: Making Depthwise
+ * Convolution Compute-Efficient on GPUs", section 5.1: the filter gradient
+ * is a convolution of the input with the output gradient, a reduction over
+ * the batch and the output positions).  x: N*H*W*C, dy: N*OH*OW*C,
+ * dw and scale: FH*FW*C (scale = sum |x*dy| per tap, may be NULL).  Plain
+ * loop, one filter tap of one channel at a time, fp64.  Returns 0, or -1 on
+ * a bad shape. */
+int dwref_bwd_filter_f64(const double *x, const double *dy, double *dw, double *scale,
+                         int N, int H, int W, int C, int FH, int FW, int S, int D, int P)
+{
+    int OH, OW;
+    if (!shape_ok(N, H, W, C, FH, FW, S, D, P, &OH, &OW)) return -1;
+    for (int fh = 0; fh < FH; ++fh)
+        for (int fw = 0; fw < FW; ++fw)
+            for (int c = 0; c < C; ++c) {
+                double acc = 0.0, sabs = 0.0;
+                for (long long n = 0; n < N; ++n)
+                    for (int oh = 0; oh < OH; ++oh) {
+                        int ih = oh * S - P + fh * D;
+                        if (ih < 0 || ih >= H) continue;      /* padding: no input */
+                        for (int ow = 0; ow < OW; ++ow) {
+                            int iw = ow * S - P + fw * D;
+                            if (iw < 0 || iw >= W) continue;
+                            double prod = x[((n * H + ih) * (long long)W + iw) * C + c] *
+                                          dy[((n * OH + oh) * (long long)OW + ow) * C + c];
+                            acc += prod;
+                            sabs += fabs(prod);
+                        }
+                    }
+                long long o = ((long long)fh * FW + fw) * C + c;
+                dw[o] = acc;
+                if (scale) scale[o] = sabs;
+            }
+    return 0;
+}

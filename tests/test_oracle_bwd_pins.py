@@ -1,4 +1,4 @@
-"""Pins of the oracle's backward-data pass (CPU).
+"""Pins of the oracle's backward passes (CPU): backward data, then backward filter.
 
 The oracle writes the input gradient as the plain scatter over the forward's
 taps ("Flash-DWC: Making Depthwise Convolution Compute-Efficient on GPUs",
@@ -165,13 +165,137 @@ def _bwd_pins(lib):
 def test_bwd_mutants_are_caught(tmp_path):
     src = open(os.path.join(os.path.dirname(oracle.__file__), "dwref.c")).read()
     head, tail = src.split("int dwref_bwd_data_f64(", 1)
+    body, rest = tail.split("\n/* Backward filter", 1)   # this function only
     for name, (old, new) in BWD_MUTANTS.items():
-        assert tail.count(old) == 1, name
+        assert body.count(old) == 1, name
         path = tmp_path / f"bwd_{name}.c"
-        path.write_text(head + "int dwref_bwd_data_f64(" + tail.replace(old, new, 1))
+        path.write_text(head + "int dwref_bwd_data_f64(" + body.replace(old, new, 1) +
+                        "\n/* Backward filter" + rest)
         so = tmp_path / f"libbwd_{name}.so"
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", str(path),
                                "-o", str(so), "-lm"])
         failed = _bwd_pins(oracle.bind(str(so)))
         assert failed, f"mutant {name} passed every pin"
     assert _bwd_pins(oracle._load()) == []
+
+
+# ---------------------------------------------------------------- backward filter
+
+def run_bilinear(lib, cases=80, seed=11):
+    """<conv(x, w), dy> = <w, dW(x, dy)>: the forward pass is linear in w."""
+    rng = np.random.default_rng(seed)
+    for _ in range(cases):
+        shape = _case(rng)
+        N, H, W, C, FH, FW, S, D, P = shape
+        OH, OW = oracle.out_dim(H, FH, S, D, P), oracle.out_dim(W, FW, S, D, P)
+        x = rng.integers(-8, 9, size=(N, H, W, C)).astype(np.float32)
+        w = rng.integers(-8, 9, size=(FH, FW, C)).astype(np.float32)
+        dy = rng.integers(-8, 9, size=(N, OH, OW, C)).astype(np.float32)
+        y, _ = oracle.fwd(x, w, None, S, D, P, "f32", lib=lib)
+        dw, _ = oracle.bwd_filter(x, dy, shape, "f32", lib=lib)
+        lhs = float(np.sum(y * dy.astype(np.float64)))
+        rhs = float(np.sum(w.astype(np.float64) * dw))
+        assert lhs == rhs, (shape, lhs, rhs)
+
+
+def run_torch_filter(lib, cases=40, seed=12):
+    rng = np.random.default_rng(seed)
+    for _ in range(cases):
+        shape = _case(rng)
+        N, H, W, C, FH, FW, S, D, P = shape
+        OH, OW = oracle.out_dim(H, FH, S, D, P), oracle.out_dim(W, FW, S, D, P)
+        x = rng.standard_normal((N, H, W, C)).astype(np.float32)
+        dy = rng.standard_normal((N, OH, OW, C)).astype(np.float32)
+        xt = torch.from_numpy(x.astype(np.float64)).permute(0, 3, 1, 2)
+        wt = torch.zeros((C, 1, FH, FW), dtype=torch.float64, requires_grad=True)
+        y = torch.nn.functional.conv2d(xt, wt, stride=S, padding=P, dilation=D, groups=C)
+        y.backward(torch.from_numpy(dy.astype(np.float64)).permute(0, 3, 1, 2))
+        ref = wt.grad[:, 0].permute(1, 2, 0).numpy()
+        dw, _ = oracle.bwd_filter(x, dy, shape, "f32", lib=lib)
+        np.testing.assert_allclose(dw, ref, rtol=1e-12, atol=1e-12)
+
+
+def run_box_filter(lib, cases=40, seed=13):
+    """x = dy = 1: each tap's gradient counts the outputs whose input for that
+    tap lies inside the image, a product of two per-axis counts."""
+    rng = np.random.default_rng(seed)
+    for _ in range(cases):
+        shape = _case(rng)
+        N, H, W, C, FH, FW, S, D, P = shape
+        OH, OW = oracle.out_dim(H, FH, S, D, P), oracle.out_dim(W, FW, S, D, P)
+        dw, _ = oracle.bwd_filter(np.ones((N, H, W, C), np.float32),
+                                  np.ones((N, OH, OW, C), np.float32), shape, "f32", lib=lib)
+        rows = [sum(1 for o in range(OH) if 0 <= o * S - P + f * D < H) for f in range(FH)]
+        cols = [sum(1 for o in range(OW) if 0 <= o * S - P + f * D < W) for f in range(FW)]
+        want = N * np.outer(rows, cols)[:, :, None] * np.ones((1, 1, C))
+        assert np.array_equal(dw, want), shape
+
+
+def run_scale_filter(lib, cases=30, seed=14):
+    rng = np.random.default_rng(seed)
+    for _ in range(cases):
+        shape = _case(rng)
+        N, H, W, C, FH, FW, S, D, P = shape
+        OH, OW = oracle.out_dim(H, FH, S, D, P), oracle.out_dim(W, FW, S, D, P)
+        x = rng.integers(-8, 9, size=(N, H, W, C)).astype(np.float32)
+        dy = rng.integers(-8, 9, size=(N, OH, OW, C)).astype(np.float32)
+        _, scale = oracle.bwd_filter(x, dy, shape, "f32", lib=lib)
+        ref, _ = oracle.bwd_filter(np.abs(x), np.abs(dy), shape, "f32", lib=lib)
+        assert np.array_equal(scale, ref), shape
+
+
+def test_filter_bilinear_identity():
+    run_bilinear(None)
+
+
+def test_filter_matches_torch_autograd():
+    run_torch_filter(None)
+
+
+def test_filter_box_counts():
+    run_box_filter(None)
+
+
+def test_filter_scale_is_abs_pass():
+    run_scale_filter(None)
+
+
+BWF_MUTANTS = {
+    "pad_sign": ("int ih = oh * S - P + fh * D;", "int ih = oh * S + P + fh * D;"),
+    "no_width_dilation": ("int iw = ow * S - P + fw * D;", "int iw = ow * S - P + fw;"),
+    "no_height_stride": ("int ih = oh * S - P + fh * D;", "int ih = oh - P + fh * D;"),
+    "tap_transposed": ("long long o = ((long long)fh * FW + fw) * C + c;",
+                       "long long o = ((long long)(FH - 1 - fh) * FW + (FW - 1 - fw)) * C + c;"),
+    "dy_transposed": ("dy[((n * OH + oh) * (long long)OW + ow) * C + c];",
+                      "dy[((n * OW + ow) * (long long)OH + oh) * C + c];"),
+    "scale_signed": ("sabs += fabs(prod);", "sabs += prod;"),
+}
+
+
+def _bwf_pins(lib):
+    failed = []
+    for name, fn in [("bilinear", lambda: run_bilinear(lib, cases=40)),
+                     ("torch", lambda: run_torch_filter(lib, cases=20)),
+                     ("box", lambda: run_box_filter(lib, cases=20)),
+                     ("scale", lambda: run_scale_filter(lib, cases=15))]:
+        try:
+            fn()
+        except (AssertionError, ValueError):
+            failed.append(name)
+    return failed
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_bwd_filter_mutants_are_caught(tmp_path):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "dwref.c")).read()
+    head, tail = src.split("int dwref_bwd_filter_f64(", 1)
+    for name, (old, new) in BWF_MUTANTS.items():
+        assert tail.count(old) == 1, name
+        path = tmp_path / f"bwf_{name}.c"
+        path.write_text(head + "int dwref_bwd_filter_f64(" + tail.replace(old, new, 1))
+        so = tmp_path / f"libbwf_{name}.so"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", str(path),
+                               "-o", str(so), "-lm"])
+        failed = _bwf_pins(oracle.bind(str(so)))
+        assert failed, f"mutant {name} passed every pin"
+    assert _bwf_pins(oracle._load()) == []
