@@ -69,6 +69,12 @@ _lib.dwconv_bwd_data_supported.argtypes = [_H]
 _lib.dwconv_bwd_data_supported.restype = _I
 _lib.dwconv_bwd_data_describe.argtypes = [_H]
 _lib.dwconv_bwd_data_describe.restype = ctypes.c_char_p
+_lib.dwconv_bwd_filter_workspace.argtypes = [_H, ctypes.POINTER(ctypes.c_size_t)]
+_lib.dwconv_bwd_filter_workspace.restype = _I
+_lib.dwconv_bwd_filter.argtypes = [_H, _H, _H, _H, _H, _H]
+_lib.dwconv_bwd_filter.restype = _I
+_lib.dwconv_bwd_filter_describe.argtypes = [_H]
+_lib.dwconv_bwd_filter_describe.restype = ctypes.c_char_p
 
 
 class DwconvError(RuntimeError):
@@ -179,6 +185,28 @@ def dwconv_bwd_data_describe(h) -> str:
     return _lib.dwconv_bwd_data_describe(h).decode()
 
 
+def dwconv_bwd_filter_workspace(h) -> int:
+    """Bytes of workspace dwconv_bwd_filter needs for this plan."""
+    n = ctypes.c_size_t()
+    rc = _lib.dwconv_bwd_filter_workspace(h, ctypes.byref(n))
+    if rc != 0:
+        raise DwconvError(rc, "dwconv_bwd_filter_workspace")
+    return n.value
+
+
+def dwconv_bwd_filter(h, x, dy, dw, workspace, stream=None) -> None:
+    """Enqueues the backward-filter pass: dw (FH x FW x C, float32) from x and
+    dy; ``workspace`` holds at least dwconv_bwd_filter_workspace(h) bytes."""
+    rc = _lib.dwconv_bwd_filter(h, _ptr(x), _ptr(dy), _ptr(dw), _ptr(workspace),
+                                _stream(stream, x))
+    if rc != 0:
+        raise DwconvError(rc, "dwconv_bwd_filter")
+
+
+def dwconv_bwd_filter_describe(h) -> str:
+    return _lib.dwconv_bwd_filter_describe(h).decode()
+
+
 class DepthwiseConv2d:
     """Owns a plan; ``conv(x, w, bias)`` allocates y with torch and runs the
     kernel.  x: N x H x W x C, w: FH x FW x C, bias: C (fp32, or int32 for
@@ -218,6 +246,21 @@ class DepthwiseConv2d:
             dx = torch.empty((N, H, W, C), device=dy.device, dtype=dy.dtype)
         dwconv_bwd_data(self.handle, dy, w, dx, stream)
         return dx
+
+    def backward_filter(self, x, dy, dw=None, workspace=None, stream=None):
+        """dw (FH x FW x C, float32) = the filter gradient for input x and
+        output gradient dy; allocates dw and the workspace with torch when
+        they are not given."""
+        import torch
+        FH, FW = self.shape[4], self.shape[5]
+        C = self.shape[3]
+        if dw is None:
+            dw = torch.empty((FH, FW, C), device=x.device, dtype=torch.float32)
+        if workspace is None:
+            workspace = torch.empty(dwconv_bwd_filter_workspace(self.handle), device=x.device,
+                                    dtype=torch.uint8)
+        dwconv_bwd_filter(self.handle, x, dy, dw, workspace, stream)
+        return dw
 
     def close(self):
         if self.handle:

@@ -9,6 +9,8 @@ struct dwconv_plan {
     dw::Plan p;      // forward
     dw::Plan bwd;    // backward data, when has_bwd
     bool has_bwd;
+    dw::BwfPlan bwf; // backward filter, when has_bwf
+    bool has_bwf;
 };
 
 // Backward data at stride 1 is a forward pass over dY (N x OH x OW x C) with
@@ -46,6 +48,7 @@ dwconv_status_t dwconv_create_variant(dwconv_handle_t *out, int N, int H, int W,
         return (dwconv_status_t)rc;
     }
     h->has_bwd = plan_bwd_data(h->bwd, h->p, (int)variant);
+    h->has_bwf = dw::plan_bwd_filter(h->bwf, h->p);
     *out = h;
     return DWCONV_OK;
 }
@@ -87,6 +90,31 @@ int dwconv_bwd_data_supported(dwconv_handle_t h) { return h && h->has_bwd ? 1 : 
 
 const char *dwconv_bwd_data_describe(dwconv_handle_t h) {
     return h && h->has_bwd ? h->bwd.desc : "";
+}
+
+dwconv_status_t dwconv_bwd_filter_workspace(dwconv_handle_t h, size_t *bytes) {
+    if (!h || !bytes) return DWCONV_ERR_INVALID_ARG;
+    if (!h->has_bwf) return DWCONV_ERR_UNSUPPORTED;
+    *bytes = h->bwf.ws_bytes;
+    return DWCONV_OK;
+}
+
+dwconv_status_t dwconv_bwd_filter(dwconv_handle_t h, const void *x, const void *dy,
+                                  float *dw, void *workspace, hipStream_t stream) {
+    if (!h || !x || !dy || !dw || !workspace) return DWCONV_ERR_INVALID_ARG;
+    if (!h->has_bwf) return DWCONV_ERR_UNSUPPORTED;
+    const dw::BwfPlan &b = h->bwf;
+    // the 16-byte channel vectors need aligned x and dy; the workspace and
+    // dw are written as floats
+    if (((uintptr_t)workspace & 3u) != 0 || ((uintptr_t)dw & 3u) != 0)
+        return DWCONV_ERR_INVALID_ARG;
+    dw::BwfLaunchFn fn = aligned16(x) && aligned16(dy) ? b.vec_launch : b.one_launch;
+    hipError_t e = fn(b, x, dy, dw, workspace, stream);
+    return e == hipSuccess ? DWCONV_OK : DWCONV_ERR_HIP;
+}
+
+const char *dwconv_bwd_filter_describe(dwconv_handle_t h) {
+    return h && h->has_bwf ? h->bwf.desc : "";
 }
 
 dwconv_status_t dwconv_destroy(dwconv_handle_t h) {

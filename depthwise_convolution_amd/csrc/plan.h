@@ -35,6 +35,25 @@ struct Plan {
     char desc[192];
 };
 
+// Backward-filter plan: pass 1 writes Z chunk sums per filter element into a
+// caller-provided fp32 workspace, pass 2 merges them.  vec_launch needs
+// 16-byte aligned x and dy (and C * element size a multiple of 16);
+// one_launch takes any alignment.
+struct BwfPlan;
+using BwfLaunchFn = hipError_t (*)(const BwfPlan &, const void *x, const void *dy,
+                                   float *dw, void *ws, hipStream_t);
+struct BwfPlan {
+    Shape s;
+    int dtype;
+    int vec;              // channels per lane
+    int ncv, nfc;         // channel vectors, 8-tap column chunks
+    int Z, rpc;           // chunks of the (n, oh) rows, rows per chunk
+    size_t ws_bytes;      // Z * FH * FW * C floats
+    BwfLaunchFn vec_launch, one_launch;
+    char desc[160];
+};
+bool plan_bwd_filter(BwfPlan &b, const Plan &forward);
+
 // Output extent along one axis; 0 when not even one output fits.
 int out_extent(int in, int f, int s, int d, int p);
 

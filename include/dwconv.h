@@ -1,6 +1,6 @@
 /*
  * dwconv.h -- C ABI of the MI355X (gfx950) depthwise 2-D convolution: the
- * forward pass and its backward-data pass.
+ * forward pass and its backward-data and backward-filter passes.
  *
  * Operation ("Flash-DWC: Making Depthwise Convolution Compute-Efficient on
  * GPUs", sections 2.1 and 2.3; "Tiles, halos and partial sums", section
@@ -32,8 +32,9 @@
  * never rounded to the storage type before the end; fp16/bf16 outputs are
  * rounded once, to nearest even, from the fp32 sum.
  *
- * Ownership: the caller allocates and owns every buffer (device memory).  The
- * library allocates no device memory.  A handle holds host-side plan data
+ * Ownership: the caller allocates and owns every buffer (device memory),
+ * including the backward-filter workspace.  The library allocates no device
+ * memory.  A handle holds host-side plan data
  * only, is immutable after creation, and may be used from several host
  * threads and on several streams at once.
  *
@@ -131,6 +132,33 @@ dwconv_status_t dwconv_bwd_data(dwconv_handle_t h, const void *dy, const void *w
  * NULL); and a one-line description of the kernel it launches ("" if none). */
 int dwconv_bwd_data_supported(dwconv_handle_t h);
 const char *dwconv_bwd_data_describe(dwconv_handle_t h);
+
+/* Backward filter: the gradient with respect to the filter of the forward
+ * operation the handle plans ("Flash-DWC: Making Depthwise Convolution
+ * Compute-Efficient on GPUs", section 5.1):
+ *
+ *   dW[fh,fw,c] = sum_{n, oh, ow} X[n, oh*S - P + fh*D, ow*S - P + fw*D, c]
+ *                                 * dY[n, oh, ow, c]
+ *
+ * (out-of-image X is zero).  Any stride, dilation, padding and filter shape.
+ *   x          N x H x W x C      (as for the forward pass)
+ *   dy         N x OH x OW x C    (as y)
+ *   dw         FH x FW x C float  (fp32 for every float dtype; overwritten)
+ *   workspace  at least dwconv_bwd_filter_workspace() bytes of device
+ *              memory, 4-byte aligned, owned by the caller; its contents on
+ *              entry do not matter and are undefined on return
+ * The batch and output positions are split into chunks whose fp32 sums land
+ * in the workspace; a second kernel adds them pairwise, so the result is the
+ * same on every run (no atomics).  Enqueued on `stream` without waiting.
+ * Returns DWCONV_ERR_INVALID_ARG for a NULL argument or a misaligned dw or
+ * workspace, DWCONV_ERR_UNSUPPORTED for int8, DWCONV_ERR_HIP if a launch
+ * fails. */
+dwconv_status_t dwconv_bwd_filter_workspace(dwconv_handle_t h, size_t *bytes);
+dwconv_status_t dwconv_bwd_filter(dwconv_handle_t h, const void *x, const void *dy,
+                                  float *dw, void *workspace, hipStream_t stream);
+
+/* A one-line description of the backward-filter kernels ("" if none). */
+const char *dwconv_bwd_filter_describe(dwconv_handle_t h);
 
 /* Frees the plan.  NULL is a no-op. */
 dwconv_status_t dwconv_destroy(dwconv_handle_t h);

@@ -161,3 +161,26 @@ def test_bwd_data_argument_errors():
     finally:
         dw.dwconv_destroy(h)
         dw.dwconv_destroy(g)
+
+
+def test_bwd_filter_workspace_and_errors():
+    """Workspace sizes and argument errors of the backward-filter pass (host
+    only: every call below returns before any launch)."""
+    lib = dw._lib
+    h = dw.dwconv_create(2, 9, 9, 8, 3, 3, 1, 1, 1, "f32")
+    q = dw.dwconv_create(2, 9, 9, 8, 3, 3, 1, 1, 1, "i8")
+    try:
+        n = dw.dwconv_bwd_filter_workspace(h)
+        assert n > 0 and n % (3 * 3 * 8 * 4) == 0
+        assert dw.dwconv_bwd_filter_describe(h).startswith("bwf")
+        with pytest.raises(dw.DwconvError):
+            dw.dwconv_bwd_filter_workspace(q)
+        assert dw.dwconv_bwd_filter_describe(q) == ""
+        fake = 1 << 40
+        assert lib.dwconv_bwd_filter(h, None, fake, fake, fake, None) == 1
+        assert lib.dwconv_bwd_filter(h, fake, fake, fake, None, None) == 1
+        assert lib.dwconv_bwd_filter(h, fake, fake, fake + 2, fake, None) == 1   # dw misaligned
+        assert lib.dwconv_bwd_filter(q, fake, fake, fake, fake, None) == 2
+    finally:
+        dw.dwconv_destroy(h)
+        dw.dwconv_destroy(q)

@@ -139,3 +139,101 @@ def test_bwd_is_adjoint_of_fwd_on_gpu():
         lhs = float(np.sum(y.cpu().numpy().astype(np.float64) * dy))
         rhs = float(np.sum(x.astype(np.float64) * dx.cpu().numpy()))
         assert lhs == rhs, (shape, lhs, rhs)
+
+
+# ------------------------------------------------------------ backward filter
+
+def run_bwf(x, dy, shape, fmt):
+    """dw on the host (float32), from a NaN-filled buffer whose guard bands
+    are checked; the workspace is filled with garbage first."""
+    N, H, W, C, FH, FW, S, D, P = shape
+    h = dw.dwconv_create(N, H, W, C, FH, FW, S, D, P, fmt)
+    try:
+        nbytes = dw.dwconv_bwd_filter_workspace(h)
+        ws = torch.full((nbytes // 4 + 1,), float("nan"), dtype=torch.float32, device=DEV)
+        guard, n_w = 256, FH * FW * C
+        buf = torch.full((n_w + 2 * guard,), float("nan"), dtype=torch.float32, device=DEV)
+        dwt = buf[guard:guard + n_w]
+        dw.dwconv_bwd_filter(h, to_dev(x, fmt), to_dev(dy, fmt), dwt, ws)
+        torch.cuda.synchronize()
+        host = buf.cpu().numpy()
+        assert np.all(np.isnan(np.concatenate([host[:guard], host[guard + n_w:]]))), \
+            "write outside dw"
+        return host[guard:guard + n_w].reshape(FH, FW, C), dw.dwconv_bwd_filter_describe(h)
+    finally:
+        dw.dwconv_destroy(h)
+
+
+def check_bwf(dwv, x, dy, shape, fmt, what):
+    ref, scale = oracle.bwd_filter(x, dy, shape, fmt)
+    return check.assert_float(dwv, "f32", ref, scale, what)
+
+
+def bwf_inputs(shape, fmt, seed):
+    N, H, W, C, FH, FW, S, D, P = shape
+    OH, OW = oracle.out_dim(H, FH, S, D, P), oracle.out_dim(W, FW, S, D, P)
+    rng = np.random.default_rng(seed)
+    x = synth.to_storage(rng.standard_normal((N, H, W, C)), fmt)
+    dy = synth.to_storage(rng.standard_normal((N, OH, OW, C)), fmt)
+    return x, dy
+
+
+@pytest.mark.parametrize("name", ["mobilenet_f32_3x3", "convnext_f16_7x7",
+                                  "largekernel_bf16_31x31"])
+def test_workload_bwd_filter(name):
+    wl = WORKLOADS[name]
+    N = wl.N if wl.FH < 31 else 2   # the oracle's 31x31 pass on 32 images takes minutes
+    shape = (N, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
+    x, dy = bwf_inputs(shape, wl.dtype, 200 + wl.seed)
+    say(f"[gpu] bwd filter {name} N={N}")
+    dwv, desc = run_bwf(x, dy, shape, wl.dtype)
+    rep = check_bwf(dwv, x, dy, shape, wl.dtype, f"bwf {name}")
+    say(f"      ok ({desc[:60]}) {rep}")
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_bwd_filter_random_small(fmt):
+    rng = np.random.default_rng({"f32": 71, "f16": 72, "bf16": 73}[fmt])
+    for _ in range(30):
+        wl = synth.random_small(rng, fmt, max_hw=24, max_c=40, max_f=9)
+        shape = (wl.N, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
+        x, dy = bwf_inputs(shape, fmt, wl.seed)
+        say(f"[gpu] bwd filter {fmt} {shape}")
+        dwv, _ = run_bwf(x, dy, shape, fmt)
+        check_bwf(dwv, x, dy, shape, fmt, f"bwf {shape}")
+
+
+def test_bwd_filter_long_rows_and_many_chunks():
+    """Rows longer than one 64-pixel partial, a batch large enough for many
+    chunks, and a channel count with no 16-byte vectors."""
+    for shape, fmt in [((2, 9, 150, 16, 3, 5, 1, 1, 2), "f32"),
+                       ((8, 40, 40, 24, 7, 7, 1, 1, 3), "f16"),
+                       ((3, 33, 70, 7, 5, 3, 1, 2, 1), "bf16")]:
+        x, dy = bwf_inputs(shape, fmt, 7)
+        say(f"[gpu] bwd filter {fmt} {shape}")
+        dwv, desc = run_bwf(x, dy, shape, fmt)
+        check_bwf(dwv, x, dy, shape, fmt, f"bwf {shape} ({desc})")
+
+
+def test_bwd_filter_bilinear_and_deterministic():
+    """<fwd(x, w), dy> = <w, dW(x, dy)> with both passes on the GPU (fp32,
+    small integers: exact), and two runs agree bit for bit."""
+    rng = np.random.default_rng(74)
+    for shape in [(2, 17, 13, 8, 3, 3, 1, 1, 1), (1, 30, 30, 16, 5, 5, 2, 2, 3),
+                  (3, 12, 21, 4, 7, 3, 1, 1, 2)]:
+        N, H, W, C, FH, FW, S, D, P = shape
+        OH, OW = oracle.out_dim(H, FH, S, D, P), oracle.out_dim(W, FW, S, D, P)
+        x = rng.integers(-4, 5, size=(N, H, W, C)).astype(np.float32)
+        w = rng.integers(-4, 5, size=(FH, FW, C)).astype(np.float32)
+        dy = rng.integers(-4, 5, size=(N, OH, OW, C)).astype(np.float32)
+        conv = dw.DepthwiseConv2d(*shape, dtype="f32")
+        xd, dyd = torch.from_numpy(x).to(DEV), torch.from_numpy(dy).to(DEV)
+        y = conv(xd, torch.from_numpy(w).to(DEV))
+        g1 = conv.backward_filter(xd, dyd)
+        g2 = conv.backward_filter(xd, dyd)
+        torch.cuda.synchronize()
+        conv.close()
+        lhs = float(np.sum(y.cpu().numpy().astype(np.float64) * dy))
+        rhs = float(np.sum(w.astype(np.float64) * g1.cpu().numpy()))
+        assert lhs == rhs, (shape, lhs, rhs)
+        assert torch.equal(g1, g2)
