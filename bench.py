@@ -2,7 +2,8 @@
 """Throughput of the forward depthwise convolution on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--variant auto|direct|rowwin|ldstile|mfma] [--op fwd|bwd_data]
+                    [--variant auto|direct|rowwin|ldstile|mfma]
+                    [--op fwd|bwd_data|bwd_filter]
                     [--no-cpu] [--no-copy]
 
 A step is one forward pass (one launch of the library's kernel) over one batch
@@ -43,6 +44,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "depthwise-conv fwd GB/s + GFLOP/s and fraction of HBM roofline, 1 MI355X"
 METRIC_BWD = ("depthwise-conv bwd-data GB/s + GFLOP/s and fraction of HBM roofline, "
+              "1 MI355X")
+METRIC_BWF = ("depthwise-conv bwd-filter GB/s + GFLOP/s and fraction of HBM roofline, "
               "1 MI355X")
 DEFAULT_WORKLOAD = "mobilenet_f32_3x3"
 HBM_PEAK_GBS = 8000.0
@@ -95,7 +98,7 @@ def roofline(wl, variant, nbytes, flops, kernel_s, traffic):
 
 # the source file each kernel family is compiled from
 FAMILY_SOURCES = {"direct": "k_direct.hip", "rowwin": "k_rowwin.hip",
-                  "ldstile": "k_ldstile.hip", "mfma": "k_mfma.hip"}
+                  "ldstile": "k_ldstile.hip", "mfma": "k_mfma.hip", "bwf": "k_bwf.hip"}
 
 
 def kernel_sources_hash(variant):
@@ -156,7 +159,10 @@ def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd"):
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
 
     def run(n, t):
-        if op == "bwd_data":
+        if op == "bwd_filter":
+            shape = (n, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
+            oracle.bwd_filter(x[:n], w[:n], shape, wl.dtype)
+        elif op == "bwd_data":
             shape = (n, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
             oracle.bwd_data(x[:n], w, shape, wl.dtype, threads=t)
         else:
@@ -174,6 +180,9 @@ def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd"):
     if op == "bwd_data":
         nbytes = (n * OH * OW + n * wl.H * wl.W) * wl.C * XB[wl.dtype] + \
             wl.FH * wl.FW * wl.C * XB[wl.dtype]
+    if op == "bwd_filter":
+        nbytes = (n * OH * OW + n * wl.H * wl.W) * wl.C * XB[wl.dtype] + \
+            wl.FH * wl.FW * wl.C * 4
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n} of {wl.N} images of {wl.name} ({op}; fp64/int64 loop nest, "
@@ -187,8 +196,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--variant", default="auto")
-    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd_data"],
-                    help="the forward pass (default) or the backward-data pass")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd_data", "bwd_filter"],
+                    help="the forward pass (default), backward data or backward filter")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-copy", action="store_true",
                     help="skip the device-to-device copy ceiling measurement")
@@ -206,8 +215,17 @@ def main():
     wl = WORKLOADS[args.workload]
     nbytes, flops, OH, OW = work(wl)
     bwd = args.op == "bwd_data"
+    bwf = args.op == "bwd_filter"
     print(f"[bench] {wl.name} ({args.op}): generating inputs", file=sys.stderr, flush=True)
     x, w, b = make_inputs(wl)
+    if bwf:
+        # the pass reads x and dy (N x OH x OW x C, drawn like x) and writes
+        # the fp32 filter gradient; w holds dy here
+        w, _, _ = make_inputs(type(wl)(**{**wl.__dict__, "H": OH, "W": OW, "b_dist": None,
+                                           "seed": wl.seed + 200}))
+        b = None
+        nbytes = (wl.N * OH * OW + wl.N * wl.H * wl.W) * wl.C * XB[wl.dtype] + \
+            wl.FH * wl.FW * wl.C * 4
     if bwd:
         # the pass reads dy (N x OH x OW x C, drawn like x) and w, writes dx
         # (N x H x W x C); no bias
@@ -235,6 +253,11 @@ def main():
     xd0 = to_dev(x, wl.dtype)
     xs = [xd0] + [xd0.clone() for _ in range(sets - 1)]
     yshape = (wl.N, wl.H, wl.W, wl.C) if bwd else (wl.N, OH, OW, wl.C)
+    if bwf:
+        # dy rotates with x; dw is tiny and written every step
+        ydt, yshape = torch.float32, (wl.FH, wl.FW, wl.C)
+        wd0 = to_dev(w, wl.dtype)
+        dys = [wd0] + [wd0.clone() for _ in range(sets - 1)]
     ys = [torch.empty(yshape, dtype=ydt, device=dev) for _ in range(sets)]
     wd = to_dev(w, wl.dtype)
     bd = to_dev(b, "f32" if wl.dtype != "i8" else "i8")
@@ -242,7 +265,18 @@ def main():
 
     h = dw.dwconv_create_variant(wl.N, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride,
                                  wl.dilation, wl.pad, wl.dtype, args.variant)
-    if bwd:
+    if bwf:
+        desc = dw.dwconv_bwd_filter_describe(h)
+        if not desc:
+            print(f"bench.py: {wl.name} has no backward-filter pass in this build",
+                  file=sys.stderr)
+            sys.exit(2)
+        variant = "bwf"
+        wsb = torch.empty(dw.dwconv_bwd_filter_workspace(h), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            dw.dwconv_bwd_filter(h, xs[i % sets], dys[i % sets], ys[i % sets], wsb, stream)
+    elif bwd:
         if not dw.dwconv_bwd_data_supported(h):
             print(f"bench.py: {wl.name} has no backward-data pass in this build",
                   file=sys.stderr)
@@ -300,7 +334,7 @@ def main():
     kavg_ms = ms_per_step
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kavg_ms * 1e-3) / 1e9
-    traffic = stored_traffic(wl.name + (":bwd_data" if bwd else ""), variant)
+    traffic = stored_traffic(wl.name + (f":{args.op}" if args.op != "fwd" else ""), variant)
     print(f"[bench] kernel avg {kavg_ms * 1e3:.2f} us over the timed region; single "
           f"launches with events: mean {kern_ms.mean() * 1e3:.2f}, median "
           f"{np.median(kern_ms) * 1e3:.2f}, min {kern_ms.min() * 1e3:.2f}, p90 "
@@ -321,7 +355,7 @@ def main():
         cpu = cpu_baseline(wl, x, w, b, op=args.op)
 
     rec = {
-        "metric": METRIC if not bwd else METRIC_BWD,
+        "metric": {"fwd": METRIC, "bwd_data": METRIC_BWD, "bwd_filter": METRIC_BWF}[args.op],
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,

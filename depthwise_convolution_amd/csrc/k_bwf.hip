@@ -12,11 +12,12 @@
 // pass over a caller-provided workspace, with a pairwise sum.
 //
 // Pass 1 (k_bwf_partial): a lane owns one vector of VEC channels (one
-// 16-byte load, or one element), one filter row fh, a chunk of up to 8
+// 16-byte load, or one element), one filter row fh, a chunk of 3, 5 or 8
 // filter columns and a chunk of consecutive (n, oh) output rows.  It walks
-// each output row once: per output pixel one dY vector, and at stride 1 and
-// dilation 1 a sliding window of the 8 input vectors its taps need (one new
-// load per pixel); otherwise each tap's input is loaded directly.  Input
+// each output row once, in blocks of pixels whose loads are all issued before
+// their arithmetic: per pixel one dY vector, and at stride 1 and dilation 1
+// one window of input vectors shared by the block's taps; otherwise each
+// tap's input is loaded directly.  Input
 // positions outside the image count as zero.  Sums are fp32, with a fresh
 // partial every 64 pixels and every row; the chunk's totals go to the
 // workspace, ws[z][fh][fw][c].
@@ -35,15 +36,20 @@
 namespace dw {
 
 namespace {
-constexpr int BWF_TAPS = 8;   // filter columns per lane
 constexpr int BWF_SEG = 64;   // pixels per fresh partial
 }  // namespace
 
-template <class DT, int VEC, bool SLIDE>
+// BWF_TAPS: filter columns per lane (3, 5 or 8, the smallest chunk that
+// holds a filter row of up to 5 taps; wider rows take chunks of 8)
+template <class DT, int VEC, bool SLIDE, int BWF_TAPS>
 __global__ void __launch_bounds__(256)
 k_bwf_partial(const typename DT::X *__restrict__ x, const typename DT::X *__restrict__ dy,
               float *__restrict__ ws, Shape s, int ncv, int nfc, int rpc, long long lanes) {
     using X = typename DT::X;
+    // pixels per block of loads: enough loads in flight, registers <= 256
+    // (without the sliding window each pixel already loads 1 + TAPS vectors)
+    constexpr int U = !SLIDE ? (VEC == 1 ? 4 : 1)
+                             : VEC == 1 ? 16 : VEC == 4 ? 8 : BWF_TAPS == 8 ? 2 : 4;
     const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= lanes) return;
     const int cv = (int)(g % ncv);
@@ -87,7 +93,6 @@ k_bwf_partial(const typename DT::X *__restrict__ x, const typename DT::X *__rest
         if ((unsigned)ih >= (unsigned)s.H) continue;  // the whole row taps padding
         const X *xr = x + ((n * s.H + ih) * (long long)s.W) * s.C + c0;
         const X *gr = dy + ((n * s.OH + oh) * (long long)s.OW) * s.C + c0;
-        float win[BWF_TAPS][VEC];  // SLIDE: inputs of columns iw0 + j
         for (int seg = 0; seg < s.OW; seg += BWF_SEG) {
             const int seg1 = seg + BWF_SEG < s.OW ? seg + BWF_SEG : s.OW;
             float part[BWF_TAPS][VEC];
@@ -95,43 +100,47 @@ k_bwf_partial(const typename DT::X *__restrict__ x, const typename DT::X *__rest
             for (int j = 0; j < BWF_TAPS; ++j)
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) part[j][v] = 0.0f;
-            if constexpr (SLIDE) {
-                // stride 1, dilation 1: tap j of pixel ow reads column
-                // ow - P + fw0 + j, the next pixel's tap j - 1.  Entries are
-                // masked by the image only: one loaded for a tap past FW
-                // serves a valid tap after shifting (taps past FW are never
-                // written out).
+            // blocks of U pixels: every load of a block is issued before its
+            // arithmetic (pixels past the segment read as zero gradients)
+            for (int ow0 = seg; ow0 < seg1; ow0 += U) {
+                float gv[U][VEC];
 #pragma unroll
-                for (int j = 0; j < BWF_TAPS; ++j) {
-                    const int iw = seg - s.P + fw0 + j;
-                    const bool ok = (unsigned)iw < (unsigned)s.W;
-                    load(win[j], xr + (long long)(ok ? iw : 0) * s.C, ok);
-                }
-            }
-            for (int ow = seg; ow < seg1; ++ow) {
-                float gv[VEC];
-                load(gv, gr + (long long)ow * s.C, true);
-                if constexpr (!SLIDE) {
-#pragma unroll
-                    for (int j = 0; j < BWF_TAPS; ++j) {
-                        const int iw = ow * s.S - s.P + (fw0 + j) * s.D;
-                        const bool ok = (unsigned)iw < (unsigned)s.W && fw0 + j < s.FW;
-                        load(win[j], xr + (long long)(ok ? iw : 0) * s.C, ok);
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < BWF_TAPS; ++j)
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v)
-                        part[j][v] = __builtin_fmaf(win[j][v], gv[v], part[j][v]);
+                for (int u = 0; u < U; ++u)
+                    load(gv[u], gr + (long long)(ow0 + u < seg1 ? ow0 + u : ow0) * s.C,
+                         ow0 + u < seg1);
                 if constexpr (SLIDE) {
+                    // stride 1, dilation 1: tap j of pixel ow0 + u reads
+                    // column ow0 + u - P + fw0 + j, window entry u + j
+                    float xw[U + BWF_TAPS - 1][VEC];
 #pragma unroll
-                    for (int j = 0; j + 1 < BWF_TAPS; ++j)
+                    for (int k = 0; k < U + BWF_TAPS - 1; ++k) {
+                        const int iw = ow0 - s.P + fw0 + k;
+                        const bool ok = (unsigned)iw < (unsigned)s.W;
+                        load(xw[k], xr + (long long)(ok ? iw : 0) * s.C, ok);
+                    }
 #pragma unroll
-                        for (int v = 0; v < VEC; ++v) win[j][v] = win[j + 1][v];
-                    const int iw = ow + 1 - s.P + fw0 + BWF_TAPS - 1;
-                    const bool ok = (unsigned)iw < (unsigned)s.W;
-                    load(win[BWF_TAPS - 1], xr + (long long)(ok ? iw : 0) * s.C, ok);
+                    for (int u = 0; u < U; ++u)
+#pragma unroll
+                        for (int j = 0; j < BWF_TAPS; ++j)
+#pragma unroll
+                            for (int v = 0; v < VEC; ++v)
+                                part[j][v] = __builtin_fmaf(xw[u + j][v], gv[u][v], part[j][v]);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        float xw[BWF_TAPS][VEC];
+#pragma unroll
+                        for (int j = 0; j < BWF_TAPS; ++j) {
+                            const int iw = (ow0 + u) * s.S - s.P + (fw0 + j) * s.D;
+                            const bool ok = (unsigned)iw < (unsigned)s.W && fw0 + j < s.FW;
+                            load(xw[j], xr + (long long)(ok ? iw : 0) * s.C, ok);
+                        }
+#pragma unroll
+                        for (int j = 0; j < BWF_TAPS; ++j)
+#pragma unroll
+                            for (int v = 0; v < VEC; ++v)
+                                part[j][v] = __builtin_fmaf(xw[j][v], gv[u][v], part[j][v]);
+                    }
                 }
             }
 #pragma unroll
@@ -194,11 +203,11 @@ k_bwf_reduce(const float *__restrict__ ws, float *__restrict__ dw, long long ele
     dw[e] = total;
 }
 
-template <class DT, int VEC, bool SLIDE>
+template <class DT, int VEC, bool SLIDE, int TAPS>
 static hipError_t launch_bwf(const BwfPlan &b, const void *x, const void *dy, float *dw,
                              void *ws, hipStream_t st) {
     const long long lanes = (long long)b.ncv * b.nfc * b.s.FH * b.Z;
-    hipLaunchKernelGGL((k_bwf_partial<DT, VEC, SLIDE>), dim3((uint32_t)((lanes + 255) / 256)),
+    hipLaunchKernelGGL((k_bwf_partial<DT, VEC, SLIDE, TAPS>), dim3((uint32_t)((lanes + 255) / 256)),
                        dim3(256), 0, st, (const typename DT::X *)x,
                        (const typename DT::X *)dy, (float *)ws, b.s, b.ncv, b.nfc, b.rpc, lanes);
     hipError_t e = hipGetLastError();
@@ -218,9 +227,10 @@ bool plan_bwd_filter(BwfPlan &b, const Plan &f) {
     const bool vec_ok = (f.s.C * eb) % 16 == 0;
     const int VEC = vec_ok ? 16 / eb : 1;
     const bool slide = f.s.S == 1 && f.s.D == 1;
+    const int taps = f.s.FW <= 3 ? 3 : f.s.FW <= 5 ? 5 : 8;
     b.vec = VEC;
     b.ncv = f.s.C / VEC;
-    b.nfc = (f.s.FW + BWF_TAPS - 1) / BWF_TAPS;
+    b.nfc = (f.s.FW + taps - 1) / taps;
     // about 128K lanes, each over a chunk of whole output rows, and no chunk
     // adding up more than 64 partials of 64 pixels (the error bound)
     const long long nrows = (long long)f.s.N * f.s.OH;
@@ -237,27 +247,32 @@ bool plan_bwd_filter(BwfPlan &b, const Plan &f) {
     b.Z = (int)Z;
     b.rpc = (int)rpc;
     b.ws_bytes = (size_t)Z * f.s.FH * f.s.FW * f.s.C * sizeof(float);
-    b.vec_launch = nullptr;
+#define BWF_PICK(DTT, V)                                                                   \
+    (slide ? (taps == 3 ? launch_bwf<DTT, V, true, 3>                                      \
+                        : taps == 5 ? launch_bwf<DTT, V, true, 5> : launch_bwf<DTT, V, true, 8>) \
+           : (taps == 3 ? launch_bwf<DTT, V, false, 3>                                     \
+                        : taps == 5 ? launch_bwf<DTT, V, false, 5> : launch_bwf<DTT, V, false, 8>))
     switch (f.dtype) {
         case DT_F32:
-            b.vec_launch = slide ? launch_bwf<F32, 4, true> : launch_bwf<F32, 4, false>;
-            b.one_launch = slide ? launch_bwf<F32, 1, true> : launch_bwf<F32, 1, false>;
+            b.vec_launch = BWF_PICK(F32, 4);
+            b.one_launch = BWF_PICK(F32, 1);
             break;
         case DT_F16:
-            b.vec_launch = slide ? launch_bwf<F16, 8, true> : launch_bwf<F16, 8, false>;
-            b.one_launch = slide ? launch_bwf<F16, 1, true> : launch_bwf<F16, 1, false>;
+            b.vec_launch = BWF_PICK(F16, 8);
+            b.one_launch = BWF_PICK(F16, 1);
             break;
         case DT_BF16:
-            b.vec_launch = slide ? launch_bwf<BF16, 8, true> : launch_bwf<BF16, 8, false>;
-            b.one_launch = slide ? launch_bwf<BF16, 1, true> : launch_bwf<BF16, 1, false>;
+            b.vec_launch = BWF_PICK(BF16, 8);
+            b.one_launch = BWF_PICK(BF16, 1);
             break;
         default: return false;
     }
+#undef BWF_PICK
     if (!vec_ok) b.vec_launch = b.one_launch;
     snprintf(b.desc, sizeof(b.desc),
              "bwf: %d ch/lane x filter row x %d taps, Z=%d chunks of %d rows (%s), "
              "pairwise merge, workspace %zu B",
-             VEC, BWF_TAPS, b.Z, b.rpc, slide ? "sliding window" : "direct taps", b.ws_bytes);
+             VEC, taps, b.Z, b.rpc, slide ? "sliding window" : "direct taps", b.ws_bytes);
     return true;
 }
 
