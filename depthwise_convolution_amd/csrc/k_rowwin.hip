@@ -213,7 +213,10 @@ __device__ __forceinline__ void load_vec_nt(E (&dst)[VEC], const E *src) {
     __builtin_memcpy(dst, &v, sizeof(V));
 }
 
-template <class X, int VEC, int NWIN, bool NTL>
+// NTL: 0 cached loads; 1 non-temporal loads; 2 non-temporal loads only for
+// the window pixels [NT0, NT1) that no neighbouring strip reads (the shared
+// edge pixels stay cached in L2 for the neighbour)
+template <class X, int VEC, int NWIN, int NTL, int NT0, int NT1>
 __device__ __forceinline__ void fetch_run(X (&e)[NWIN][VEC], const X *xn, int ih, int H,
                                           int iw0, int W, int C) {
     const int ihc = (unsigned)ih < (unsigned)H ? ih : 0;
@@ -222,7 +225,7 @@ __device__ __forceinline__ void fetch_run(X (&e)[NWIN][VEC], const X *xn, int ih
     for (int j = 0; j < NWIN; ++j) {
         const int iw = iw0 + j;
         const int iwc = (unsigned)iw < (unsigned)W ? iw : 0;
-        if constexpr (NTL)
+        if (NTL == 1 || (NTL == 2 && j >= NT0 && j < NT1))  // j is unrolled
             load_vec_nt<X, VEC>(e[j], xr + (long long)iwc * C);
         else
             load_vec<X, VEC>(e[j], xr + (long long)iwc * C);
@@ -233,7 +236,7 @@ __device__ __forceinline__ void fetch_run(X (&e)[NWIN][VEC], const X *xn, int ih
 // Bottom-up visits input row i = NROW-1 .. 0; output row o then receives its
 // filter rows in the order fh = FH-1 .. 0, starts (bias) at fh = FH-1 and is
 // stored after fh = 0.
-template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, bool NTL,
+template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, int NTL,
           bool UP>
 __device__ __forceinline__ void colstream_walk(const typename DT::X *xn,
                                                const typename DT::Acc (&wt)[FH][FW][VEC],
@@ -252,14 +255,14 @@ __device__ __forceinline__ void colstream_walk(const typename DT::X *xn,
     X raw[RING][NWIN][VEC];
 #pragma unroll
     for (int k = 0; k < PF && k < NROW; ++k)
-        fetch_run<X, VEC, NWIN, NTL>(raw[k % RING], xn, ih0 + row_of(k), s.H, iw0, s.W, s.C);
+        fetch_run<X, VEC, NWIN, NTL, (FW - 1) * D, TM>(raw[k % RING], xn, ih0 + row_of(k), s.H, iw0, s.W, s.C);
 
     Acc acc[TH][TM][VEC];
 #pragma unroll
     for (int k = 0; k < NROW; ++k) {
         const int i = row_of(k);
         if (k + PF < NROW)
-            fetch_run<X, VEC, NWIN, NTL>(raw[(k + PF) % RING], xn, ih0 + row_of(k + PF), s.H, iw0,
+            fetch_run<X, VEC, NWIN, NTL, (FW - 1) * D, TM>(raw[(k + PF) % RING], xn, ih0 + row_of(k + PF), s.H, iw0,
                                     s.W, s.C);
         const bool row_ok = (unsigned)(ih0 + i) < (unsigned)s.H;
         Acc xw[NWIN][VEC];
@@ -313,7 +316,7 @@ __device__ __forceinline__ void colstream_walk(const typename DT::X *xn,
 // directions, so that the two strips on either side of every boundary reach
 // the shared rows at about the same time (both at the start of their walk, or
 // both at the end) and the second request finds them in L2.
-template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, bool NTL>
+template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, int NTL>
 __global__ void __launch_bounds__(256)
 k_colstream(const typename DT::X *__restrict__ x, const typename DT::X *__restrict__ w,
             const typename DT::Bias *__restrict__ bias, typename DT::Y *__restrict__ y,
@@ -371,7 +374,7 @@ static hipError_t launch_rowwin(const Plan &p, const void *x, const void *w,
     return hipGetLastError();
 }
 
-template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, bool NTL>
+template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, int NTL>
 static hipError_t launch_colstream(const Plan &p, const void *x, const void *w,
                                    const void *bias, void *y, hipStream_t st) {
     int ohg_n = (p.s.OH + TH - 1) / TH;
@@ -399,6 +402,7 @@ struct RegTile {
      launch_colstream<DTT, VEC_, FH_, FW_, TM_, TH_, D_, PF_, NT_, NTL_>}
 
 static const RegTile kTiles[] = {
+    CS(DT_F32, F32, 3, 3, 1, 4, 4, 14, 2, 1, 2),
     CS(DT_F32, F32, 3, 3, 1, 4, 4, 14, 2, 1, 0),
     CS(DT_F32, F32, 3, 3, 1, 4, 2, 28, 2, 1, 0),
     CS(DT_F32, F32, 3, 3, 1, 4, 4, 8, 2, 1, 0),
@@ -430,7 +434,8 @@ static bool tile_matches(const RegTile &k, const Plan &p) {
 bool plan_rowwin(Plan &p) {
     const RegTile *e = nullptr;
     // DWCONV_TILE="TMxTH[pPF[flags]]", flags: n = non-temporal y stores,
-    // l = non-temporal x loads (a tuning hook; the table order is the default)
+    // l = non-temporal x loads, i = non-temporal loads of the pixels no other
+    // strip reads (a tuning hook; the table order is the default)
     int want_tm = 0, want_th = -1, want_pf = -1, want_nt = -1, want_ntl = -1;
     if (const char *env = getenv("DWCONV_TILE")) {
         char rest[8] = {0};
@@ -438,7 +443,7 @@ bool plan_rowwin(Plan &p) {
         if (got < 2) want_th = -1;
         if (got >= 3) {
             want_nt = strchr(rest, 'n') != nullptr;
-            want_ntl = strchr(rest, 'l') != nullptr;
+            want_ntl = strchr(rest, 'l') != nullptr ? 1 : strchr(rest, 'i') != nullptr ? 2 : 0;
         }
     }
     for (const auto &k : kTiles) {
@@ -472,7 +477,9 @@ bool plan_rowwin(Plan &p) {
                  "colstream: VEC=%d ch/lane, TM=%d x TH=%d outputs/lane, %dx%d D=%d, "
                  "prefetch %d rows%s%s, %u x %d",
                  e->vec, e->tm, e->th, e->fh, e->fw, e->d, e->pf,
-                 e->nt ? ", nt stores" : "", e->ntl ? ", nt loads" : "", p.grid, p.block);
+                 e->nt ? ", nt stores" : "",
+                 e->ntl == 1 ? ", nt loads" : e->ntl == 2 ? ", nt loads of unshared pixels" : "",
+                 p.grid, p.block);
     else
         snprintf(p.desc, sizeof(p.desc),
                  "rowwin: VEC=%d ch/lane, TM=%d outputs/lane, FW=%d S=%d D=%d, %u x %d",
