@@ -81,7 +81,7 @@ def roofline(wl, variant, nbytes, flops, kernel_s, traffic):
     of the units the kernel uses (matrix cores for the mfma family, VALU
     otherwise) takes longer than moving the algorithmic bytes at 8 TB/s."""
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
-    if variant == "mfma":
+    if variant in ("mfma", "bwf_mfma"):
         bound, peak = "mfma", MFMA_PEAK_TFLOPS[wl.dtype]
     else:
         bound, peak = "alu", VALU_PEAK_TFLOPS
@@ -96,9 +96,10 @@ def roofline(wl, variant, nbytes, flops, kernel_s, traffic):
             "hbm_gbs": round(nbytes / kernel_s / 1e9, 2)}
 
 
-# the source file each kernel family is compiled from
-FAMILY_SOURCES = {"direct": "k_direct.hip", "rowwin": "k_rowwin.hip",
-                  "ldstile": "k_ldstile.hip", "mfma": "k_mfma.hip", "bwf": "k_bwf.hip"}
+# the source files each kernel family is compiled from
+FAMILY_SOURCES = {"direct": ("k_direct.hip",), "rowwin": ("k_rowwin.hip",),
+                  "ldstile": ("k_ldstile.hip",), "mfma": ("k_mfma.hip",),
+                  "bwf": ("k_bwf.hip",), "bwf_mfma": ("k_bwf_mfma.hip", "k_bwf.hip")}
 
 
 def kernel_sources_hash(variant):
@@ -107,7 +108,7 @@ def kernel_sources_hash(variant):
     it matches the hash they were taken with."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "depthwise_convolution_amd", "csrc")
-    for f in ("dw_common.h", "plan.h", FAMILY_SOURCES[variant]):
+    for f in ("dw_common.h", "plan.h") + FAMILY_SOURCES[variant]:
         h.update(f.encode())
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
@@ -271,7 +272,7 @@ def main():
             print(f"bench.py: {wl.name} has no backward-filter pass in this build",
                   file=sys.stderr)
             sys.exit(2)
-        variant = "bwf"
+        variant = "bwf_mfma" if desc.startswith("bwf mfma") else "bwf"
         wsb = torch.empty(dw.dwconv_bwd_filter_workspace(h), dtype=torch.uint8, device=dev)
 
         def step(i):

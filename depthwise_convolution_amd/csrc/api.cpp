@@ -104,11 +104,14 @@ dwconv_status_t dwconv_bwd_filter(dwconv_handle_t h, const void *x, const void *
     if (!h || !x || !dy || !dw || !workspace) return DWCONV_ERR_INVALID_ARG;
     if (!h->has_bwf) return DWCONV_ERR_UNSUPPORTED;
     const dw::BwfPlan &b = h->bwf;
-    // the 16-byte channel vectors need aligned x and dy; the workspace and
-    // dw are written as floats
+    // the 16-byte channel vectors need aligned x and dy (the matrix-core
+    // pass also a 16-byte aligned workspace); the workspace and dw are
+    // written as floats
     if (((uintptr_t)workspace & 3u) != 0 || ((uintptr_t)dw & 3u) != 0)
         return DWCONV_ERR_INVALID_ARG;
-    dw::BwfLaunchFn fn = aligned16(x) && aligned16(dy) ? b.vec_launch : b.one_launch;
+    dw::BwfLaunchFn fn = b.one_launch;
+    if (aligned16(x) && aligned16(dy))
+        fn = b.mfma_launch && aligned16(workspace) ? b.mfma_launch : b.vec_launch;
     hipError_t e = fn(b, x, dy, dw, workspace, stream);
     return e == hipSuccess ? DWCONV_OK : DWCONV_ERR_HIP;
 }

@@ -203,6 +203,13 @@ k_bwf_reduce(const float *__restrict__ ws, float *__restrict__ dw, long long ele
     dw[e] = total;
 }
 
+hipError_t launch_bwf_reduce(const Shape &s, const float *ws, float *dw, int Z, hipStream_t st) {
+    const long long elems = (long long)s.FH * s.FW * s.C;
+    hipLaunchKernelGGL(k_bwf_reduce, dim3((uint32_t)((elems + 255) / 256)), dim3(256), 0, st, ws,
+                       dw, elems, Z);
+    return hipGetLastError();
+}
+
 template <class DT, int VEC, bool SLIDE, int TAPS>
 static hipError_t launch_bwf(const BwfPlan &b, const void *x, const void *dy, float *dw,
                              void *ws, hipStream_t st) {
@@ -212,10 +219,7 @@ static hipError_t launch_bwf(const BwfPlan &b, const void *x, const void *dy, fl
                        (const typename DT::X *)dy, (float *)ws, b.s, b.ncv, b.nfc, b.rpc, lanes);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long long elems = (long long)b.s.FH * b.s.FW * b.s.C;
-    hipLaunchKernelGGL(k_bwf_reduce, dim3((uint32_t)((elems + 255) / 256)), dim3(256), 0, st,
-                       (const float *)ws, dw, elems, b.Z);
-    return hipGetLastError();
+    return launch_bwf_reduce(b.s, (const float *)ws, dw, b.Z, st);
 }
 
 bool plan_bwd_filter(BwfPlan &b, const Plan &f) {
@@ -273,6 +277,9 @@ bool plan_bwd_filter(BwfPlan &b, const Plan &f) {
              "bwf: %d ch/lane x filter row x %d taps, Z=%d chunks of %d rows (%s), "
              "pairwise merge, workspace %zu B",
              VEC, taps, b.Z, b.rpc, slide ? "sliding window" : "direct taps", b.ws_bytes);
+    // fp16 / bf16 at stride 1: the matrix-core pass 1 for aligned tensors
+    // (it sizes the workspace for both and describes itself)
+    plan_bwf_mfma(b);
     return true;
 }
 

@@ -48,11 +48,22 @@ struct BwfPlan {
     int vec;              // channels per lane
     int ncv, nfc;         // channel vectors, 8-tap column chunks
     int Z, rpc;           // chunks of the (n, oh) rows, rows per chunk
-    size_t ws_bytes;      // Z * FH * FW * C floats
+    size_t ws_bytes;      // enough for either pass 1 (Z or mZ chunk sums)
     BwfLaunchFn vec_launch, one_launch;
-    char desc[160];
+    // matrix-core pass 1 (fp16 / bf16, stride 1, dilation 1), used when x,
+    // dy and the workspace are 16-byte aligned: workgroup = one image, cs
+    // channels, a chunk of mrpc output rows; mZ = N * mnrc chunk sums
+    BwfLaunchFn mfma_launch;
+    int mcs, mncs, mnrc, mrpc, mZ, mlds;
+    uint32_t mgrid;
+    char desc[192];
 };
 bool plan_bwd_filter(BwfPlan &b, const Plan &forward);
+// Fills the matrix-core fields of `b` (b.s and b.dtype set); false when the
+// shape is not covered.
+bool plan_bwf_mfma(BwfPlan &b);
+// Pass 2: dw[e] = pairwise sum over z < Z of ws[z * FH*FW*C + e].
+hipError_t launch_bwf_reduce(const Shape &s, const float *ws, float *dw, int Z, hipStream_t st);
 
 // Output extent along one axis; 0 when not even one output fits.
 int out_extent(int in, int f, int s, int d, int p);

@@ -143,14 +143,17 @@ def test_bwd_is_adjoint_of_fwd_on_gpu():
 
 # ------------------------------------------------------------ backward filter
 
-def run_bwf(x, dy, shape, fmt):
+def run_bwf(x, dy, shape, fmt, ws_offset=0):
     """dw on the host (float32), from a NaN-filled buffer whose guard bands
-    are checked; the workspace is filled with garbage first."""
+    are checked; the workspace is filled with garbage first.  ws_offset
+    floats of offset give a workspace that is not 16-byte aligned (the
+    matrix-core pass 1 then gives way to the vector one)."""
     N, H, W, C, FH, FW, S, D, P = shape
     h = dw.dwconv_create(N, H, W, C, FH, FW, S, D, P, fmt)
     try:
         nbytes = dw.dwconv_bwd_filter_workspace(h)
-        ws = torch.full((nbytes // 4 + 1,), float("nan"), dtype=torch.float32, device=DEV)
+        ws = torch.full((nbytes // 4 + 1 + ws_offset,), float("nan"), dtype=torch.float32,
+                        device=DEV)[ws_offset:]
         guard, n_w = 256, FH * FW * C
         buf = torch.full((n_w + 2 * guard,), float("nan"), dtype=torch.float32, device=DEV)
         dwt = buf[guard:guard + n_w]
@@ -237,3 +240,39 @@ def test_bwd_filter_bilinear_and_deterministic():
         rhs = float(np.sum(w.astype(np.float64) * g1.cpu().numpy()))
         assert lhs == rhs, (shape, lhs, rhs)
         assert torch.equal(g1, g2)
+
+
+def test_bwd_filter_mfma_tiles():
+    """The matrix-core pass 1 (fp16 / bf16, stride 1): one and two 16-tap
+    tiles per axis, window counts at their limits (OW + FW - 1 = 64 and 65),
+    padding wider than the filter, 4- and 8-channel slices, images split into
+    row chunks, and a workspace that is not 16-byte aligned (vector pass 1);
+    each against the oracle."""
+    cases = [((2, 20, 58, 8, 7, 7, 1, 1, 3), "f16"),      # OW + FW - 1 = 64: 2 windows
+             ((2, 20, 59, 8, 7, 7, 1, 1, 3), "bf16"),     # 65: 4 windows
+             ((1, 40, 23, 12, 17, 5, 1, 1, 8), "f16"),    # two row tiles
+             ((1, 21, 40, 4, 3, 31, 1, 1, 15), "bf16"),   # two column tiles
+             ((1, 52, 52, 4, 31, 31, 1, 1, 15), "f16"),   # 31 x 31, 3 windows
+             ((1, 100, 20, 8, 3, 3, 1, 1, 1), "bf16"),    # rows split into chunks
+             ((1, 30, 12, 16, 3, 5, 1, 1, 6), "f16"),     # padding past the filter
+             ((3, 9, 9, 24, 9, 9, 1, 1, 0), "bf16")]      # no padding
+    for shape, fmt in cases:
+        x, dy = bwf_inputs(shape, fmt, 75)
+        for off in (0, 1):
+            dwv, desc = run_bwf(x, dy, shape, fmt, ws_offset=off)
+            say(f"[gpu] bwd filter {fmt} {shape} ws+{4 * off}B ({desc[:40]})")
+            if off == 0:
+                assert desc.startswith("bwf mfma"), desc
+            check_bwf(dwv, x, dy, shape, fmt, f"bwf {shape} ws+{off}")
+
+
+def test_bwd_filter_mfma_tall_image_chunks():
+    """A single tall image split into many row chunks (a batch of one gives
+    too few workgroups otherwise): the chunk sums of one image are merged
+    like those of separate images."""
+    shape, fmt = (1, 1100, 6, 8, 3, 3, 1, 1, 1), "bf16"
+    x, dy = bwf_inputs(shape, fmt, 76)
+    dwv, desc = run_bwf(x, dy, shape, fmt)
+    say(f"[gpu] bwd filter tall ({desc})")
+    assert "Z=23" in desc, desc
+    check_bwf(dwv, x, dy, shape, fmt, "bwf tall")
