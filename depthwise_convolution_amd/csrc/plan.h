@@ -48,8 +48,12 @@ struct BwfPlan {
     int vec;              // channels per lane
     int ncv, nfc;         // channel vectors, 8-tap column chunks
     int Z, rpc;           // chunks of the (n, oh) rows, rows per chunk
-    size_t ws_bytes;      // enough for either pass 1 (Z or mZ chunk sums)
+    size_t ws_bytes;      // enough for every pass 1 (Z, vZ or mZ chunk sums)
     BwfLaunchFn vec_launch, one_launch;
+    // vec_launch's own chunking when it is the column stream (else vZ = Z)
+    int vZ, vaux[5];
+    long long vstrips;
+    uint32_t vgrid;
     // matrix-core pass 1 (fp16 / bf16, stride 1, dilation 1), used when x,
     // dy and the workspace are 16-byte aligned: workgroup = one image, cs
     // channels, a chunk of mrpc output rows; mZ = N * mnrc chunk sums
