@@ -99,7 +99,8 @@ struct MfmaTile {
 // issued before the current block's MFMAs so that their latency is hidden.
 // FHK > 0: filters of at most FHK rows and one fragment keep every B operand
 // of the wavefront's channels in registers for the whole strip.
-template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT>
+// AL: every lane reads its A windows of each filter row from LDS (no DPP)
+template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL = false>
 __global__ void __launch_bounds__(CS >= 16 ? 512 : 256, 2)  // at most 256 registers
 k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
        const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int ncs, int nct) {
@@ -340,6 +341,13 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
             slot -= slot >= XR ? XR : 0;
 #pragma unroll
             for (int ci = 0; ci < NCH; ++ci) {
+                if constexpr (AL) {
+                    const uint16_t *xr = xc[ci] + slot * PITCH;
+#pragma unroll
+                    for (int win = 0; win < NWIN; ++win)
+                        o.A[ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
+                    continue;
+                }
 #pragma unroll
                 for (int win = 0; win < NWIN; ++win)
 #pragma unroll
@@ -382,16 +390,83 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     }
         };
 
-        if constexpr (FHT > 0) {
+        if constexpr (FHT > 0 && FHK > 0) {
+            // B operands kept in registers: one row of lookahead
             Ops o[2];
             full_a(o[0]);
-            load_bs(o[0], 0);
 #pragma unroll
             for (int fh = 0; fh < FHT; ++fh) {
-                if (fh + 1 < FHT) {
-                    next_a(o[(fh + 1) & 1], o[fh & 1], fh + 1);
-                    load_bs(o[(fh + 1) & 1], fh + 1);
+                if (fh + 1 < FHT) next_a(o[(fh + 1) & 1], o[fh & 1], fh + 1);
+                mfmas(o[fh & 1], fh);
+                // keep the scheduler from hoisting later rows' operands
+                // (and their registers) above this row's MFMAs
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if constexpr (FHT > 0) {
+            // Software pipeline two filter rows deep: while the MFMAs of row
+            // fh run, the operands of row fh+1 are formed from LDS data
+            // loaded during row fh-1, and the LDS reads of row fh+2 are
+            // issued, so no row waits for LDS.  The new row of lane 15 is
+            // the DPP's old value: lanes 0..14 take lane t16+1 of row fh's
+            // windows, lane 15 (no source in its row) keeps what it loaded.
+            Ops o[2];   // formed operands of rows fh, fh+1
+            u32x4 Lw[2][NCH][NWIN];          // loaded windows, rows fh+1, fh+2
+            uint32_t Rb[2][NCH][NFRAG][5];   // loaded B dwords, rows fh+1, fh+2
+            auto load_rows = [&](int fh) {
+                int slot = slot0 + fh;
+                slot -= slot >= XR ? XR : 0;
+#pragma unroll
+                for (int ci = 0; ci < NCH; ++ci)
+                    if (AL || t16 == 15) {
+                        const uint16_t *xr = xc[ci] + slot * PITCH;
+#pragma unroll
+                        for (int win = 0; win < NWIN; ++win)
+                            Lw[fh & 1][ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
+                    }
+                {
+#pragma unroll
+                    for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+                        for (int f = 0; f < NFRAG; ++f) {
+                            const uint32_t *zd = reinterpret_cast<const uint32_t *>(
+                                zc[ci] + (fh * NFRAG + f) * ZLEN);
+#pragma unroll
+                            for (int q = 0; q < 5; ++q) Rb[fh & 1][ci][f][q] = zd[q];
+                        }
                 }
+            };
+            auto form = [&](int fh) {
+                Ops &n = o[fh & 1];
+                const Ops &p = o[(fh + 1) & 1];  // row fh - 1
+#pragma unroll
+                for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+                    for (int win = 0; win < NWIN; ++win)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            n.A[ci][win][q] =
+                                AL ? Lw[fh & 1][ci][win][q]
+                                   : __builtin_amdgcn_update_dpp((int)Lw[fh & 1][ci][win][q],
+                                                                 (int)p.A[ci][win][q], 0x101, 0xf,
+                                                                 0xf, false);
+                {
+#pragma unroll
+                    for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+                        for (int f = 0; f < NFRAG; ++f)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                n.B[ci][f][q] = __builtin_amdgcn_alignbit(
+                                    Rb[fh & 1][ci][f][q + 1], Rb[fh & 1][ci][f][q], bsh);
+                }
+            };
+            full_a(o[0]);
+            load_bs(o[0], 0);
+            if (FHT > 1) load_rows(1);
+#pragma unroll
+            for (int fh = 0; fh < FHT; ++fh) {
+                if (fh + 2 < FHT) load_rows(fh + 2);
+                if (fh + 1 < FHT) form(fh + 1);
                 mfmas(o[fh & 1], fh);
                 // keep the scheduler from hoisting later rows' operands
                 // (and their registers) above this row's MFMAs
@@ -480,16 +555,16 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     }
 }
 
-template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT>
+template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL>
 static hipError_t launch_mfma(const Plan &p, const void *x, const void *w, const void *bias,
                               void *y, hipStream_t st) {
     if (p.lds_bytes > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, FHT>),
+            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL>),
             hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT>), dim3(p.grid),
+    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL>), dim3(p.grid),
                        dim3(MfmaTile<CS, NB, NFRAG>::NT), p.lds_bytes, st,
                        (const uint16_t *)x, (const uint16_t *)w, (const float *)bias,
                        (uint16_t *)y, p.s, p.aux0, p.aux1);
@@ -507,20 +582,26 @@ static int mfma_lds_bytes(const Shape &s) {
 }
 
 struct MfmaEntry {
-    int dtype, cs, nb, nfrag, fhk, fht;
+    int dtype, cs, nb, nfrag, fhk, fht, al;
     LaunchFn fn;
     int (*lds)(const Shape &);
 };
 
-#define MF(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_)                                             \
-    {DTE,     CS_, NB_, NF_, FHK_, FHT_, launch_mfma<DTT, CS_, NB_, NF_, FHK_, FHT_>, \
+#define MFA(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_, AL_)                                      \
+    {DTE, CS_, NB_, NF_, FHK_, FHT_, AL_, launch_mfma<DTT, CS_, NB_, NF_, FHK_, FHT_, AL_>, \
      mfma_lds_bytes<CS_, NB_, NF_>}
+#define MF(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_) MFA(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_, false)
 
 // Wider channel slices first (16-byte loads, more work per tile); the
 // planner falls back to 4 channels when the 8-channel tile exceeds 64 KiB of
 // LDS (tall filters), to keep several workgroups per CU.
 static const MfmaEntry kMfma[] = {
-    // compile-time filter heights of the common square filters
+    // compile-time filter heights of the common square filters, A windows
+    // read from LDS by every lane (measured faster than the DPP row shift
+    // on 7x7 and 31x31)
+    MFA(DT_F16, F16, 8, 4, 1, 8, 7, true),   MFA(DT_BF16, BF16, 8, 4, 1, 8, 7, true),
+    MFA(DT_F16, F16, 4, 4, 2, 0, 31, true),  MFA(DT_BF16, BF16, 4, 4, 2, 0, 31, true),
+    // the same with the DPP row shift (DWCONV_MFMA_AL=0)
     MF(DT_F16, F16, 8, 4, 1, 8, 7),    MF(DT_BF16, BF16, 8, 4, 1, 8, 7),
     // 32-byte pixel slices, 8 wavefronts (measured slower on 7x7: kept for
     // DWCONV_MFMA_CS=16)
@@ -535,14 +616,17 @@ static const MfmaEntry kMfma[] = {
     MF(DT_BF16, BF16, 4, 4, 1, 0, 0),  MF(DT_BF16, BF16, 4, 4, 2, 0, 0),
 };
 #undef MF
+#undef MFA
 
 bool plan_mfma(Plan &p) {
     if (p.dtype != DT_F16 && p.dtype != DT_BF16) return false;
     if (p.s.S != 1 || p.s.D != 1) return false;
     const int nfrag = (p.s.FW + 15) / 16;
     // DWCONV_MFMA_CS=4|8|16 picks the channel slice (a tuning hook)
-    int want_cs = 0;
+    int want_cs = 0, want_al = -1;
     if (const char *env = getenv("DWCONV_MFMA_CS")) want_cs = atoi(env);
+    // DWCONV_MFMA_AL=0|1: A windows by DPP row shift / from LDS for every lane
+    if (const char *env = getenv("DWCONV_MFMA_AL")) want_al = atoi(env);
     const MfmaEntry *e = nullptr;
     int lds = 0;
     for (const auto &k : kMfma) {
@@ -550,6 +634,7 @@ bool plan_mfma(Plan &p) {
         if (k.fhk && p.s.FH > k.fhk) continue;
         if (k.fht && p.s.FH != k.fht) continue;
         if (want_cs && k.cs != want_cs) continue;
+        if (want_al >= 0 && k.al != want_al) continue;
         const int need = k.lds(p.s);
         // 16-channel slices run one 8-wavefront workgroup per CU; narrower
         // ones aim for at least two per CU unless nothing else fits
@@ -578,8 +663,9 @@ bool plan_mfma(Plan &p) {
     p.launch = e->fn;
     snprintf(p.desc, sizeof(p.desc),
              "mfma: 16x16x32 banded GEMM, strips of %d cols x %d ch walked 16 rows at a "
-             "time, %d fragment(s) of 16 taps, LDS %d B, %u x %d",
-             16 * e->nb, e->cs, nfrag, lds, p.grid, p.block);
+             "time, %d fragment(s) of 16 taps, A by %s, LDS %d B, %u x %d",
+             16 * e->nb, e->cs, nfrag, e->al ? "LDS reads" : "DPP row shift", lds, p.grid,
+             p.block);
     return true;
 }
 

@@ -319,12 +319,16 @@ MFMA_SLICES = {  # channel slice -> (dtype, F) combinations it is compiled for
 }
 
 
+@pytest.mark.parametrize("al", [0, 1])
 @pytest.mark.parametrize("cs", sorted(MFMA_SLICES))
-def test_each_mfma_channel_slice(cs, monkeypatch):
+def test_each_mfma_channel_slice(cs, al, monkeypatch):
     """Each MFMA channel slice (picked through the DWCONV_MFMA_CS tuning
     hook) against the oracle: compiled and runtime filter heights, one and two
-    16-tap fragments, ragged strips, a short image and several slices."""
+    16-tap fragments, ragged strips, a short image and several slices; A
+    windows by DPP row shift (al=0) and by LDS reads (al=1, the compiled
+    7x7 and 31x31 entries)."""
     monkeypatch.setenv("DWCONV_MFMA_CS", str(cs))
+    monkeypatch.setenv("DWCONV_MFMA_AL", str(al))
     rng = np.random.default_rng(31 + cs)
     for fmt, F in MFMA_SLICES[cs]:
         for (N, H, W, C) in [(1, 23, 37, 2 * cs), (2, 9, 70, cs), (1, 40, 17, 3 * cs)]:
