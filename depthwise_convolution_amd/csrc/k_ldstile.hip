@@ -402,14 +402,15 @@ static const TapEntry kTap[] = {
 };
 #undef TT
 
-// Rows per tile: as many as fit 40 KiB of LDS while the grid keeps at least
-// 768 workgroups (three per CU); DWCONV_LDS_TB=n forces n rows (a tuning hook).
+// Rows per tile: as many as fit lds_cap bytes of LDS while the grid keeps at
+// least min_grid workgroups; DWCONV_LDS_TB=n forces n rows (a tuning hook).
 template <class RowsFn>
-static int pick_tb(const Plan &p, int nct, long long row_bytes, RowsFn rows) {
+static int pick_tb(const Plan &p, int nct, long long row_bytes, RowsFn rows, int min_grid,
+                   long long lds_cap) {
     auto grid_of = [&](int tb) { return (long long)((p.s.OH + tb - 1) / tb) * nct * p.s.N; };
     int TB = 1;
-    while (TB < 16 && TB < p.s.OH && (long long)rows(TB + 1) * row_bytes <= 40 * 1024 &&
-           grid_of(TB + 1) >= 768)
+    while (TB < 16 && TB < p.s.OH && (long long)rows(TB + 1) * row_bytes <= lds_cap &&
+           grid_of(TB + 1) >= min_grid)
         ++TB;
     if (const char *env = getenv("DWCONV_LDS_TB")) {
         const int want = atoi(env);
@@ -448,7 +449,9 @@ static bool plan_i8tap(Plan &p) {
     const long long row_bytes = rowb + (long long)p.s.C * kqp;
     auto rows = [&](int tb) { return (tb - 1) * SD + p.s.FH; };
     const int nct = (p.s.OW + 4 * TM - 1) / (4 * TM);
-    const int TB = pick_tb(p, nct, row_bytes, rows);
+    // two workgroups per CU: taller tiles cut the halo rows per output row,
+    // which measured faster than more, smaller workgroups
+    const int TB = pick_tb(p, nct, row_bytes, rows, 512, 80 * 1024);
     const long long lds = rows(TB) * row_bytes;
     if (lds > 160 * 1024) return false;
     const int nrb = (p.s.OH + TB - 1) / TB;
@@ -494,7 +497,8 @@ bool plan_ldstile(Plan &p) {
     const int g = gcd_c(p.s.S, p.s.D);
     auto rows = [&](int tb) { return ((tb - 1) * p.s.S + (p.s.FH - 1) * p.s.D) / g + 1; };
     const int nct = (p.s.OW + 4 * e->tm - 1) / (4 * e->tm);
-    const int TB = pick_tb(p, nct, rowb, rows);
+    // at least three workgroups per CU, four fit LDS
+    const int TB = pick_tb(p, nct, rowb, rows, 768, 40 * 1024);
     const long long lds = (long long)rows(TB) * rowb;
     if (lds > 160 * 1024) return false;
     const int nrb = (p.s.OH + TB - 1) / TB;
