@@ -163,3 +163,18 @@ def random_small(rng, dtype, max_hw=20, max_c=70, max_f=7):
                     dist, dist, bd if rng.integers(0, 4) else None,
                     int(rng.integers(0, 2**31)))
 
+
+
+def device_input(shape, fmt, seed, device):
+    """A large seeded input drawn on the GPU by torch's generator (for
+    tensors too big to draw and copy from the host in a test): N(0, 1) for
+    the float formats (drawn in fp32, then rounded to the storage format by
+    torch), uniform integers in [-128, 127] for int8.  Returns a torch
+    tensor in the storage format (bf16 as torch.bfloat16)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    if fmt == "i8":
+        return torch.randint(-128, 128, shape, generator=g, device=device, dtype=torch.int8)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return t.to({"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[fmt])

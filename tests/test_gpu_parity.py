@@ -347,3 +347,89 @@ def test_each_mfma_channel_slice(cs, al, monkeypatch):
             y, used = run(x, w, b, shape, fmt, "mfma", guard=512)
             assert used == "mfma", used
             assert_matches_oracle(y, x, w, b, shape, fmt, f"mfma cs{cs} {shape}")
+
+
+# --------------------------------------------- tensors at the size limit
+
+# just under 2^31 elements (the largest tensors a plan accepts): per-image
+# element offsets reach the 32-bit range the kernels index within an image
+BIG = [((1, 16383, 16384, 8, 3, 3, 1, 1, 1), "f32"),      # column stream
+       ((1, 16383, 16384, 8, 7, 7, 1, 1, 3), "f16"),      # MFMA, 8-channel slices
+       ((1, 16383, 16384, 8, 31, 31, 1, 1, 15), "bf16"),  # MFMA, two fragments
+       ((2, 1100, 16000, 61, 5, 5, 2, 2, 4), "i8")]       # int8 tap-packed
+
+
+@pytest.mark.parametrize("case", range(len(BIG)))
+def test_size_limit_sampled(case):
+    """The largest accepted tensors, input drawn on the GPU: 4000 random
+    outputs plus the first and last pixels of every image, each against the
+    oracle on the dilated FH x FW input patch that output reads (zeros
+    outside the image), gathered from the device."""
+    shape, fmt = BIG[case]
+    N, H, W, C, FH, FW, S, D, P = shape
+    OH, OW = oracle.out_dim(H, FH, S, D, P), oracle.out_dim(W, FW, S, D, P)
+    rng = np.random.default_rng(900 + case)
+    w = synth.to_storage(rng.normal(0, 1 / np.sqrt(FH * FW), (FH, FW, C)), fmt) if fmt != "i8" \
+        else rng.integers(-128, 128, (FH, FW, C)).astype(np.int8)
+    b = synth.to_storage(rng.uniform(-0.1, 0.1, C), "f32") if fmt != "i8" \
+        else rng.integers(-2**15, 2**15 + 1, C).astype(np.int32)
+    say(f"[gpu] size limit {fmt} {shape}: drawing the input on the device")
+    x = synth.device_input((N, H, W, C), fmt, 910 + case, DEV)
+    ydt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+           "i8": torch.int32}[fmt]
+    y = torch.empty((N, OH, OW, C), dtype=ydt, device=DEV)
+    wt = (torch.from_numpy(w.view(np.int16)).view(torch.bfloat16) if fmt == "bf16"
+          else torch.from_numpy(w)).to(DEV)
+    bt = torch.from_numpy(b).to(DEV)
+    h = dw.dwconv_create(*shape, fmt)
+    try:
+        desc = dw.dwconv_plan_describe(h)
+        say(f"      plan {desc[:60]}")
+        dw.dwconv_fwd(h, x, wt, bt, y)
+        torch.cuda.synchronize()
+    finally:
+        dw.dwconv_destroy(h)
+    # sampled outputs: random, plus the corners of every image
+    total = N * OH * OW * C
+    idx = [rng.integers(0, total, 4000)]
+    for n in range(N):
+        for (oh, ow) in [(0, 0), (0, OW - 1), (OH - 1, 0), (OH - 1, OW - 1)]:
+            idx.append(((n * OH + oh) * OW + ow) * C + np.arange(C))
+    idx = np.unique(np.concatenate(idx))
+    c_ = idx % C
+    ow_ = (idx // C) % OW
+    oh_ = (idx // (C * OW)) % OH
+    n_ = idx // (C * OW * OH)
+    # the dilated patch each sampled output reads, gathered on the device
+    ih = oh_[:, None] * S - P + D * np.arange(FH)[None, :]          # npts x FH
+    iw = ow_[:, None] * S - P + D * np.arange(FW)[None, :]          # npts x FW
+    inside = ((ih >= 0) & (ih < H))[:, :, None] & ((iw >= 0) & (iw < W))[:, None, :]
+    flat = ((n_[:, None, None] * H + np.clip(ih, 0, H - 1)[:, :, None]) * W
+            + np.clip(iw, 0, W - 1)[:, None, :]) * C + c_[:, None, None]
+    xf = x.view(-1)
+    g = xf[torch.from_numpy(flat.reshape(-1)).to(DEV)]
+    g = (g.view(torch.int16).cpu().numpy().view(np.uint16) if fmt == "bf16"
+         else g.cpu().numpy()).reshape(flat.shape)
+    zero = np.zeros((), g.dtype)
+    patches = np.where(inside, g, zero)
+    yv = y.view(-1)[torch.from_numpy(idx).to(DEV)]
+    yv = (yv.view(torch.int16).cpu().numpy().view(np.uint16) if fmt == "bf16"
+          else yv.cpu().numpy())
+    del x, y
+    torch.cuda.empty_cache()
+    # the oracle, one channel at a time: every sampled output of channel c is
+    # one 1 x 1 output of an FH x FW image (stride 1, dilation 1, no padding)
+    for c in range(C):
+        sel = np.nonzero(c_ == c)[0]
+        if sel.size == 0:
+            continue
+        xs = np.ascontiguousarray(patches[sel][:, :, :, None])
+        ws = np.ascontiguousarray(w[:, :, c:c + 1])
+        bs = np.ascontiguousarray(b[c:c + 1])
+        ye, scale = oracle.points(xs, ws, bs, 1, 1, 0, fmt, np.arange(sel.size))
+        what = f"size limit {fmt} {shape} channel {c}"
+        if fmt == "i8":
+            check.assert_int(yv[sel], ye, what)
+        else:
+            check.assert_float(yv[sel], fmt, ye, scale, what)
+    say(f"      ok: {idx.size} outputs")
