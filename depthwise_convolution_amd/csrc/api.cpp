@@ -16,20 +16,26 @@ struct dwconv_plan {
 // Backward data at stride 1 is a forward pass over dY (N x OH x OW x C) with
 // the filter rotated by 180 degrees and padding D(F-1) - P, whose output is
 // exactly H x W ("Flash-DWC: Making Depthwise Convolution Compute-Efficient
-// on GPUs", section 5.1).  One padding serves both axes only for square
-// filters.  Float dtypes only.
+// on GPUs", section 5.1): every forward kernel family serves it.  One padding
+// serves both axes only for square filters; every other float shape (stride
+// above 1, non-square filters, padding beyond D(F-1)) runs the direct
+// backward kernel, which sums each input element's taps.
 static bool plan_bwd_data(dw::Plan &b, const dw::Plan &f, int variant) {
     const dw::Shape &s = f.s;
-    if (f.dtype == dw::DT_I8 || s.S != 1 || s.FH != s.FW) return false;
+    if (f.dtype == dw::DT_I8) return false;
     const int P2 = s.D * (s.FH - 1) - s.P;
-    if (P2 < 0) return false;
-    int rc = dw::make_plan(b, s.N, s.OH, s.OW, s.C, s.FH, s.FW, 1, s.D, P2, f.dtype, variant);
-    if (rc != DWCONV_OK && variant != dw::V_AUTO)
-        rc = dw::make_plan(b, s.N, s.OH, s.OW, s.C, s.FH, s.FW, 1, s.D, P2, f.dtype,
-                           dw::V_AUTO);
-    if (rc != DWCONV_OK || b.s.OH != s.H || b.s.OW != s.W) return false;
-    b.s.flip = 1;
-    return true;
+    if (s.S == 1 && s.FH == s.FW && P2 >= 0) {
+        int rc = dw::make_plan(b, s.N, s.OH, s.OW, s.C, s.FH, s.FW, 1, s.D, P2, f.dtype,
+                               variant);
+        if (rc != DWCONV_OK && variant != dw::V_AUTO)
+            rc = dw::make_plan(b, s.N, s.OH, s.OW, s.C, s.FH, s.FW, 1, s.D, P2, f.dtype,
+                               dw::V_AUTO);
+        if (rc == DWCONV_OK && b.s.OH == s.H && b.s.OW == s.W) {
+            b.s.flip = 1;
+            return true;
+        }
+    }
+    return dw::plan_bwd_direct(b, f);
 }
 
 extern "C" {

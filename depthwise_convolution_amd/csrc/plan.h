@@ -79,6 +79,9 @@ int make_plan(Plan &p, int N, int H, int W, int C, int FH, int FW, int S, int D,
 // Per-family planners, defined next to their kernels.  Each returns true and
 // fills the tiling and launcher when it can run the shape.
 bool plan_direct(Plan &p);
+// Backward data for any float shape, one lane per input element; b gets the
+// forward plan's shape (dy N x OH x OW x C in, dx N x H x W x C out).
+bool plan_bwd_direct(Plan &b, const Plan &forward);
 bool plan_rowwin(Plan &p);
 bool plan_ldstile(Plan &p);
 bool plan_mfma(Plan &p);

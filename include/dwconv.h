@@ -113,17 +113,18 @@ dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
  *   dX[n,ih,iw,c] = sum over (oh, ow, fh, fw) with oh*S - P + fh*D = ih and
  *                   ow*S - P + fw*D = iw of dY[n,oh,ow,c] * Wt[fh,fw,c]
  *
- * At stride 1 this is a forward pass over dY with the filter rotated by 180
- * degrees and padding D(F-1) - P, run here by the forward kernels reading
- * the filter rotated in place (no copy is made).
+ * At stride 1 with a square filter and P <= D(F-1) this is a forward pass
+ * over dY with the filter rotated by 180 degrees and padding D(F-1) - P, run
+ * by the forward kernels reading the filter rotated in place (no copy is
+ * made); every other float shape runs a direct kernel that sums each input
+ * element's taps.
  *   dy  N x OH x OW x C   (float / fp16 / bf16, as y)
  *   w   FH x FW x C       (the forward filter, not rotated)
  *   dx  N x H  x W  x C   (as x; overwritten)
  * Partial sums are fp32; fp16/bf16 dx is rounded once.  Enqueued on `stream`
  * without waiting; dx must not overlap dy or w; any alignment is accepted.
  * Returns DWCONV_ERR_INVALID_ARG for a NULL handle, dy, w or dx,
- * DWCONV_ERR_UNSUPPORTED when the plan has no backward-data pass (int8; a
- * stride other than 1; FH != FW; padding larger than D(F-1)), and
+ * DWCONV_ERR_UNSUPPORTED when the plan has no backward-data pass (int8), and
  * DWCONV_ERR_HIP if the launch fails. */
 dwconv_status_t dwconv_bwd_data(dwconv_handle_t h, const void *dy, const void *w,
                                 void *dx, hipStream_t stream);

@@ -131,15 +131,20 @@ def test_bwd_data_support_matrix():
              ((2, 9, 9, 8, 7, 7, 1, 1, 3, "f16"), True),
              ((1, 20, 20, 16, 31, 31, 1, 1, 15, "bf16"), True),
              ((2, 9, 9, 8, 3, 3, 1, 2, 0, "f32"), True),     # dilated, no padding
-             ((2, 9, 9, 8, 3, 3, 2, 1, 1, "f32"), False),    # stride 2
-             ((2, 9, 9, 8, 3, 5, 1, 1, 1, "f32"), False),    # not square
-             ((2, 9, 9, 8, 3, 3, 1, 1, 3, "f32"), False),    # pad > D(F-1)
-             ((2, 9, 9, 8, 3, 3, 1, 1, 1, "i8"), False)]     # int8
+             ((2, 9, 9, 8, 3, 3, 2, 1, 1, "f32"), "direct"),    # stride 2
+             ((2, 9, 9, 8, 3, 5, 1, 1, 1, "f16"), "direct"),    # not square
+             ((2, 9, 9, 8, 3, 3, 1, 1, 3, "bf16"), "direct"),   # pad > D(F-1)
+             ((2, 9, 9, 8, 3, 3, 1, 1, 1, "i8"), False)]        # int8
     for (N, H, W, C, FH, FW, S, D, P, dt), want in cases:
         h = dw.dwconv_create(N, H, W, C, FH, FW, S, D, P, dt)
         try:
-            assert dw.dwconv_bwd_data_supported(h) == want, (N, H, W, C, FH, FW, S, D, P, dt)
-            assert bool(dw.dwconv_bwd_data_describe(h)) == want
+            shape = (N, H, W, C, FH, FW, S, D, P, dt)
+            assert dw.dwconv_bwd_data_supported(h) == bool(want), shape
+            desc = dw.dwconv_bwd_data_describe(h)
+            assert bool(desc) == bool(want), shape
+            # the forward families serve stride 1 with square filters; the
+            # direct backward kernel everything else
+            assert desc.startswith("direct (backward data)") == (want == "direct"), (shape, desc)
         finally:
             dw.dwconv_destroy(h)
 
@@ -147,7 +152,7 @@ def test_bwd_data_support_matrix():
 def test_bwd_data_argument_errors():
     """NULL arguments and unsupported plans are refused before any launch."""
     lib = dw._lib
-    h = dw.dwconv_create(1, 8, 8, 4, 3, 3, 2, 1, 1, "f32")   # stride 2: no bwd pass
+    h = dw.dwconv_create(1, 8, 8, 4, 3, 3, 1, 1, 1, "i8")    # int8: no bwd pass
     g = dw.dwconv_create(1, 8, 8, 4, 3, 3, 1, 1, 1, "f32")
     try:
         fake = 1 << 40   # never dereferenced: every path below returns first

@@ -141,6 +141,53 @@ def test_bwd_is_adjoint_of_fwd_on_gpu():
         assert lhs == rhs, (shape, lhs, rhs)
 
 
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_bwd_any_shape(fmt):
+    """The direct backward kernel: strides 1-3, dilations 1-3, non-square
+    filters and padding past D(F-1), against the oracle; misaligned dx too."""
+    rng = np.random.default_rng({"f32": 65, "f16": 66, "bf16": 67}[fmt])
+    done = 0
+    while done < 30:
+        FH, FW = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        S, D = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        P = int(rng.integers(0, 2 * max(FH, FW) + 1))
+        H, W = int(rng.integers(1, 30)), int(rng.integers(1, 30))
+        C = int(rng.choice([1, 3, 8, 13, 32, 64]))
+        N = int(rng.integers(1, 3))
+        shape = (N, H, W, C, FH, FW, S, D, P)
+        if oracle.out_dim(H, FH, S, D, P) < 1 or oracle.out_dim(W, FW, S, D, P) < 1:
+            continue
+        if S == 1 and FH == FW and P <= D * (FH - 1):
+            continue  # the forward families' path, covered above
+        dy, w = grads(shape, fmt, int(rng.integers(0, 2**31)))
+        say(f"[gpu] bwd any {fmt} {shape}")
+        dx, desc = run_bwd(dy, w, shape, fmt)
+        assert desc.startswith("direct (backward data)"), desc
+        check_bwd(dx, dy, w, shape, fmt, f"bwd any {shape}")
+        done += 1
+
+
+def test_bwd_any_shape_is_adjoint():
+    """<fwd(x), dy> = <x, bwd(dy)> on the GPU for strided, dilated and
+    non-square shapes (fp32 small integers: exact)."""
+    rng = np.random.default_rng(68)
+    for shape in [(2, 17, 13, 8, 3, 3, 2, 1, 1), (1, 30, 31, 16, 5, 3, 3, 2, 4),
+                  (1, 12, 21, 4, 2, 7, 2, 3, 9), (2, 9, 9, 12, 3, 3, 1, 1, 4)]:
+        N, H, W, C, FH, FW, S, D, P = shape
+        OH, OW = oracle.out_dim(H, FH, S, D, P), oracle.out_dim(W, FW, S, D, P)
+        x = rng.integers(-4, 5, size=(N, H, W, C)).astype(np.float32)
+        w = rng.integers(-4, 5, size=(FH, FW, C)).astype(np.float32)
+        dy = rng.integers(-4, 5, size=(N, OH, OW, C)).astype(np.float32)
+        conv = dw.DepthwiseConv2d(*shape, dtype="f32")
+        y = conv(torch.from_numpy(x).to(DEV), torch.from_numpy(w).to(DEV))
+        dx = conv.backward_data(torch.from_numpy(dy).to(DEV), torch.from_numpy(w).to(DEV))
+        torch.cuda.synchronize()
+        conv.close()
+        lhs = float(np.sum(y.cpu().numpy().astype(np.float64) * dy))
+        rhs = float(np.sum(x.astype(np.float64) * dx.cpu().numpy()))
+        assert lhs == rhs, (shape, lhs, rhs)
+
+
 # ------------------------------------------------------------ backward filter
 
 def run_bwf(x, dy, shape, fmt, ws_offset=0):
