@@ -190,6 +190,80 @@ def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd"):
                       f"{dt:.2f} s, {flops / dt / 1e9:.2f} GFLOP/s)"}
 
 
+# The pages' kernel sweep: square filters of growing size on three NHWC
+# feature maps ("Flash-DWC: Making Depthwise Convolution Compute-Efficient on
+# GPUs", Fig. 6 and the evaluation's filter-size sweep), stride 1 and same
+# padding, fp32 and fp16 (fp32 accumulate).
+SWEEP_SHAPES = [(128, 128, 128, 128), (128, 64, 64, 256), (128, 32, 32, 1024)]
+SWEEP_FILTERS = "3,5,7,9,13,17,21,25,31,41,51"
+
+
+def run_sweep(args):
+    """TFLOP/s against the filter size; one JSON line per point on stdout,
+    progress on stderr.  Inputs are drawn on the GPU (seeded)."""
+    import torch
+    import depthwise_convolution_amd as dw
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    filters = [int(f) for f in args.sweep_filters.split(",")]
+    dtypes = args.sweep_dtypes.split(",")
+    shapes = SWEEP_SHAPES[:args.sweep_shapes]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    summary = []
+    for si, (N, H, W, C) in enumerate(shapes):
+        for fmt in dtypes:
+            x = synth.device_input((N, H, W, C), fmt, 7000 + 10 * si + len(fmt), dev)
+            y = torch.empty((N, H, W, C), dtype=tdt[fmt], device=dev)
+            rng = np.random.default_rng(7100 + si)
+            for F in filters:
+                P = F // 2
+                w = synth.to_storage(rng.normal(0.0, 1.0 / F, (F, F, C)), fmt)
+                b = synth.to_storage(rng.uniform(-0.1, 0.1, C), "f32")
+                wt = (torch.from_numpy(w.view(np.int16)).view(torch.bfloat16) if fmt == "bf16"
+                      else torch.from_numpy(w)).to(dev)
+                bt = torch.from_numpy(b).to(dev)
+                h = dw.dwconv_create(N, H, W, C, F, F, 1, 1, P, fmt)
+                plan = dw.dwconv_plan_describe(h)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                dw.dwconv_fwd(h, x, wt, bt, y, stream)   # warm-up
+                e0.record(stream)
+                dw.dwconv_fwd(h, x, wt, bt, y, stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t1 = e0.elapsed_time(e1) * 1e-3
+                K = int(max(1, min(20, args.sweep_seconds / max(t1, 1e-6))))
+                e0.record(stream)
+                for _ in range(K):
+                    dw.dwconv_fwd(h, x, wt, bt, y, stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                dw.dwconv_destroy(h)
+                t = e0.elapsed_time(e1) * 1e-3 / K
+                flops = 2 * N * H * W * C * F * F
+                nbytes = 2 * N * H * W * C * XB[fmt] + F * F * C * XB[fmt] + C * 4
+                mfma = plan.startswith("mfma")
+                peak = MFMA_PEAK_TFLOPS[fmt] if mfma else VALU_PEAK_TFLOPS
+                bound = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (peak * 1e12) else (
+                    "mfma" if mfma else "alu")
+                rec = {"sweep": "filter size", "shape": [N, H, W, C], "dtype": fmt, "F": F,
+                       "pad": P, "plan": plan, "us": round(t * 1e6, 2), "launches": K,
+                       "tflops": round(flops / t / 1e12, 3), "gbs": round(nbytes / t / 1e9, 1),
+                       "bound": bound,
+                       "frac": round((nbytes / t / 1e9) / HBM_PEAK_GBS if bound == "hbm"
+                                     else flops / t / 1e12 / peak, 4)}
+                print(json.dumps(rec), flush=True)
+                print(f"[sweep] {N}x{H}x{W}x{C} {fmt} F={F}: {t * 1e3:.3f} ms, "
+                      f"{rec['tflops']:.2f} TFLOP/s ({plan.split(':')[0]})", file=sys.stderr,
+                      flush=True)
+                summary.append(rec)
+            del x, y
+            torch.cuda.empty_cache()
+    return summary
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,12 +276,24 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-copy", action="store_true",
                     help="skip the device-to-device copy ceiling measurement")
+    ap.add_argument("--sweep", action="store_true",
+                    help="the filter-size sweep instead of the bench line: TFLOP/s against "
+                         "F on three NHWC maps of 128 images (one JSON line per point)")
+    ap.add_argument("--sweep-filters", default=SWEEP_FILTERS)
+    ap.add_argument("--sweep-dtypes", default="f32,f16")
+    ap.add_argument("--sweep-shapes", type=int, default=len(SWEEP_SHAPES),
+                    help="how many of the three feature maps to sweep")
+    ap.add_argument("--sweep-seconds", type=float, default=0.3,
+                    help="timed launches per point: about this many seconds, 1 to 20")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
               "supported (shard over the batch: one process per GPU, no exchange)",
               file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        run_sweep(args)
+        return
 
     import torch
     import depthwise_convolution_amd as dw

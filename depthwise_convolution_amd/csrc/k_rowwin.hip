@@ -189,6 +189,98 @@ k_rowwin(const typename DT::X *__restrict__ x, const typename DT::X *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Row chunks: the row window for filters of any height and width at stride 1
+// and dilation 1 (both runtime values).  A filter row is walked in chunks of
+// CH taps; a chunk loads the TM + CH - 1 input vectors it needs and its CH
+// filter vectors (zero past FW) and adds TM * CH products per channel into
+// the filter row's fresh fp32 partial, which is added to the running sum at
+// the end of the row ("Flash-DWC: Making Depthwise Convolution
+// Compute-Efficient on GPUs", section 3.3: the 2-D filter as FH 1-D rows,
+// each reusing one input run across its taps).
+// ---------------------------------------------------------------------------
+template <class DT, int VEC, int TM, int CH>
+__global__ void __launch_bounds__(256)
+k_rowchunk(const typename DT::X *__restrict__ x, const typename DT::X *__restrict__ w,
+           const typename DT::Bias *__restrict__ bias, typename DT::Y *__restrict__ y,
+           Shape s, int ncv, int owg_n, long long total) {
+    using X = typename DT::X;
+    using Acc = typename DT::Acc;
+    constexpr int NWIN = TM + CH - 1;
+
+    const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
+    const long long g = (long long)b * blockDim.x + threadIdx.x;
+    if (g >= total) return;
+    const int cv = (int)(g % ncv);
+    long long r = g / ncv;
+    const int owg = (int)(r % owg_n);
+    r /= owg_n;
+    const int oh = (int)(r % s.OH);
+    const long long n = r / s.OH;
+    const int c0 = cv * VEC;
+    const int ow0 = owg * TM;
+    const int iw0 = ow0 - s.P;
+    const int nch = (s.FW + CH - 1) / CH;
+
+    Acc acc[TM][VEC];
+    {
+        Acc b0[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) b0[v] = bias ? bias[c0 + v] : Acc(0);
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[t][v] = b0[v];
+    }
+
+    for (int fh = 0; fh < s.FH; ++fh) {
+        const int ih = oh - s.P + fh;
+        if ((unsigned)ih >= (unsigned)s.H) continue;  // generated zero rows
+        const X *xr = x + ((n * s.H + ih) * (long long)s.W) * s.C + c0;
+        Acc row[TM][VEC];
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) row[t][v] = Acc(0);
+        for (int k = 0; k < nch; ++k) {
+            const int fw0 = k * CH;
+            Acc xw[NWIN][VEC];
+            load_window<DT, VEC, NWIN>(xw, xr, iw0 + fw0, s.W, s.C);
+            Acc wt[CH][VEC];
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                X e[VEC];
+                const bool ok = fw0 + j < s.FW;
+                load_vec<X, VEC>(e, w + (long long)tap_index(s, fh, ok ? fw0 + j : 0) * s.C + c0);
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) wt[j][v] = ok ? DT::widen(e[v]) : Acc(0);
+            }
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+#pragma unroll
+                for (int t = 0; t < TM; ++t)
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v)
+                        row[t][v] = mac<Acc>(row[t][v], xw[t + j][v], wt[j][v]);
+        }
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[t][v] += row[t][v];
+    }
+
+    typename DT::Y *yr = y + ((n * s.OH + oh) * (long long)s.OW + ow0) * s.C + c0;
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        if (ow0 + t < s.OW) {  // masked ragged tail along width
+            typename DT::Y o[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) o[v] = DT::narrow(acc[t][v]);
+            store_out<typename DT::Y, VEC, false>(yr + (long long)t * s.C, o);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Column stream (stride 1): each lane walks TH output rows of its TM x VEC
 // strip.  Every input row of the strip's halo -- TH + (FH-1)D rows -- is
 // loaded once; for each filter row fh it feeds output row o = i - fh*D, whose
@@ -374,6 +466,17 @@ static hipError_t launch_rowwin(const Plan &p, const void *x, const void *w,
     return hipGetLastError();
 }
 
+template <class DT, int VEC, int TM, int CH>
+static hipError_t launch_rowchunk(const Plan &p, const void *x, const void *w,
+                                  const void *bias, void *y, hipStream_t st) {
+    long long total = (long long)p.aux0 * p.aux1 * p.s.N * p.s.OH;
+    hipLaunchKernelGGL((k_rowchunk<DT, VEC, TM, CH>), dim3(p.grid), dim3(p.block), 0, st,
+                       (const typename DT::X *)x, (const typename DT::X *)w,
+                       (const typename DT::Bias *)bias, (typename DT::Y *)y, p.s, p.aux0,
+                       p.aux1, total);
+    return hipGetLastError();
+}
+
 template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, int NTL>
 static hipError_t launch_colstream(const Plan &p, const void *x, const void *w,
                                    const void *bias, void *y, hipStream_t st) {
@@ -431,6 +534,38 @@ static bool tile_matches(const RegTile &k, const Plan &p) {
     return p.s.C % k.vec == 0;  // every pixel a whole number of vectors
 }
 
+// Filters no compiled tiling covers, at stride 1 and dilation 1, in float
+// formats with whole 16-byte channel vectors: row chunks of 8 taps.
+static bool plan_rowchunk(Plan &p) {
+    if (p.s.S != 1 || p.s.D != 1 || p.dtype == DT_I8) return false;
+    const int VEC = 16 / p.elem_bytes;
+    const int TM = p.dtype == DT_F32 ? 8 : 4;
+    if (p.s.C % VEC != 0) return false;
+    const int ncv = p.s.C / VEC;
+    const int owg_n = (p.s.OW + TM - 1) / TM;
+    const long long total = (long long)ncv * owg_n * p.s.OH * p.s.N;
+    const long long blocks = (total + 255) / 256;
+    if (blocks >= (1LL << 31)) return false;
+    p.variant = V_ROWWIN;
+    p.vec = VEC;
+    p.tm = TM;
+    p.th = 0;
+    p.block = 256;
+    p.grid = (uint32_t)blocks;
+    p.aux0 = ncv;
+    p.aux1 = owg_n;
+    switch (p.dtype) {
+        case DT_F32: p.launch = launch_rowchunk<F32, 4, 8, 8>; break;
+        case DT_F16: p.launch = launch_rowchunk<F16, 8, 4, 8>; break;
+        case DT_BF16: p.launch = launch_rowchunk<BF16, 8, 4, 8>; break;
+        default: return false;
+    }
+    snprintf(p.desc, sizeof(p.desc),
+             "rowchunk: VEC=%d ch/lane, TM=%d outputs/lane, 8-tap chunks of a %dx%d filter, "
+             "%u x %d", VEC, TM, p.s.FH, p.s.FW, p.grid, p.block);
+    return true;
+}
+
 bool plan_rowwin(Plan &p) {
     const RegTile *e = nullptr;
     // DWCONV_TILE="TMxTH[pPF[flags]]", flags: n = non-temporal y stores,
@@ -456,7 +591,7 @@ bool plan_rowwin(Plan &p) {
         break;
     }
     if (!e && want_th >= 0) return false;  // asked for a tiling that is not compiled
-    if (!e) return false;
+    if (!e) return plan_rowchunk(p);
     int ncv = p.s.C / e->vec;
     int owg_n = (p.s.OW + e->tm - 1) / e->tm;
     long long rows = e->th > 0 ? (long long)(p.s.OH + e->th - 1) / e->th : p.s.OH;

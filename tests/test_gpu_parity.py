@@ -433,3 +433,60 @@ def test_size_limit_sampled(case):
         else:
             check.assert_float(yv[sel], fmt, ye, scale, what)
     say(f"      ok: {idx.size} outputs")
+
+
+# ------------------------------------------- filters of any size (row chunks)
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_row_chunks_any_filter(fmt):
+    """The row-chunk kernel (stride 1, dilation 1, any filter the compiled
+    tilings do not cover): chunk-boundary widths (8, 9, 15, 16, 17), tall
+    and flat filters, padding below, at and past half the filter, ragged
+    widths, against the whole-tensor oracle."""
+    rng = np.random.default_rng({"f32": 81, "f16": 82, "bf16": 83}[fmt])
+    vec = 4 if fmt == "f32" else 8
+    cases = [(2, 23, 37, 2 * vec, 9, 9, 4), (1, 20, 41, vec, 8, 8, 3), (1, 17, 30, 3 * vec, 15, 16, 7),
+             (1, 33, 35, vec, 17, 17, 8), (1, 12, 51, vec, 1, 33, 16), (1, 40, 20, 2 * vec, 33, 2, 1),
+             (1, 52, 53, vec, 51, 51, 25), (2, 9, 14, vec, 6, 11, 0), (1, 16, 16, vec, 12, 12, 13)]
+    for (N, H, W, C, FH, FW, P) in cases:
+        shape = (N, H, W, C, FH, FW, 1, 1, P)
+        if oracle.out_dim(H, FH, 1, 1, P) < 1 or oracle.out_dim(W, FW, 1, 1, P) < 1:
+            continue
+        h = dw.dwconv_create_variant(*shape, fmt, "rowwin")
+        desc = dw.dwconv_plan_describe(h)
+        dw.dwconv_destroy(h)
+        if not desc.startswith("rowchunk"):
+            continue  # a compiled tiling covers this filter
+        wl = synth.Workload("chunk", fmt, *shape, ("normal", 0.0, 1.0),
+                            ("normal", 0.0, 1.0 / (FH * FW)), ("uniform", -0.1, 0.1),
+                            int(rng.integers(0, 2**31)))
+        x, w, b = make_inputs(wl)
+        say(f"[gpu] row chunks {fmt} {shape}")
+        y, used = run(x, w, b, shape, fmt, "rowwin", guard=256)
+        assert_matches_oracle(y, x, w, b, shape, fmt, f"rowchunk {fmt} {shape}")
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16"])
+def test_sweep_maps_sampled(fmt):
+    """The filter-size sweep's three feature maps (two images instead of
+    128) at the sweep's filter sizes, through the planner's choice:
+    every output of the first and last rows and 3000 random ones, each
+    against the oracle."""
+    rng = np.random.default_rng(84 if fmt == "f32" else 85)
+    for (H, W, C) in [(128, 128, 128), (64, 64, 256), (32, 32, 1024)]:
+        for F in (3, 9, 17, 31, 51):
+            shape = (2, H, W, C, F, F, 1, 1, F // 2)
+            wl = synth.Workload("sweep", fmt, *shape, ("normal", 0.0, 1.0),
+                                ("normal", 0.0, 1.0 / (F * F)), ("uniform", -0.1, 0.1),
+                                int(rng.integers(0, 2**31)))
+            x, w, b = make_inputs(wl)
+            OH, OW = H, W
+            idx = [rng.integers(0, 2 * OH * OW * C, 3000)]
+            for n in (0, 1):
+                for oh in (0, OH - 1):
+                    idx.append(((n * OH + oh) * OW * C) + np.arange(OW * C))
+            idx = np.unique(np.concatenate(idx))
+            ye, scale = oracle.points(x, w, b, 1, 1, F // 2, fmt, idx)
+            say(f"[gpu] sweep map {fmt} {shape}")
+            y, used = run(x, w, b, shape, fmt, "auto", guard=256)
+            check.assert_float(y.ravel()[idx], fmt, ye, scale, f"sweep {fmt} {shape} {used}")
