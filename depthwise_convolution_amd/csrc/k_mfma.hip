@@ -200,11 +200,11 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         for (int e = 8 * tid; e < zlen; e += 8 * NT)   // zlen is a multiple of 8
             *reinterpret_cast<u32x4 *>(zt + e) = (u32x4){0u, 0u, 0u, 0u};
         __syncthreads();
-        // thread -> (fw = tid % 32, fh = tid / 32 + RPP*k): no divisions;
-        // the (at most 4) loads of a thread are issued before its LDS writes
+        // thread -> (fw = tid % 32 + 32j, fh = tid / 32 + RPP*k): no
+        // divisions; the (at most 4) loads of a thread are issued before its
+        // LDS writes
         constexpr int RPP = NT / 32;  // filter rows per pass of the workgroup
-        const int fw = tid & 31;
-        if (fw < s.FW) {
+        for (int fw = tid & 31; fw < s.FW; fw += 32) {
             const int f = fw >> 4, q = fw & 15;
             for (int fh0 = tid >> 5; fh0 < FH; fh0 += 4 * RPP) {
                 PixV v[4];
@@ -316,6 +316,31 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         for (int ci = 0; ci < NCH; ++ci)
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[ci][b] = (f32x4){bv[ci], bv[ci], bv[ci], bv[ci]};
+        // More than two fragments (filters wider than 32 taps): the chain of
+        // 16 filter rows (at most 64 MFMAs) is added into a separate fp32
+        // total, which the bias seeds, and restarts from zero.
+        constexpr bool FOLD = NFRAG > 2;
+        f32x4 tot[FOLD ? NCH : 1][FOLD ? NB : 1];
+        auto fold = [&]() {
+            if constexpr (FOLD) {
+#pragma unroll
+                for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        tot[ci][b] += acc[ci][b];
+                        acc[ci][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                    }
+            }
+        };
+        if constexpr (FOLD) {
+#pragma unroll
+            for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    tot[ci][b] = acc[ci][b];
+                    acc[ci][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                }
+        }
 
         // A windows of filter row fh: lane t16 holds row fh + t16 of the row
         // block.  Row fh+1's windows are row fh's moved down one lane within
@@ -495,8 +520,16 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     load_bs(o0, fh + 2);
                 }
                 mfmas(o1, fh + 1);
+                if (FOLD && (fh + 2) % 16 == 0) fold();
             }
             if (fh < FH) mfmas(o0, fh);
+        }
+        if constexpr (FOLD) {
+            fold();
+#pragma unroll
+            for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) acc[ci][b] = tot[ci][b];
         }
 
         // ---- epilogue: round once, regroup through LDS into NHWC vectors ----
@@ -614,6 +647,9 @@ static const MfmaEntry kMfma[] = {
     MF(DT_BF16, BF16, 8, 4, 1, 8, 0),  MF(DT_BF16, BF16, 8, 4, 1, 0, 0),
     MF(DT_BF16, BF16, 8, 4, 2, 0, 0),  MF(DT_BF16, BF16, 4, 4, 1, 8, 0),
     MF(DT_BF16, BF16, 4, 4, 1, 0, 0),  MF(DT_BF16, BF16, 4, 4, 2, 0, 0),
+    // filters of 33 to 64 taps: 32-column strips, one workgroup per CU
+    MF(DT_F16, F16, 4, 2, 3, 0, 0),    MF(DT_F16, F16, 4, 2, 4, 0, 0),
+    MF(DT_BF16, BF16, 4, 2, 3, 0, 0),  MF(DT_BF16, BF16, 4, 2, 4, 0, 0),
 };
 #undef MF
 #undef MFA

@@ -236,6 +236,26 @@ REG_TILES = {
 }
 
 
+def test_column_stream_5x5():
+    """The fp32 5x5 column stream (two channels per lane): ragged row strips
+    and column groups, an image shorter than a strip, odd channel-vector
+    counts, padding 0 to 4, against the oracle."""
+    rng = np.random.default_rng(86)
+    for shape in [(2, 30, 19, 16, 5, 5, 1, 1, 2), (1, 5, 57, 8, 5, 5, 1, 1, 2),
+                  (1, 33, 16, 6, 5, 5, 1, 1, 0), (1, 17, 17, 10, 5, 5, 1, 1, 4),
+                  (3, 40, 41, 2, 5, 5, 1, 1, 1)]:
+        wl = synth.Workload("cs5", "f32", *shape, ("normal", 0.0, 1.0), ("normal", 0.0, 1 / 25),
+                            ("uniform", -0.1, 0.1), int(rng.integers(0, 2**31)))
+        x, w, b = make_inputs(wl)
+        h = dw.dwconv_create(*shape, "f32")
+        desc = dw.dwconv_plan_describe(h)
+        dw.dwconv_destroy(h)
+        assert desc.startswith("colstream"), desc
+        say(f"[gpu] column stream 5x5 {shape}")
+        y, used = run(x, w, b, shape, "f32", "auto", guard=512)
+        assert_matches_oracle(y, x, w, b, shape, "f32", f"cs5 {shape}")
+
+
 @pytest.mark.parametrize("fmt", sorted(REG_TILES))
 def test_each_column_stream_tiling(fmt, monkeypatch):
     """Each compiled column-stream tiling (picked through the DWCONV_TILE
@@ -313,7 +333,7 @@ def test_each_lds_tile_entry(entry, monkeypatch):
 
 
 MFMA_SLICES = {  # channel slice -> (dtype, F) combinations it is compiled for
-    4: [("f16", 31), ("bf16", 31), ("f16", 5), ("bf16", 9)],
+    4: [("f16", 31), ("bf16", 31), ("f16", 5), ("bf16", 9), ("f16", 41), ("bf16", 51)],
     8: [("f16", 7), ("bf16", 7), ("f16", 5), ("bf16", 17)],
     16: [("f16", 7), ("bf16", 7)],
 }
