@@ -55,6 +55,7 @@ def bind(path):
     lib.dwref_bwd_data_f64.argtypes = [P, P, P, P] + [I] * 11
     lib.dwref_bwd_data_f64.restype = I
     lib.dwref_bwd_filter_f64.argtypes = [P, P, P, P] + [I] * 9
+    lib.dwref_fwd_bnact_f64.argtypes = [P, P, P, P, P, I, P, P] + [I] * 11
     lib.dwref_bwd_filter_f64.restype = I
     return lib
 
@@ -232,3 +233,49 @@ def bwd_filter(x, dy, shape, dtype, lib=None):
     if rc:
         raise ValueError("oracle rejected the shape")
     return dw, scale
+
+
+ACTS = {"none": 0, "relu": 1, "relu6": 2}
+
+
+def fwd_bn_act(x, w, bias, bn_scale, bn_shift, act, stride, dilation, pad, dtype, threads=1,
+               lib=None):
+    """Forward pass of act(x * bn_scale + bn_shift) -- a per-channel affine
+    (folded batch normalization) and an activation fused in front of the
+    convolution ("Flash-DWC", section 5.2) -- with zero padding of the
+    activated input.  ``act`` is "none", "relu" or "relu6"; bn_scale and
+    bn_shift hold C fp32 values.  Float dtypes only.  Returns ``(y, scale)``
+    in fp64, scale the sum of |x*s + b| * |w| over each output's taps."""
+    if dtype not in ("f32", "f16", "bf16"):
+        raise ValueError("the fused prologue is defined here for float dtypes")
+    if act not in ACTS:
+        raise ValueError(f"unknown activation {act!r}")
+    xx, ww, bb = _prep(x, w, bias, dtype)
+    N, H, W, C = xx.shape
+    FH, FW = ww.shape[:2]
+    ss = np.ascontiguousarray(np.asarray(bn_scale, dtype=np.float32).astype(np.float64))
+    tt = np.ascontiguousarray(np.asarray(bn_shift, dtype=np.float32).astype(np.float64))
+    if ss.shape != (C,) or tt.shape != (C,):
+        raise ValueError("bn_scale and bn_shift must have C elements")
+    lib = lib or _load()
+    OH = out_dim(H, FH, stride, dilation, pad, lib)
+    OW = out_dim(W, FW, stride, dilation, pad, lib)
+    if OH < 1 or OW < 1:
+        raise ValueError("no output: the filter span exceeds the padded input")
+    y = np.empty((N, OH, OW, C), np.float64)
+    scale = np.empty((N, OH, OW, C), np.float64)
+
+    def run(n0, n1):
+        return lib.dwref_fwd_bnact_f64(_ptr(xx), _ptr(ww), _ptr(bb), _ptr(ss), _ptr(tt),
+                                       ACTS[act], _ptr(y), _ptr(scale),
+                                       N, H, W, C, FH, FW, stride, dilation, pad, n0, n1)
+    threads = max(1, min(int(threads), N))
+    if threads == 1:
+        rcs = [run(0, N)]
+    else:
+        bounds = np.linspace(0, N, threads + 1).astype(int)
+        with ThreadPoolExecutor(threads) as ex:
+            rcs = list(ex.map(run, bounds[:-1], bounds[1:]))
+    if any(rcs):
+        raise ValueError("oracle rejected the shape")
+    return y, scale

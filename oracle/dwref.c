@@ -290,3 +290,58 @@ int dwref_bwd_filter_f64(const double *x, const double *dy, double *dw, double *
             }
     return 0;
 }
+
+/* Forward pass with the per-channel affine (batch normalization folded to a
+ * scale and a shift) and an activation fused in front of the convolution
+ * ("Flash-DWC: Making Depthwise Convolution Compute-Efficient on GPUs",
+ * section 5.2: the common BN + Act + DWC pattern, with BN and Act applied to
+ * the input inside the convolution kernel).  The convolution's input is
+ *
+ *   U[n,h,w,c] = act(X[n,h,w,c] * bn_scale[c] + bn_shift[c])
+ *
+ * with act 0 = identity, 1 = max(u, 0), 2 = min(max(u, 0), 6); positions
+ * outside the image are zeros of U (the convolution pads its own input, so
+ * they are not act(bn_shift)).  Then
+ *
+ *   Y[n,oh,ow,c] = bias[c] + sum over in-image taps of U * W[fh,fw,c]
+ *
+ * all in fp64.  scale = sum over the same taps of |X*s + b| * |W| (the
+ * magnitude before the activation).  Same layouts and batch split as
+ * dwref_fwd_f64.  Returns 0, or -1 on a bad shape or activation. */
+int dwref_fwd_bnact_f64(const double *x, const double *w, const double *bias,
+                        const double *bn_scale, const double *bn_shift, int act,
+                        double *y, double *scale,
+                        int N, int H, int W, int C, int FH, int FW, int S, int D, int P,
+                        int n0, int n1)
+{
+    int OH, OW;
+    if (!shape_ok(N, H, W, C, FH, FW, S, D, P, &OH, &OW)) return -1;
+    if (n0 < 0 || n1 > N || n0 > n1 || act < 0 || act > 2) return -1;
+    for (long long n = n0; n < n1; ++n)
+        for (int oh = 0; oh < OH; ++oh)
+            for (int ow = 0; ow < OW; ++ow)
+                for (int c = 0; c < C; ++c) {
+                    double acc = bias ? bias[c] : 0.0;
+                    double sabs = 0.0;
+                    for (int fh = 0; fh < FH; ++fh) {
+                        int ih = oh * S - P + fh * D;
+                        if (ih < 0 || ih >= H) continue;      /* zero of U */
+                        for (int fw = 0; fw < FW; ++fw) {
+                            int iw = ow * S - P + fw * D;
+                            if (iw < 0 || iw >= W) continue;
+                            double pre = x[((n * H + ih) * (long long)W + iw) * C + c] *
+                                         bn_scale[c] + bn_shift[c];
+                            double u = pre;
+                            if (act >= 1 && u < 0.0) u = 0.0;
+                            if (act == 2 && u > 6.0) u = 6.0;
+                            double wv = w[((long long)fh * FW + fw) * C + c];
+                            acc += u * wv;
+                            sabs += fabs(pre) * fabs(wv);
+                        }
+                    }
+                    long long o = ((n * OH + oh) * (long long)OW + ow) * C + c;
+                    y[o] = acc;
+                    if (scale) scale[o] = sabs;
+                }
+    return 0;
+}
