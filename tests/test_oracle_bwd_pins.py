@@ -289,10 +289,12 @@ def _bwf_pins(lib):
 def test_bwd_filter_mutants_are_caught(tmp_path):
     src = open(os.path.join(os.path.dirname(oracle.__file__), "dwref.c")).read()
     head, tail = src.split("int dwref_bwd_filter_f64(", 1)
+    body, rest = tail.split("\n/* Forward pass with the per-channel affine", 1)  # this function
     for name, (old, new) in BWF_MUTANTS.items():
-        assert tail.count(old) == 1, name
+        assert body.count(old) == 1, name
         path = tmp_path / f"bwf_{name}.c"
-        path.write_text(head + "int dwref_bwd_filter_f64(" + tail.replace(old, new, 1))
+        path.write_text(head + "int dwref_bwd_filter_f64(" + body.replace(old, new, 1) +
+                        "\n/* Forward pass with the per-channel affine" + rest)
         so = tmp_path / f"libbwf_{name}.so"
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", str(path),
                                "-o", str(so), "-lm"])
