@@ -47,6 +47,8 @@ METRIC_BWD = ("depthwise-conv bwd-data GB/s + GFLOP/s and fraction of HBM roofli
               "1 MI355X")
 METRIC_BWF = ("depthwise-conv bwd-filter GB/s + GFLOP/s and fraction of HBM roofline, "
               "1 MI355X")
+METRIC_BNACT = ("depthwise-conv fwd with fused BN+ReLU prologue GB/s + GFLOP/s and fraction "
+                "of HBM roofline, 1 MI355X")
 DEFAULT_WORKLOAD = "mobilenet_f32_3x3"
 HBM_PEAK_GBS = 8000.0
 # Published dense peaks of MI355X used for compute-bound kernels.  The VALU
@@ -152,10 +154,11 @@ def copy_ceiling(torch, dev, stream, nbytes, sets, K, warmup):
             "bytes": 2 * half, "kind": "torch copy_ (device to device), back to back"}
 
 
-def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd"):
+def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd", bn=None):
     """The CPU oracle (test infrastructure, untuned) on this host's cores.
     Sample: whole images of the same workload, as many as fit the budget
-    after a one-image probe.  For the backward-data pass x holds dy."""
+    after a one-image probe.  For the backward-data pass x holds dy; for the
+    fused-prologue pass bn is (scale, shift) as numpy fp32 arrays."""
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
 
@@ -166,6 +169,9 @@ def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd"):
         elif op == "bwd_data":
             shape = (n, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
             oracle.bwd_data(x[:n], w, shape, wl.dtype, threads=t)
+        elif op == "fwd_bn_act":
+            oracle.fwd_bn_act(x[:n], w, b, bn[0], bn[1], "relu", wl.stride, wl.dilation,
+                              wl.pad, wl.dtype, threads=t)
         else:
             oracle.fwd(x[:n], w, b, wl.stride, wl.dilation, wl.pad, wl.dtype, threads=t)
     t0 = time.perf_counter()
@@ -184,6 +190,8 @@ def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd"):
     if op == "bwd_filter":
         nbytes = (n * OH * OW + n * wl.H * wl.W) * wl.C * XB[wl.dtype] + \
             wl.FH * wl.FW * wl.C * 4
+    if op == "fwd_bn_act":
+        nbytes += 2 * wl.C * 4
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n} of {wl.N} images of {wl.name} ({op}; fp64/int64 loop nest, "
@@ -271,7 +279,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--variant", default="auto")
-    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd_data", "bwd_filter"],
+    ap.add_argument("--op", default="fwd",
+                    choices=["fwd", "bwd_data", "bwd_filter", "fwd_bn_act"],
                     help="the forward pass (default), backward data or backward filter")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-copy", action="store_true",
@@ -303,8 +312,12 @@ def main():
     nbytes, flops, OH, OW = work(wl)
     bwd = args.op == "bwd_data"
     bwf = args.op == "bwd_filter"
+    bna = args.op == "fwd_bn_act"
     print(f"[bench] {wl.name} ({args.op}): generating inputs", file=sys.stderr, flush=True)
     x, w, b = make_inputs(wl)
+    if bna:
+        # the forward pass plus the per-channel scale and shift it reads
+        nbytes += 2 * wl.C * 4
     if bwf:
         # the pass reads x and dy (N x OH x OW x C, drawn like x) and writes
         # the fp32 filter gradient; w holds dy here
@@ -375,6 +388,21 @@ def main():
 
         def step(i):
             dw.dwconv_bwd_data(h, xs[i % sets], wd, ys[i % sets], stream)
+    elif bna:
+        desc = dw.dwconv_fwd_bn_act_describe(h)
+        if not desc:
+            print(f"bench.py: {wl.name} has no fused-prologue pass", file=sys.stderr)
+            sys.exit(2)
+        variant = next(v for v in ("mfma", "ldstile", "direct", "rowwin", "colstream",
+                                   "rowchunk") if desc.startswith(v))
+        variant = "rowwin" if variant in ("colstream", "rowchunk") else variant
+        rs = np.random.default_rng(wl.seed + 300)
+        bn_s = torch.from_numpy(rs.uniform(0.5, 1.5, wl.C).astype(np.float32)).to(dev)
+        bn_b = torch.from_numpy(rs.normal(0.0, 0.5, wl.C).astype(np.float32)).to(dev)
+
+        def step(i):
+            dw.dwconv_fwd_bn_act(h, xs[i % sets], wd, bd, bn_s, bn_b, "relu", ys[i % sets],
+                                 stream)
     else:
         variant = dw.dwconv_plan_variant(h)
         desc = dw.dwconv_plan_describe(h)
@@ -439,10 +467,12 @@ def main():
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, x, w, b, op=args.op)
+        cpu = cpu_baseline(wl, x, w, b, op=args.op,
+                           bn=(bn_s.cpu().numpy(), bn_b.cpu().numpy()) if bna else None)
 
     rec = {
-        "metric": {"fwd": METRIC, "bwd_data": METRIC_BWD, "bwd_filter": METRIC_BWF}[args.op],
+        "metric": {"fwd": METRIC, "bwd_data": METRIC_BWD, "bwd_filter": METRIC_BWF,
+                   "fwd_bn_act": METRIC_BNACT}[args.op],
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -63,6 +63,12 @@ _lib.dwconv_plan_describe.argtypes = [_H]
 _lib.dwconv_plan_describe.restype = ctypes.c_char_p
 _lib.dwconv_status_string.argtypes = [_I]
 _lib.dwconv_status_string.restype = ctypes.c_char_p
+_lib.dwconv_fwd_bn_act.argtypes = [_H, _H, _H, _H, _H, _H, _I, _H, _H]
+_lib.dwconv_fwd_bn_act.restype = _I
+_lib.dwconv_fwd_bn_act_supported.argtypes = [_H]
+_lib.dwconv_fwd_bn_act_supported.restype = _I
+_lib.dwconv_fwd_bn_act_describe.argtypes = [_H]
+_lib.dwconv_fwd_bn_act_describe.restype = ctypes.c_char_p
 _lib.dwconv_bwd_data.argtypes = [_H, _H, _H, _H, _H]
 _lib.dwconv_bwd_data.restype = _I
 _lib.dwconv_bwd_data_supported.argtypes = [_H]
@@ -167,6 +173,29 @@ def dwconv_fwd(h, x, w, bias, y, stream=None) -> None:
         raise DwconvError(rc, "dwconv_fwd")
 
 
+ACTIVATIONS = {"none": 0, "relu": 1, "relu6": 2}
+
+
+def dwconv_fwd_bn_act(h, x, w, bias, bn_scale, bn_shift, act, y, stream=None) -> None:
+    """Enqueues the forward pass of act(x * bn_scale + bn_shift) (the fused
+    batch-normalization + activation prologue): bn_scale and bn_shift are C
+    float32 GPU tensors (or device pointers); ``act`` is "none", "relu",
+    "relu6" or its number.  Other arguments as for ``dwconv_fwd``."""
+    a = ACTIVATIONS[act] if isinstance(act, str) else int(act)
+    rc = _lib.dwconv_fwd_bn_act(h, _ptr(x), _ptr(w), _ptr(bias), _ptr(bn_scale), _ptr(bn_shift),
+                                a, _ptr(y), _stream(stream, x))
+    if rc != 0:
+        raise DwconvError(rc, "dwconv_fwd_bn_act")
+
+
+def dwconv_fwd_bn_act_supported(h) -> bool:
+    return bool(_lib.dwconv_fwd_bn_act_supported(h))
+
+
+def dwconv_fwd_bn_act_describe(h) -> str:
+    return _lib.dwconv_fwd_bn_act_describe(h).decode()
+
+
 def dwconv_bwd_data(h, dy, w, dx, stream=None) -> None:
     """Enqueues the backward-data pass: dx (N x H x W x C) from dy
     (N x OH x OW x C) and the forward filter w.  Tensors or raw device
@@ -236,6 +265,17 @@ class DepthwiseConv2d:
             y = torch.empty((N, self.OH, self.OW, C), device=x.device,
                             dtype=getattr(torch, self._TORCH_Y[self.dtype]))
         dwconv_fwd(self.handle, x, w, bias, y, stream)
+        return y
+
+    def forward_bn_act(self, x, w, bn_scale, bn_shift, act="relu", bias=None, y=None,
+                       stream=None):
+        """y = conv(act(x * bn_scale + bn_shift)) with the prologue fused."""
+        import torch
+        N, _, _, C = self.shape[:4]
+        if y is None:
+            y = torch.empty((N, self.OH, self.OW, C), device=x.device,
+                            dtype=getattr(torch, self._TORCH_Y[self.dtype]))
+        dwconv_fwd_bn_act(self.handle, x, w, bias, bn_scale, bn_shift, act, y, stream)
         return y
 
     def backward_data(self, dy, w, dx=None, stream=None):

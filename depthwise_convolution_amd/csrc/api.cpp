@@ -7,6 +7,8 @@
 
 struct dwconv_plan {
     dw::Plan p;      // forward
+    dw::Plan bnp;    // forward with the fused prologue, when has_bn
+    bool has_bn;
     dw::Plan bwd;    // backward data, when has_bwd
     bool has_bwd;
     dw::BwfPlan bwf; // backward filter, when has_bwf
@@ -53,6 +55,7 @@ dwconv_status_t dwconv_create_variant(dwconv_handle_t *out, int N, int H, int W,
         delete h;
         return (dwconv_status_t)rc;
     }
+    h->has_bn = dw::plan_bn_act(h->bnp, h->p);
     h->has_bwd = plan_bwd_data(h->bwd, h->p, (int)variant);
     h->has_bwf = dw::plan_bwd_filter(h->bwf, h->p);
     *out = h;
@@ -79,6 +82,27 @@ dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
     dw::LaunchFn fn = ok_align ? p.launch : p.fallback;
     hipError_t e = fn(p, x, w, bias, y, stream);
     return e == hipSuccess ? DWCONV_OK : DWCONV_ERR_HIP;
+}
+
+dwconv_status_t dwconv_fwd_bn_act(dwconv_handle_t h, const void *x, const void *w,
+                                  const void *bias, const float *bn_scale,
+                                  const float *bn_shift, dwconv_act_t act, void *y,
+                                  hipStream_t stream) {
+    if (!h || !x || !w || !y || !bn_scale || !bn_shift) return DWCONV_ERR_INVALID_ARG;
+    if ((int)act < DWCONV_ACT_NONE || (int)act > DWCONV_ACT_RELU6) return DWCONV_ERR_INVALID_ARG;
+    if (!h->has_bn) return DWCONV_ERR_UNSUPPORTED;
+    const dw::Plan &p = h->bnp;
+    bool ok_align = aligned16(x) && aligned16(w) && aligned16(y) &&
+                    (bias == nullptr || aligned16(bias));
+    dw::LaunchBnFn fn = ok_align ? p.bn_launch : p.bn_fallback;
+    hipError_t e = fn(p, x, w, bias, bn_scale, bn_shift, (int)act, y, stream);
+    return e == hipSuccess ? DWCONV_OK : DWCONV_ERR_HIP;
+}
+
+int dwconv_fwd_bn_act_supported(dwconv_handle_t h) { return h && h->has_bn ? 1 : 0; }
+
+const char *dwconv_fwd_bn_act_describe(dwconv_handle_t h) {
+    return h && h->has_bn ? h->bnp.desc : "";
 }
 
 dwconv_status_t dwconv_bwd_data(dwconv_handle_t h, const void *dy, const void *w, void *dx,

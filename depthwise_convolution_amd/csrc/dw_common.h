@@ -88,6 +88,19 @@ __device__ __forceinline__ int32_t mac<int32_t>(int32_t acc, int32_t a, int32_t 
     return acc + __mul24(a, b);
 }
 
+// The fused prologue of the forward pass ("Flash-DWC: Making Depthwise
+// Convolution Compute-Efficient on GPUs", section 5.2: BN and the activation
+// applied to the input inside the convolution kernel): the input value x,
+// widened to fp32, becomes act(x * s + b) with one fused multiply-add and no
+// rounding to the storage format; act 0 = identity, 1 = ReLU, 2 = ReLU6.
+// Padding positions are zeros of the result, so callers apply it to in-image
+// values only.
+__device__ __forceinline__ float bn_act(float x, float s, float b, int act) {
+    float u = __builtin_fmaf(x, s, b);
+    u = act >= 1 ? __builtin_fmaxf(u, 0.0f) : u;
+    return act == 2 ? __builtin_fminf(u, 6.0f) : u;
+}
+
 // Greatest common divisor (compile-time or host use).
 __host__ __device__ constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 

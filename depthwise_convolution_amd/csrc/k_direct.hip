@@ -18,11 +18,14 @@
 
 namespace dw {
 
-template <class DT>
+// BN: every in-image input value goes through the fused prologue
+// act(x * bns[c] + bnb[c]) first (float formats only).
+template <class DT, bool BN>
 __global__ void __launch_bounds__(256)
 k_direct(const typename DT::X *__restrict__ x, const typename DT::X *__restrict__ w,
          const typename DT::Bias *__restrict__ bias, typename DT::Y *__restrict__ y,
-         Shape s, long long total) {
+         Shape s, long long total, const float *__restrict__ bns,
+         const float *__restrict__ bnb, int act) {
     using Acc = typename DT::Acc;
     const long long stride = (long long)gridDim.x * blockDim.x;
     for (long long o = (long long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
@@ -34,6 +37,11 @@ k_direct(const typename DT::X *__restrict__ x, const typename DT::X *__restrict_
         int oh = (int)(r % s.OH);
         long long n = r / s.OH;
         Acc acc = bias ? bias[c] : Acc(0);
+        Acc bs = Acc(0), bb = Acc(0);
+        if constexpr (BN) {
+            bs = bns[c];
+            bb = bnb[c];
+        }
         for (int fh = 0; fh < s.FH; ++fh) {
             int ih = oh * s.S - s.P + fh * s.D;
             if ((unsigned)ih >= (unsigned)s.H) continue;  // generated zero rows
@@ -43,8 +51,9 @@ k_direct(const typename DT::X *__restrict__ x, const typename DT::X *__restrict_
             for (int fw = 0; fw < s.FW; ++fw) {
                 int iw = ow * s.S - s.P + fw * s.D;
                 if ((unsigned)iw >= (unsigned)s.W) continue;  // generated zeros
-                row = mac<Acc>(row, DT::widen(xr[(long long)iw * s.C]),
-                               DT::widen(wc[(long long)tap_index(s, fh, fw) * s.C]));
+                Acc xv = DT::widen(xr[(long long)iw * s.C]);
+                if constexpr (BN) xv = bn_act(xv, bs, bb, act);
+                row = mac<Acc>(row, xv, DT::widen(wc[(long long)tap_index(s, fh, fw) * s.C]));
             }
             acc += row;
         }
@@ -56,9 +65,22 @@ template <class DT>
 static hipError_t launch_direct(const Plan &p, const void *x, const void *w,
                                 const void *bias, void *y, hipStream_t st) {
     long long total = (long long)p.s.N * p.s.OH * p.s.OW * p.s.C;
-    hipLaunchKernelGGL(k_direct<DT>, dim3(p.grid), dim3(p.block), 0, st,
+    hipLaunchKernelGGL((k_direct<DT, false>), dim3(p.grid), dim3(p.block), 0, st,
                        (const typename DT::X *)x, (const typename DT::X *)w,
-                       (const typename DT::Bias *)bias, (typename DT::Y *)y, p.s, total);
+                       (const typename DT::Bias *)bias, (typename DT::Y *)y, p.s, total,
+                       nullptr, nullptr, 0);
+    return hipGetLastError();
+}
+
+template <class DT>
+static hipError_t launch_direct_bn(const Plan &p, const void *x, const void *w,
+                                   const void *bias, const float *bns, const float *bnb,
+                                   int act, void *y, hipStream_t st) {
+    long long total = (long long)p.s.N * p.s.OH * p.s.OW * p.s.C;
+    hipLaunchKernelGGL((k_direct<DT, true>), dim3(p.grid), dim3(p.block), 0, st,
+                       (const typename DT::X *)x, (const typename DT::X *)w,
+                       (const typename DT::Bias *)bias, (typename DT::Y *)y, p.s, total, bns,
+                       bnb, act);
     return hipGetLastError();
 }
 
@@ -125,6 +147,7 @@ static hipError_t launch_bwd_direct(const Plan &p, const void *dy, const void *w
 bool plan_bwd_direct(Plan &b, const Plan &f) {
     b = f;
     b.s.flip = 0;
+    b.bn_launch = b.bn_fallback = nullptr;
     const long long total = (long long)f.s.N * f.s.H * f.s.W * f.s.C;
     b.variant = V_DIRECT;
     b.block = 256;
@@ -152,12 +175,13 @@ bool plan_direct(Plan &p) {
     p.vec = 1;
     p.tm = 1;
     switch (p.dtype) {
-        case DT_F32: p.launch = launch_direct<F32>; break;
-        case DT_F16: p.launch = launch_direct<F16>; break;
-        case DT_BF16: p.launch = launch_direct<BF16>; break;
-        case DT_I8: p.launch = launch_direct<I8>; break;
+        case DT_F32: p.launch = launch_direct<F32>; p.bn_launch = launch_direct_bn<F32>; break;
+        case DT_F16: p.launch = launch_direct<F16>; p.bn_launch = launch_direct_bn<F16>; break;
+        case DT_BF16: p.launch = launch_direct<BF16>; p.bn_launch = launch_direct_bn<BF16>; break;
+        case DT_I8: p.launch = launch_direct<I8>; p.bn_launch = nullptr; break;
         default: return false;
     }
+    p.bn_fallback = p.bn_launch;
     snprintf(p.desc, sizeof(p.desc), "direct: 1 output/lane, %u x %d", p.grid, p.block);
     return true;
 }

@@ -68,10 +68,13 @@ __device__ __forceinline__ void store_vec(E *dst, const E (&src)[VEC]) {
 // it to the accumulator type.  Columns outside the image read as zero: their
 // address is clamped to column 0 (always inside the row, so the load is in
 // bounds and branch-free) and the value is replaced by zero.
-template <class DT, int VEC, int NWIN>
+// BN: in-image values go through the fused prologue bn_act (bs, bb: the
+// lane's VEC scales and shifts); positions outside the image stay zero.
+template <class DT, int VEC, int NWIN, bool BN = false>
 __device__ __forceinline__ void load_window(typename DT::Acc (&xw)[NWIN][VEC],
                                             const typename DT::X *xr, int iw0, int W,
-                                            int C) {
+                                            int C, const float *bs = nullptr,
+                                            const float *bb = nullptr, int act = 0) {
     using X = typename DT::X;
     X e[NWIN][VEC];
 #pragma unroll
@@ -84,7 +87,22 @@ __device__ __forceinline__ void load_window(typename DT::Acc (&xw)[NWIN][VEC],
     for (int j = 0; j < NWIN; ++j) {
         const bool ok = (unsigned)(iw0 + j) < (unsigned)W;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) xw[j][v] = ok ? DT::widen(e[j][v]) : typename DT::Acc(0);
+        for (int v = 0; v < VEC; ++v) {
+            typename DT::Acc val = DT::widen(e[j][v]);
+            if constexpr (BN) val = bn_act(val, bs[v], bb[v], act);
+            xw[j][v] = ok ? val : typename DT::Acc(0);
+        }
+    }
+}
+
+// The lane's VEC fused-prologue scales and shifts (channels c0 ..).
+template <int VEC>
+__device__ __forceinline__ void load_bn(float (&bs)[VEC], float (&bb)[VEC], const float *bns,
+                                        const float *bnb, int c0) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        bs[v] = bns[c0 + v];
+        bb[v] = bnb[c0 + v];
     }
 }
 
@@ -110,11 +128,12 @@ __device__ __forceinline__ void store_out(Y *dst, const Y (&o)[VEC]) {
 // ---------------------------------------------------------------------------
 // Row window: one output row per lane, any stride and dilation.
 // ---------------------------------------------------------------------------
-template <class DT, int VEC, int FW, int TM, int S, int D>
+template <class DT, int VEC, int FW, int TM, int S, int D, bool BN>
 __global__ void __launch_bounds__(256)
 k_rowwin(const typename DT::X *__restrict__ x, const typename DT::X *__restrict__ w,
          const typename DT::Bias *__restrict__ bias, typename DT::Y *__restrict__ y,
-         Shape s, int ncv, int owg_n, long long total) {
+         Shape s, int ncv, int owg_n, long long total, const float *__restrict__ bns,
+         const float *__restrict__ bnb, int act) {
     using X = typename DT::X;
     using Acc = typename DT::Acc;
     constexpr int NWIN = (TM - 1) * S + (FW - 1) * D + 1;
@@ -131,6 +150,8 @@ k_rowwin(const typename DT::X *__restrict__ x, const typename DT::X *__restrict_
     const int c0 = cv * VEC;
     const int ow0 = owg * TM;
     const int iw0 = ow0 * S - s.P;
+    float bs[VEC], bb[VEC];
+    if constexpr (BN) load_bn<VEC>(bs, bb, bns, bnb, c0);
 
     Acc acc[TM][VEC];
     {
@@ -149,7 +170,7 @@ k_rowwin(const typename DT::X *__restrict__ x, const typename DT::X *__restrict_
         const X *xr = x + ((n * s.H + ih) * (long long)s.W) * s.C + c0;
 
         Acc xw[NWIN][VEC];  // input run of this filter row, widened once
-        load_window<DT, VEC, NWIN>(xw, xr, iw0, s.W, s.C);
+        load_window<DT, VEC, NWIN, BN>(xw, xr, iw0, s.W, s.C, bs, bb, act);
         Acc wt[FW][VEC];
 #pragma unroll
         for (int fw = 0; fw < FW; ++fw) {
@@ -198,11 +219,12 @@ k_rowwin(const typename DT::X *__restrict__ x, const typename DT::X *__restrict_
 // Compute-Efficient on GPUs", section 3.3: the 2-D filter as FH 1-D rows,
 // each reusing one input run across its taps).
 // ---------------------------------------------------------------------------
-template <class DT, int VEC, int TM, int CH>
+template <class DT, int VEC, int TM, int CH, bool BN>
 __global__ void __launch_bounds__(256)
 k_rowchunk(const typename DT::X *__restrict__ x, const typename DT::X *__restrict__ w,
            const typename DT::Bias *__restrict__ bias, typename DT::Y *__restrict__ y,
-           Shape s, int ncv, int owg_n, long long total) {
+           Shape s, int ncv, int owg_n, long long total, const float *__restrict__ bns,
+           const float *__restrict__ bnb, int act) {
     using X = typename DT::X;
     using Acc = typename DT::Acc;
     constexpr int NWIN = TM + CH - 1;
@@ -220,6 +242,8 @@ k_rowchunk(const typename DT::X *__restrict__ x, const typename DT::X *__restric
     const int ow0 = owg * TM;
     const int iw0 = ow0 - s.P;
     const int nch = (s.FW + CH - 1) / CH;
+    float bs[VEC], bb[VEC];
+    if constexpr (BN) load_bn<VEC>(bs, bb, bns, bnb, c0);
 
     Acc acc[TM][VEC];
     {
@@ -244,7 +268,7 @@ k_rowchunk(const typename DT::X *__restrict__ x, const typename DT::X *__restric
         for (int k = 0; k < nch; ++k) {
             const int fw0 = k * CH;
             Acc xw[NWIN][VEC];
-            load_window<DT, VEC, NWIN>(xw, xr, iw0 + fw0, s.W, s.C);
+            load_window<DT, VEC, NWIN, BN>(xw, xr, iw0 + fw0, s.W, s.C, bs, bb, act);
             Acc wt[CH][VEC];
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
@@ -329,12 +353,13 @@ __device__ __forceinline__ void fetch_run(X (&e)[NWIN][VEC], const X *xn, int ih
 // filter rows in the order fh = FH-1 .. 0, starts (bias) at fh = FH-1 and is
 // stored after fh = 0.
 template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, int NTL,
-          bool UP>
+          bool UP, bool BN>
 __device__ __forceinline__ void colstream_walk(const typename DT::X *xn,
                                                const typename DT::Acc (&wt)[FH][FW][VEC],
                                                const typename DT::Acc (&b0)[VEC],
                                                typename DT::Y *yn, const Shape &s, int ih0,
-                                               int iw0, int oh0, int ow0) {
+                                               int iw0, int oh0, int ow0, const float *bs,
+                                               const float *bb, int act) {
     using X = typename DT::X;
     using Acc = typename DT::Acc;
     using Y = typename DT::Y;
@@ -362,8 +387,11 @@ __device__ __forceinline__ void colstream_walk(const typename DT::X *xn,
         for (int j = 0; j < NWIN; ++j) {
             const bool ok = row_ok && (unsigned)(iw0 + j) < (unsigned)s.W;
 #pragma unroll
-            for (int v = 0; v < VEC; ++v)
-                xw[j][v] = ok ? DT::widen(raw[k % RING][j][v]) : Acc(0);
+            for (int v = 0; v < VEC; ++v) {
+                Acc val = DT::widen(raw[k % RING][j][v]);
+                if constexpr (BN) val = bn_act(val, bs[v], bb[v], act);
+                xw[j][v] = ok ? val : Acc(0);
+            }
         }
 #pragma unroll
         for (int q = 0; q < FH; ++q) {
@@ -408,11 +436,13 @@ __device__ __forceinline__ void colstream_walk(const typename DT::X *xn,
 // directions, so that the two strips on either side of every boundary reach
 // the shared rows at about the same time (both at the start of their walk, or
 // both at the end) and the second request finds them in L2.
-template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, int NTL>
+template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, int NTL,
+          bool BN>
 __global__ void __launch_bounds__(256)
 k_colstream(const typename DT::X *__restrict__ x, const typename DT::X *__restrict__ w,
             const typename DT::Bias *__restrict__ bias, typename DT::Y *__restrict__ y,
-            Shape s, int ncv, int owg_n, int ohg_n, long long total) {
+            Shape s, int ncv, int owg_n, int ohg_n, long long total,
+            const float *__restrict__ bns, const float *__restrict__ bnb, int act) {
     using X = typename DT::X;
     using Acc = typename DT::Acc;
 
@@ -445,48 +475,89 @@ k_colstream(const typename DT::X *__restrict__ x, const typename DT::X *__restri
     Acc b0[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) b0[v] = bias ? bias[c0 + v] : Acc(0);
+    float bs[VEC], bb[VEC];
+    if constexpr (BN) load_bn<VEC>(bs, bb, bns, bnb, c0);
 
     typename DT::Y *yn = y + ((n * s.OH + oh0) * (long long)s.OW + ow0) * s.C + c0;
     if (ohg & 1)
-        colstream_walk<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL, true>(xn, wt, b0, yn, s, ih0, iw0,
-                                                                  oh0, ow0);
+        colstream_walk<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL, true, BN>(
+            xn, wt, b0, yn, s, ih0, iw0, oh0, ow0, bs, bb, act);
     else
-        colstream_walk<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL, false>(xn, wt, b0, yn, s, ih0, iw0,
-                                                                   oh0, ow0);
+        colstream_walk<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL, false, BN>(
+            xn, wt, b0, yn, s, ih0, iw0, oh0, ow0, bs, bb, act);
 }
 
+template <class DT, int VEC, int FW, int TM, int S, int D, bool BN>
+static hipError_t run_rowwin(const Plan &p, const void *x, const void *w, const void *bias,
+                             const float *bns, const float *bnb, int act, void *y,
+                             hipStream_t st) {
+    long long total = (long long)p.aux0 * p.aux1 * p.s.N * p.s.OH;
+    hipLaunchKernelGGL((k_rowwin<DT, VEC, FW, TM, S, D, BN>), dim3(p.grid), dim3(p.block), 0,
+                       st, (const typename DT::X *)x, (const typename DT::X *)w,
+                       (const typename DT::Bias *)bias, (typename DT::Y *)y, p.s, p.aux0,
+                       p.aux1, total, bns, bnb, act);
+    return hipGetLastError();
+}
 template <class DT, int VEC, int FW, int TM, int S, int D>
 static hipError_t launch_rowwin(const Plan &p, const void *x, const void *w,
                                 const void *bias, void *y, hipStream_t st) {
-    long long total = (long long)p.aux0 * p.aux1 * p.s.N * p.s.OH;
-    hipLaunchKernelGGL((k_rowwin<DT, VEC, FW, TM, S, D>), dim3(p.grid), dim3(p.block), 0, st,
-                       (const typename DT::X *)x, (const typename DT::X *)w,
-                       (const typename DT::Bias *)bias, (typename DT::Y *)y, p.s, p.aux0,
-                       p.aux1, total);
-    return hipGetLastError();
+    return run_rowwin<DT, VEC, FW, TM, S, D, false>(p, x, w, bias, nullptr, nullptr, 0, y, st);
+}
+template <class DT, int VEC, int FW, int TM, int S, int D>
+static hipError_t launch_rowwin_bn(const Plan &p, const void *x, const void *w,
+                                   const void *bias, const float *bns, const float *bnb,
+                                   int act, void *y, hipStream_t st) {
+    return run_rowwin<DT, VEC, FW, TM, S, D, true>(p, x, w, bias, bns, bnb, act, y, st);
 }
 
+template <class DT, int VEC, int TM, int CH, bool BN>
+static hipError_t run_rowchunk(const Plan &p, const void *x, const void *w, const void *bias,
+                               const float *bns, const float *bnb, int act, void *y,
+                               hipStream_t st) {
+    long long total = (long long)p.aux0 * p.aux1 * p.s.N * p.s.OH;
+    hipLaunchKernelGGL((k_rowchunk<DT, VEC, TM, CH, BN>), dim3(p.grid), dim3(p.block), 0, st,
+                       (const typename DT::X *)x, (const typename DT::X *)w,
+                       (const typename DT::Bias *)bias, (typename DT::Y *)y, p.s, p.aux0,
+                       p.aux1, total, bns, bnb, act);
+    return hipGetLastError();
+}
 template <class DT, int VEC, int TM, int CH>
 static hipError_t launch_rowchunk(const Plan &p, const void *x, const void *w,
                                   const void *bias, void *y, hipStream_t st) {
-    long long total = (long long)p.aux0 * p.aux1 * p.s.N * p.s.OH;
-    hipLaunchKernelGGL((k_rowchunk<DT, VEC, TM, CH>), dim3(p.grid), dim3(p.block), 0, st,
-                       (const typename DT::X *)x, (const typename DT::X *)w,
-                       (const typename DT::Bias *)bias, (typename DT::Y *)y, p.s, p.aux0,
-                       p.aux1, total);
-    return hipGetLastError();
+    return run_rowchunk<DT, VEC, TM, CH, false>(p, x, w, bias, nullptr, nullptr, 0, y, st);
+}
+template <class DT, int VEC, int TM, int CH>
+static hipError_t launch_rowchunk_bn(const Plan &p, const void *x, const void *w,
+                                     const void *bias, const float *bns, const float *bnb,
+                                     int act, void *y, hipStream_t st) {
+    return run_rowchunk<DT, VEC, TM, CH, true>(p, x, w, bias, bns, bnb, act, y, st);
 }
 
+template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, int NTL,
+          bool BN>
+static hipError_t run_colstream(const Plan &p, const void *x, const void *w, const void *bias,
+                                const float *bns, const float *bnb, int act, void *y,
+                                hipStream_t st) {
+    int ohg_n = (p.s.OH + TH - 1) / TH;
+    long long total = (long long)p.aux0 * p.aux1 * ohg_n * p.s.N;
+    hipLaunchKernelGGL((k_colstream<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL, BN>), dim3(p.grid),
+                       dim3(p.block), 0, st, (const typename DT::X *)x,
+                       (const typename DT::X *)w, (const typename DT::Bias *)bias,
+                       (typename DT::Y *)y, p.s, p.aux0, p.aux1, ohg_n, total, bns, bnb, act);
+    return hipGetLastError();
+}
 template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, int NTL>
 static hipError_t launch_colstream(const Plan &p, const void *x, const void *w,
                                    const void *bias, void *y, hipStream_t st) {
-    int ohg_n = (p.s.OH + TH - 1) / TH;
-    long long total = (long long)p.aux0 * p.aux1 * ohg_n * p.s.N;
-    hipLaunchKernelGGL((k_colstream<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL>), dim3(p.grid),
-                       dim3(p.block), 0, st, (const typename DT::X *)x,
-                       (const typename DT::X *)w, (const typename DT::Bias *)bias,
-                       (typename DT::Y *)y, p.s, p.aux0, p.aux1, ohg_n, total);
-    return hipGetLastError();
+    return run_colstream<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL, false>(p, x, w, bias, nullptr,
+                                                                        nullptr, 0, y, st);
+}
+template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, int NTL>
+static hipError_t launch_colstream_bn(const Plan &p, const void *x, const void *w,
+                                      const void *bias, const float *bns, const float *bnb,
+                                      int act, void *y, hipStream_t st) {
+    return run_colstream<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL, true>(p, x, w, bias, bns, bnb,
+                                                                       act, y, st);
 }
 
 // Compiled tilings.  th == 0: row window (any stride); th > 0: column stream
@@ -496,13 +567,19 @@ static hipError_t launch_colstream(const Plan &p, const void *x, const void *w,
 struct RegTile {
     int dtype, fh, fw, s, d, vec, tm, th, pf, nt, ntl;
     LaunchFn fn;
+    LaunchBnFn bnfn;  // with the fused prologue (float formats)
 };
 
-#define RW(DTE, DTT, FW_, S_, D_, VEC_, TM_) \
-    {DTE, 0, FW_, S_, D_, VEC_, TM_, 0, 0, 0, 0, launch_rowwin<DTT, VEC_, FW_, TM_, S_, D_>}
-#define CS(DTE, DTT, FH_, FW_, D_, VEC_, TM_, TH_, PF_, NT_, NTL_) \
-    {DTE, FH_, FW_, 1, D_, VEC_, TM_, TH_, PF_, NT_, NTL_,        \
-     launch_colstream<DTT, VEC_, FH_, FW_, TM_, TH_, D_, PF_, NT_, NTL_>}
+#define RW(DTE, DTT, FW_, S_, D_, VEC_, TM_)                                          \
+    {DTE, 0, FW_, S_, D_, VEC_, TM_, 0, 0, 0, 0, launch_rowwin<DTT, VEC_, FW_, TM_, S_, D_>, \
+     launch_rowwin_bn<DTT, VEC_, FW_, TM_, S_, D_>}
+#define RWI(DTE, DTT, FW_, S_, D_, VEC_, TM_)                                         \
+    {DTE, 0, FW_, S_, D_, VEC_, TM_, 0, 0, 0, 0, launch_rowwin<DTT, VEC_, FW_, TM_, S_, D_>, \
+     nullptr}
+#define CS(DTE, DTT, FH_, FW_, D_, VEC_, TM_, TH_, PF_, NT_, NTL_)          \
+    {DTE, FH_, FW_, 1, D_, VEC_, TM_, TH_, PF_, NT_, NTL_,                 \
+     launch_colstream<DTT, VEC_, FH_, FW_, TM_, TH_, D_, PF_, NT_, NTL_>, \
+     launch_colstream_bn<DTT, VEC_, FH_, FW_, TM_, TH_, D_, PF_, NT_, NTL_>}
 
 static const RegTile kTiles[] = {
     CS(DT_F32, F32, 3, 3, 1, 4, 4, 14, 2, 1, 2),
@@ -525,10 +602,11 @@ static const RegTile kTiles[] = {
     RW(DT_BF16, BF16, 3, 1, 1, 8, 4),
     RW(DT_BF16, BF16, 7, 1, 1, 8, 4),
     RW(DT_BF16, BF16, 31, 1, 1, 2, 4),
-    RW(DT_I8, I8, 3, 1, 1, 4, 4),
-    RW(DT_I8, I8, 5, 2, 2, 4, 2),
+    RWI(DT_I8, I8, 3, 1, 1, 4, 4),
+    RWI(DT_I8, I8, 5, 2, 2, 4, 2),
 };
 #undef RW
+#undef RWI
 #undef CS
 
 static bool tile_matches(const RegTile &k, const Plan &p) {
@@ -558,9 +636,18 @@ static bool plan_rowchunk(Plan &p) {
     p.aux0 = ncv;
     p.aux1 = owg_n;
     switch (p.dtype) {
-        case DT_F32: p.launch = launch_rowchunk<F32, 4, 8, 8>; break;
-        case DT_F16: p.launch = launch_rowchunk<F16, 8, 4, 8>; break;
-        case DT_BF16: p.launch = launch_rowchunk<BF16, 8, 4, 8>; break;
+        case DT_F32:
+            p.launch = launch_rowchunk<F32, 4, 8, 8>;
+            p.bn_launch = launch_rowchunk_bn<F32, 4, 8, 8>;
+            break;
+        case DT_F16:
+            p.launch = launch_rowchunk<F16, 8, 4, 8>;
+            p.bn_launch = launch_rowchunk_bn<F16, 8, 4, 8>;
+            break;
+        case DT_BF16:
+            p.launch = launch_rowchunk<BF16, 8, 4, 8>;
+            p.bn_launch = launch_rowchunk_bn<BF16, 8, 4, 8>;
+            break;
         default: return false;
     }
     snprintf(p.desc, sizeof(p.desc),
@@ -610,6 +697,7 @@ bool plan_rowwin(Plan &p) {
     p.aux0 = ncv;
     p.aux1 = owg_n;
     p.launch = e->fn;
+    p.bn_launch = e->bnfn;
     if (e->th > 0)
         snprintf(p.desc, sizeof(p.desc),
                  "colstream: VEC=%d ch/lane, TM=%d x TH=%d outputs/lane, %dx%d D=%d, "

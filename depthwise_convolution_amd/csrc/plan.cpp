@@ -73,7 +73,26 @@ int make_plan(Plan &p, int N, int H, int W, int C, int FH, int FW, int S, int D,
     }
     if (!ok) return DWCONV_ERR_UNSUPPORTED;
     p.fallback = d.launch;
+    p.bn_fallback = d.bn_launch;
     return DWCONV_OK;
+}
+
+bool plan_bn_act(Plan &b, const Plan &f) {
+    if (f.dtype == DT_I8) return false;
+    if (f.bn_launch) {  // the forward plan's family fuses the prologue
+        b = f;
+        return true;
+    }
+    // the matrix-core and LDS-tile families do not: the row window / row
+    // chunks where they apply, else the direct family
+    const Shape &s = f.s;
+    for (int v : {V_ROWWIN, V_DIRECT}) {
+        if (make_plan(b, s.N, s.H, s.W, s.C, s.FH, s.FW, s.S, s.D, s.P, f.dtype, v) ==
+                DWCONV_OK &&
+            b.bn_launch)
+            return true;
+    }
+    return false;
 }
 
 }  // namespace dw

@@ -15,6 +15,10 @@ enum Variant { V_AUTO = 0, V_DIRECT = 1, V_ROWWIN = 2, V_LDSTILE = 3, V_MFMA = 4
 struct Plan;
 using LaunchFn = hipError_t (*)(const Plan &, const void *x, const void *w,
                                 const void *bias, void *y, hipStream_t);
+// The forward pass with the fused prologue act(x * bn_scale + bn_shift).
+using LaunchBnFn = hipError_t (*)(const Plan &, const void *x, const void *w,
+                                  const void *bias, const float *bn_scale,
+                                  const float *bn_shift, int act, void *y, hipStream_t);
 
 struct Plan {
     Shape s;
@@ -32,6 +36,8 @@ struct Plan {
     int aux0, aux1, aux2, aux3;  // family-specific extra launch parameters
     LaunchFn launch;      // launcher for `variant`
     LaunchFn fallback;    // launcher for misaligned pointers (direct family)
+    LaunchBnFn bn_launch;   // the same tiling with the fused prologue (NULL: none)
+    LaunchBnFn bn_fallback; // the direct family with the fused prologue
     char desc[192];
 };
 
@@ -82,6 +88,10 @@ bool plan_direct(Plan &p);
 // Backward data for any float shape, one lane per input element; b gets the
 // forward plan's shape (dy N x OH x OW x C in, dx N x H x W x C out).
 bool plan_bwd_direct(Plan &b, const Plan &forward);
+// The forward pass with the fused prologue: the forward plan itself when its
+// family fuses it, else the row-window / row-chunk or the direct family for
+// the same shape.  Float dtypes only.
+bool plan_bn_act(Plan &b, const Plan &forward);
 bool plan_rowwin(Plan &p);
 bool plan_ldstile(Plan &p);
 bool plan_mfma(Plan &p);

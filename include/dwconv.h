@@ -76,6 +76,13 @@ typedef enum {
     DWCONV_VARIANT_MFMA = 4      /* banded-filter GEMM on the matrix cores      */
 } dwconv_variant_t;
 
+/* Activation of the fused forward prologue (dwconv_fwd_bn_act). */
+typedef enum {
+    DWCONV_ACT_NONE = 0,         /* identity                                    */
+    DWCONV_ACT_RELU = 1,         /* max(u, 0)                                   */
+    DWCONV_ACT_RELU6 = 2         /* min(max(u, 0), 6)                           */
+} dwconv_act_t;
+
 typedef struct dwconv_plan *dwconv_handle_t;
 
 /* Validates the operation and builds a plan.  Touches no GPU state.
@@ -105,6 +112,38 @@ dwconv_status_t dwconv_create_variant(dwconv_handle_t *out, int N, int H, int W,
  * handle, x, w or y, and DWCONV_ERR_HIP if the launch fails. */
 dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
                            const void *bias, void *y, hipStream_t stream);
+
+/* Forward pass with a fused prologue ("Flash-DWC: Making Depthwise
+ * Convolution Compute-Efficient on GPUs", section 5.2: batch normalization
+ * and the activation that usually precede a depthwise convolution, applied to
+ * its input inside the convolution kernel):
+ *
+ *   U[n,h,w,c]    = act(x[n,h,w,c] * bn_scale[c] + bn_shift[c])
+ *   y[n,oh,ow,c]  = bias[c] + sum_{fh,fw} U[n, oh*S-P+fh*D, ow*S-P+fw*D, c]
+ *                                         * w[fh,fw,c]
+ *
+ * U is computed in fp32 with one fused multiply-add per input value and is
+ * never rounded to the storage format; padding positions are zeros of U.
+ * bn_scale and bn_shift are C fp32 device values each -- batch normalization
+ * folded by the caller (scale = gamma / sqrt(var + eps), shift = beta -
+ * mean * scale) -- owned by the caller, any 4-byte alignment.  x, w, bias and
+ * y as for dwconv_fwd; the same tolerance as the forward pass applies, stated
+ * against sum |x*s + b| * |w|.  Small filters run on the register families
+ * with the prologue fused (the matrix-core and LDS-tile families do not fuse
+ * it; their shapes run a row-window, row-chunk or direct kernel here).
+ * Enqueued on `stream` without waiting.  Returns DWCONV_ERR_INVALID_ARG for a
+ * NULL handle, x, w, y, bn_scale or bn_shift or an unknown activation,
+ * DWCONV_ERR_UNSUPPORTED for int8 and DWCONV_ERR_HIP if the launch fails. */
+dwconv_status_t dwconv_fwd_bn_act(dwconv_handle_t h, const void *x, const void *w,
+                                  const void *bias, const float *bn_scale,
+                                  const float *bn_shift, dwconv_act_t act, void *y,
+                                  hipStream_t stream);
+
+/* 1 when dwconv_fwd_bn_act can run the handle's operation (float dtypes),
+ * else 0 (also for NULL); and a one-line description of its kernel ("" if
+ * none). */
+int dwconv_fwd_bn_act_supported(dwconv_handle_t h);
+const char *dwconv_fwd_bn_act_describe(dwconv_handle_t h);
 
 /* Backward data: the gradient with respect to the input of the forward
  * operation the handle plans ("Flash-DWC: Making Depthwise Convolution

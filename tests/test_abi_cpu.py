@@ -189,3 +189,31 @@ def test_bwd_filter_workspace_and_errors():
     finally:
         dw.dwconv_destroy(h)
         dw.dwconv_destroy(q)
+
+
+def test_fwd_bn_act_support_and_errors():
+    """The fused-prologue forward pass: supported for float plans, not int8;
+    NULL arguments and unknown activations are refused before any launch."""
+    lib = dw._lib
+    g = dw.dwconv_create(1, 8, 8, 4, 3, 3, 1, 1, 1, "f32")
+    i = dw.dwconv_create(1, 8, 8, 4, 3, 3, 1, 1, 1, "i8")
+    try:
+        assert dw.dwconv_fwd_bn_act_supported(g) and not dw.dwconv_fwd_bn_act_supported(i)
+        assert dw.dwconv_fwd_bn_act_describe(g) and dw.dwconv_fwd_bn_act_describe(i) == ""
+        fake = 1 << 40   # never dereferenced: every call below returns first
+        ok = (g, fake, fake, None, fake, fake, 1, fake, None)
+        for k in (0, 1, 2, 4, 5, 7):   # handle, x, w, bn_scale, bn_shift, y
+            args = list(ok)
+            args[k] = None
+            assert lib.dwconv_fwd_bn_act(*args) == 1, k
+        for bad in (-1, 3, 7):
+            args = list(ok)
+            args[6] = bad
+            assert lib.dwconv_fwd_bn_act(*args) == 1, bad
+        args = list(ok)
+        args[0] = i
+        assert lib.dwconv_fwd_bn_act(*args) == 2
+        assert dw.dwconv_fwd_bn_act_supported(None) is False
+    finally:
+        dw.dwconv_destroy(g)
+        dw.dwconv_destroy(i)

@@ -1,0 +1,152 @@
+"""GPU parity of the forward pass with the fused prologue act(x*s + b)
+("Flash-DWC: Making Depthwise Convolution Compute-Efficient on GPUs",
+section 5.2) through the C ABI, against the oracle's fwd_bn_act: the same
+elementwise bound as the forward pass, |y - y_exact| <= 1e-5 * scale + 1e-6
+on the value before the final rounding, scale = sum |x*s + b| * |w|."""
+import numpy as np
+import pytest
+import torch
+
+import depthwise_convolution_amd as dw
+import oracle
+from oracle import check
+import synth
+from synth import WORKLOADS, make_inputs
+
+from gpu_helpers import to_dev, y_torch_dtype, say, DEV, run, shape_of
+
+pytestmark = pytest.mark.gpu
+
+
+def bn_params(C, seed):
+    rng = np.random.default_rng(seed)
+    s = rng.uniform(0.5, 1.5, C).astype(np.float32)
+    b = rng.normal(0.0, 0.5, C).astype(np.float32)
+    return s, b
+
+
+def run_bnact(x, w, bias, s, b, act, shape, fmt, guard=256, offset=0):
+    """y on the host from dwconv_fwd_bn_act; y sits in a guarded buffer
+    (offset elements into it, to make the pointers misaligned)."""
+    N, H, W, C, FH, FW, S, D, P = shape
+    h = dw.dwconv_create(N, H, W, C, FH, FW, S, D, P, fmt)
+    try:
+        OH, OW = dw.dwconv_output_dims(h)
+        n_y = N * OH * OW * C
+        tdt = y_torch_dtype(fmt)
+        buf = torch.full((n_y + 2 * guard + offset,), float("nan"), dtype=tdt, device=DEV)
+        y = buf[guard + offset:guard + offset + n_y]
+        xd = to_dev(x, fmt)
+        if offset:
+            xs = torch.empty(xd.numel() + offset, dtype=xd.dtype, device=DEV)
+            xs[offset:].copy_(xd.reshape(-1))
+            xd = xs[offset:]
+        dw.dwconv_fwd_bn_act(h, xd, to_dev(w, fmt), None if bias is None else to_dev(bias, "f32"),
+                             torch.from_numpy(s).to(DEV), torch.from_numpy(b).to(DEV), act, y)
+        torch.cuda.synchronize()
+        host = buf.view(torch.int16).cpu().numpy().view(np.uint16) if fmt == "bf16" \
+            else buf.cpu().numpy()
+        band = np.concatenate([host[:guard + offset], host[guard + offset + n_y:]])
+        if fmt == "bf16":
+            assert np.all(band == band[0]) and band[0] & 0x7f80 == 0x7f80, "write outside y"
+        else:
+            assert np.all(np.isnan(band)), "write outside y"
+        return host[guard + offset:guard + offset + n_y].reshape(N, OH, OW, C), \
+            dw.dwconv_fwd_bn_act_describe(h)
+    finally:
+        dw.dwconv_destroy(h)
+
+
+def check_bnact(y, x, w, bias, s, b, act, shape, fmt, what):
+    N, H, W, C, FH, FW, S, D, P = shape
+    ref, scale = oracle.fwd_bn_act(x, w, bias, s, b, act, S, D, P, fmt, threads=8)
+    return check.assert_float(y, fmt, ref, scale, what)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32_3x3", "mobilenet_f32_3x3", "convnext_f16_7x7"])
+def test_workload_bn_act(name):
+    wl = WORKLOADS[name]
+    x, w, bias = make_inputs(wl)
+    shape = shape_of(wl)
+    s, b = bn_params(wl.C, 300 + wl.seed)
+    for act in ("relu", "relu6", "none"):
+        say(f"[gpu] bn+act {name} {act}")
+        y, desc = run_bnact(x, w, bias, s, b, act, shape, wl.dtype)
+        rep = check_bnact(y, x, w, bias, s, b, act, shape, wl.dtype, f"bnact {name} {act}")
+        say(f"      ok ({desc[:40]}) {rep}")
+        if name == "mobilenet_f32_3x3":
+            break  # one activation at full size is enough for the big one
+
+
+# one shape per fused family: column stream (3x3 and fp32 5x5), compiled row
+# window (strided), row chunks (9x9), direct (a channel count with no 16-byte
+# vectors)
+FAMILY_SHAPES = [((2, 30, 19, 16, 3, 3, 1, 1, 1), "colstream"),
+                 ((1, 33, 29, 8, 5, 5, 1, 1, 2), "colstream"),
+                 ((2, 33, 35, 16, 5, 5, 2, 2, 4), "rowwin"),
+                 ((1, 24, 31, 16, 9, 9, 1, 1, 4), "rowchunk"),
+                 ((2, 13, 17, 13, 3, 3, 1, 1, 1), "direct"),
+                 ((1, 20, 20, 16, 31, 31, 1, 1, 15), "rowwin")]
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_each_fused_family(fmt):
+    rng = np.random.default_rng({"f32": 301, "f16": 302, "bf16": 303}[fmt])
+    for shape, _ in FAMILY_SHAPES:
+        N, H, W, C, FH, FW, S, D, P = shape
+        wl = synth.Workload("bn", fmt, *shape, ("normal", 0.0, 1.0),
+                            ("normal", 0.0, 1.0 / (FH * FW)), ("uniform", -0.1, 0.1),
+                            int(rng.integers(0, 2**31)))
+        x, w, bias = make_inputs(wl)
+        s, b = bn_params(C, int(rng.integers(0, 2**31)))
+        act = ("none", "relu", "relu6")[int(rng.integers(0, 3))]
+        say(f"[gpu] bn+act {fmt} {shape} {act}")
+        y, desc = run_bnact(x, w, bias, s, b, act, shape, fmt)
+        check_bnact(y, x, w, bias, s, b, act, shape, fmt, f"bnact {fmt} {shape} {desc[:20]}")
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_random_small_bn_act(fmt):
+    rng = np.random.default_rng({"f32": 311, "f16": 312, "bf16": 313}[fmt])
+    for i in range(25):
+        wl = synth.random_small(rng, fmt)
+        x, w, bias = make_inputs(wl)
+        shape = shape_of(wl)
+        s, b = bn_params(wl.C, int(rng.integers(0, 2**31)))
+        act = ("none", "relu", "relu6")[i % 3]
+        say(f"[gpu] bn+act random {fmt} #{i} {shape} {act}")
+        y, desc = run_bnact(x, w, bias, s, b, act, shape, fmt, guard=64)
+        check_bnact(y, x, w, bias, s, b, act, shape, fmt, f"bnact random {fmt} #{i} {desc[:20]}")
+
+
+def test_misaligned_pointers_take_the_fallback():
+    rng = np.random.default_rng(320)
+    shape, fmt = (2, 17, 19, 32, 3, 3, 1, 1, 1), "f32"
+    wl = synth.Workload("bn", fmt, *shape, ("normal", 0.0, 1.0), ("normal", 0.0, 1 / 9),
+                        ("uniform", -0.1, 0.1), 321)
+    x, w, bias = make_inputs(wl)
+    s, b = bn_params(32, 322)
+    y, _ = run_bnact(x, w, bias, s, b, "relu", shape, fmt, offset=1)
+    check_bnact(y, x, w, bias, s, b, "relu", shape, fmt, "bnact misaligned")
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_identity_prologue_matches_plain_forward(fmt):
+    """bn_scale = 1, bn_shift = 0, no activation: x*1 + 0 is x exactly, so
+    where the fused plan is the forward plan the outputs are bit-identical."""
+    rng = np.random.default_rng(330)
+    for shape in [(2, 30, 19, 16, 3, 3, 1, 1, 1), (1, 24, 31, 16, 9, 9, 1, 1, 4)]:
+        if fmt != "f32" and shape[4] == 9:
+            continue   # fp16/bf16 9x9 runs the matrix cores unfused
+        C = shape[3]
+        wl = synth.Workload("bn", fmt, *shape, ("normal", 0.0, 1.0), ("normal", 0.0, 0.1),
+                            ("uniform", -0.1, 0.1), int(rng.integers(0, 2**31)))
+        x, w, bias = make_inputs(wl)
+        h = dw.dwconv_create(*shape, fmt)
+        same = dw.dwconv_fwd_bn_act_describe(h) == dw.dwconv_plan_describe(h)
+        dw.dwconv_destroy(h)
+        assert same, shape
+        y0, _ = run(x, w, bias, shape, fmt, "auto", guard=64)
+        y1, _ = run_bnact(x, w, bias, np.ones(C, np.float32), np.zeros(C, np.float32), "none",
+                          shape, fmt, guard=64)
+        assert np.array_equal(y0.view(np.uint8), y1.view(np.uint8)), shape
