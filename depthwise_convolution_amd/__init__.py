@@ -28,7 +28,7 @@ __all__ = [
     "VARIANTS", "DwconvError", "DepthwiseConv2d", "library_path",
     "dwconv_create", "dwconv_create_variant", "dwconv_fwd", "dwconv_destroy",
     "dwconv_output_dims", "dwconv_plan_variant", "dwconv_plan_describe",
-    "dwconv_status_string",
+    "dwconv_plan_tile", "dwconv_status_string",
 ]
 
 DWCONV_F32, DWCONV_F16, DWCONV_BF16, DWCONV_I8 = 0, 1, 2, 3
@@ -61,6 +61,8 @@ _lib.dwconv_plan_variant.argtypes = [_H]
 _lib.dwconv_plan_variant.restype = _I
 _lib.dwconv_plan_describe.argtypes = [_H]
 _lib.dwconv_plan_describe.restype = ctypes.c_char_p
+_lib.dwconv_plan_tile.argtypes = [_H, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+_lib.dwconv_plan_tile.restype = _I
 _lib.dwconv_status_string.argtypes = [_I]
 _lib.dwconv_status_string.restype = ctypes.c_char_p
 _lib.dwconv_fwd_bn_act.argtypes = [_H, _H, _H, _H, _H, _H, _I, _H, _H]
@@ -140,6 +142,16 @@ def dwconv_plan_variant(h) -> str:
 
 def dwconv_plan_describe(h) -> str:
     return _lib.dwconv_plan_describe(h).decode()
+
+
+def dwconv_plan_tile(h):
+    """(rows, columns, channels) of the output tile whose input span the
+    forward kernel fetches as one piece."""
+    th, tw, tc = _I(), _I(), _I()
+    rc = _lib.dwconv_plan_tile(h, ctypes.byref(th), ctypes.byref(tw), ctypes.byref(tc))
+    if rc != 0:
+        raise DwconvError(rc, "dwconv_plan_tile")
+    return th.value, tw.value, tc.value
 
 
 def _ptr(t):

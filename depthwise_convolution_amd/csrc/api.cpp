@@ -168,6 +168,14 @@ dwconv_variant_t dwconv_plan_variant(dwconv_handle_t h) {
 
 const char *dwconv_plan_describe(dwconv_handle_t h) { return h ? h->p.desc : ""; }
 
+dwconv_status_t dwconv_plan_tile(dwconv_handle_t h, int *tile_h, int *tile_w, int *tile_c) {
+    if (!h || !tile_h || !tile_w || !tile_c) return DWCONV_ERR_INVALID_ARG;
+    *tile_h = h->p.tile_h;
+    *tile_w = h->p.tile_w;
+    *tile_c = h->p.tile_c;
+    return DWCONV_OK;
+}
+
 const char *dwconv_status_string(dwconv_status_t s) {
     switch (s) {
         case DWCONV_OK: return "ok";

@@ -174,6 +174,7 @@ bool plan_direct(Plan &p) {
     p.grid = (uint32_t)(blocks < (1LL << 20) ? blocks : (1LL << 20));
     p.vec = 1;
     p.tm = 1;
+    p.tile_h = p.tile_w = p.tile_c = 1;
     switch (p.dtype) {
         case DT_F32: p.launch = launch_direct<F32>; p.bn_launch = launch_direct_bn<F32>; break;
         case DT_F16: p.launch = launch_direct<F16>; p.bn_launch = launch_direct_bn<F16>; break;

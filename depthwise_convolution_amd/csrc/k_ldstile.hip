@@ -460,6 +460,9 @@ static bool plan_i8tap(Plan &p) {
     p.variant = V_LDSTILE;
     p.tm = TM;
     p.th = TB;
+    p.tile_h = TB;
+    p.tile_w = 4 * TM;
+    p.tile_c = p.s.C;
     p.aux0 = nrb;
     p.aux1 = nct;
     p.aux2 = kqp;
@@ -507,6 +510,9 @@ bool plan_ldstile(Plan &p) {
     p.variant = V_LDSTILE;
     p.tm = e->tm;
     p.th = TB;
+    p.tile_h = TB;
+    p.tile_w = 4 * e->tm;
+    p.tile_c = p.s.C;
     p.aux0 = nrb;
     p.aux1 = nct;
     p.aux2 = rowb;

@@ -691,6 +691,10 @@ bool plan_mfma(Plan &p) {
     p.cs = e->cs;
     p.tm = 16;
     p.th = 16;
+    // a strip walks the whole image height; the ring loads each row once
+    p.tile_h = p.s.OH;
+    p.tile_w = 16 * e->nb;
+    p.tile_c = e->cs;
     p.aux0 = ncs;
     p.aux1 = nct;
     p.block = e->cs >= 16 ? 512 : 256;

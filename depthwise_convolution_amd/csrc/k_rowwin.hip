@@ -631,6 +631,9 @@ static bool plan_rowchunk(Plan &p) {
     p.vec = VEC;
     p.tm = TM;
     p.th = 0;
+    p.tile_h = 1;
+    p.tile_w = TM;
+    p.tile_c = VEC;
     p.block = 256;
     p.grid = (uint32_t)blocks;
     p.aux0 = ncv;
@@ -692,6 +695,9 @@ bool plan_rowwin(Plan &p) {
     p.vec = e->vec;
     p.tm = e->tm;
     p.th = e->th;
+    p.tile_h = e->th > 0 ? e->th : 1;
+    p.tile_w = e->tm;
+    p.tile_c = e->vec;
     p.block = 256;
     p.grid = (uint32_t)blocks;
     p.aux0 = ncv;

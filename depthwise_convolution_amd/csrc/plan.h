@@ -30,6 +30,10 @@ struct Plan {
     int tm;               // consecutive outputs along width per lane
     int th;               // output rows per lane / tile
     int cs;               // channels per tile
+    // the output tile whose input span the kernel fetches once (a lane's
+    // register tile, or a workgroup's LDS tile or strip): rows x columns x
+    // channels
+    int tile_h, tile_w, tile_c;
     int lds_bytes;        // dynamic LDS per workgroup
     int block;            // threads per workgroup
     uint32_t grid;        // workgroups

@@ -212,6 +212,17 @@ dwconv_status_t dwconv_output_dims(dwconv_handle_t h, int *OH, int *OW);
 dwconv_variant_t dwconv_plan_variant(dwconv_handle_t h);
 const char *dwconv_plan_describe(dwconv_handle_t h);
 
+/* The output tile of the plan's forward kernel whose input span is fetched
+ * as one piece ("Tiles, halos and partial sums", "Partition tensors to fit
+ * storage": a tile of Th x Tw outputs reads (Th-1)S + (FH-1)D + 1 by
+ * (Tw-1)S + (FW-1)D + 1 input pixels): *tile_h rows x *tile_w columns x
+ * *tile_c channels.  It is a lane's register tile (direct: 1 x 1 x 1; row
+ * window: 1 x TM x VEC; column stream: TH x TM x VEC), a workgroup's LDS
+ * tile (TB x 4TM x all C), or a matrix-core strip (all OH rows x 16NB
+ * columns x CS channels).  Host only; DWCONV_ERR_INVALID_ARG for a NULL
+ * argument. */
+dwconv_status_t dwconv_plan_tile(dwconv_handle_t h, int *tile_h, int *tile_w, int *tile_c);
+
 /* Static, human-readable name of a status. */
 const char *dwconv_status_string(dwconv_status_t s);
 

@@ -88,6 +88,35 @@ def test_output_dims_and_plan():
     dw.dwconv_destroy(None)          # no-op
 
 
+@pytest.mark.parametrize("shape,fmt,variant,tile", [
+    ((64, 56, 56, 128, 3, 3, 1, 1, 1), "f32", "auto", (14, 4, 4)),     # column stream
+    ((64, 56, 56, 96, 7, 7, 1, 1, 3), "f16", "auto", (56, 64, 8)),     # matrix-core strip
+    ((16, 112, 112, 61, 5, 5, 2, 2, 4), "i8", "auto", (7, 16, 61)),    # int8 LDS tile
+    ((2, 20, 20, 16, 5, 5, 1, 1, 2), "f32", "rowwin", (16, 4, 2)),     # column stream 5x5
+    ((2, 20, 20, 16, 7, 7, 1, 1, 3), "f16", "rowwin", (1, 4, 8)),      # row window
+    ((2, 20, 20, 16, 11, 11, 1, 1, 5), "f32", "rowwin", (1, 8, 4)),    # row chunks
+    ((2, 9, 7, 5, 4, 2, 3, 2, 1), "bf16", "direct", (1, 1, 1)),
+])
+def test_plan_tile(shape, fmt, variant, tile):
+    """The tile whose input span the forward kernel fetches as one piece,
+    as the plan's description states it."""
+    h = dw.dwconv_create_variant(*shape, fmt, variant)
+    try:
+        got = dw.dwconv_plan_tile(h)
+        desc = dw.dwconv_plan_describe(h)
+    finally:
+        dw.dwconv_destroy(h)
+    assert all(t is None or t == g for t, g in zip(tile, got)), (got, desc)
+    assert min(got) >= 1
+    if desc.startswith(("rowwin", "rowchunk", "colstream")):
+        assert f"VEC={got[2]} " in desc and f"TM={got[1]} " in desc, desc
+    with pytest.raises(dw.DwconvError):
+        lib = ctypes.CDLL(dw.library_path)
+        lib.dwconv_plan_tile.argtypes = [ctypes.c_void_p] * 4
+        rc = lib.dwconv_plan_tile(None, None, None, None)
+        raise dw.DwconvError(rc, "dwconv_plan_tile") if rc == 1 else AssertionError(rc)
+
+
 def test_forced_variants():
     # the direct family takes every shape
     h = dw.dwconv_create_variant(2, 9, 7, 5, 4, 2, 3, 2, 1, "bf16", "direct")
