@@ -304,6 +304,8 @@ def main():
                     choices=["fwd", "bwd_data", "bwd_filter", "fwd_bn_act"],
                     help="the forward pass (default), backward data or backward filter")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--warm-cache", action="store_true",
+                    help="also time K steps on one buffer set (labelled warm cache)")
     ap.add_argument("--no-copy", action="store_true",
                     help="skip the device-to-device copy ceiling measurement")
     ap.add_argument("--sweep", action="store_true",
@@ -462,17 +464,20 @@ def main():
         ev1[i].record(stream)
     torch.cuda.synchronize()
     kern_ms = np.array([a.elapsed_time(z) for a, z in zip(ev0, ev1)])
-    # pass 3, labelled warm cache: the same buffer set every step, so up to
-    # 256 MB of it can stay in the MALL (not the headline figure)
-    w0 = torch.cuda.Event(enable_timing=True)
-    w1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0.record(stream)
-    for i in range(K):
-        step(0)
-    w1.record(stream)
-    torch.cuda.synchronize()
-    warm_us = w0.elapsed_time(w1) / K * 1e3
+    # pass 3 (--warm-cache), labelled: the same buffer set every step, so up
+    # to 256 MB of it can stay in the MALL (not the headline figure)
+    warm = None
+    if args.warm_cache:
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0.record(stream)
+        for i in range(K):
+            step(0)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        warm = {"avg_us": round(w0.elapsed_time(w1) / K * 1e3, 3),
+                "note": "one buffer set reused every step; not the headline"}
     tmodel = tile_model(wl, dw.dwconv_plan_tile(h), OH, OW) if args.op == "fwd" else None
     dw.dwconv_destroy(h)
 
@@ -533,8 +538,7 @@ def main():
                        "min": round(float(kern_ms.min()) * 1e3, 3),
                        "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3)},
                    "buffer_sets": sets},
-        "warm_cache": {"avg_us": round(warm_us, 3),
-                       "note": "one buffer set reused every step; not the headline"},
+        "warm_cache": warm,
         "tile_model": tmodel,
         "copy_ceiling": copy,
         "frac_of_copy": None if copy is None else round(achieved / copy["gbs"], 4),
