@@ -30,8 +30,8 @@
 // "Tiles, halos and partial sums", with padding generated as zeros -- sits in
 // an LDS ring, channel-major, so that one 16-byte LDS read gives a lane its 8
 // consecutive columns of one channel (the A operand); each new block loads
-// only its 16 new rows.  The row pitch is padded by 8 elements, which puts the 16 rows an
-// A read touches on distinct banks.  The filter slice is staged once as
+// only its 16 new rows.  The row pitch is 16 (mod 32) elements, which puts the 16 rows
+// an A read touches on distinct banks.  The filter slice is staged once as
 // padded fragments -- 16 zeros, the fragment's 16 taps, 16 zeros -- so that
 // a lane's 8 entries of B, B[k][t] = tap k - t, are 8 consecutive elements at
 // a fixed per-lane offset, with the band's zeros built in; the lane reads
@@ -78,7 +78,11 @@ struct MfmaOp<BF16> {
 template <int CS, int NB, int NFRAG>
 struct MfmaTile {
     static constexpr int XW = 16 * (NB + NFRAG);  // staged input columns
-    static constexpr int PITCH = XW + 8;          // elements per staged row
+    // elements per staged row: 16 (mod 32), i.e. 8 (mod 16) dwords, for
+    // which the 16-byte A reads of 16 rows count no LDS bank conflicts
+    // (measured on gfx950; 4 (mod 16) dwords counts one conflict cycle per
+    // read, 0 (mod 16) several)
+    static constexpr int PITCH = XW % 32 == 16 ? XW : XW + 16;
     static constexpr int ZLEN = 48;               // padded fragment length
     static constexpr int NW = CS >= 16 ? 8 : 4;       // wavefronts per workgroup
     static constexpr int NT = 64 * NW;                 // threads per workgroup
