@@ -264,34 +264,34 @@ k_i8tap(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 
     // ---- stage 2: channel-major transpose of the tap columns: dword kd of
     // (row rr, channel c) packs tap columns 4kd .. 4kd+3 (tile columns
-    // D*k); zeros outside the image.  The (row, dword) items are shared out
-    // over the wavefronts; lane = channel, so every byte read is one of 64
-    // consecutive bytes. ----
+    // D*k); zeros outside the image.  Rows are shared out over the
+    // wavefronts; lane = channel, so every byte read is one of 64 consecutive
+    // bytes.  All KQ byte reads of a row are issued before any is used (reads
+    // outside the image go to byte c of the first staged row and are masked)
+    // so that their LDS latency is paid once per row. ----
     {
-        const int kqd = (KQ + 3) / 4;
-        const int items = RB * kqd;
-        for (int it = wave; it < items; it += 4) {
-            const int rr = it / kqd, kd = it % kqd;
+        constexpr int KQD = (KQ + 3) / 4;
+        const int DC = D * s.C;
+        for (int rr = wave; rr < RB; rr += 4) {
             const int ih = ih0 + D * rr;
             const bool rok = (unsigned)ih < (unsigned)s.H;
             const int base = rok ? rr * rowb + flat_row_base<1>(s, n, ih, iw0) : 0;
-            bool cok[4];
-            int off[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int k = 4 * kd + j;
-                const int iw = iw0 + D * k;
-                cok[j] = rok && k < KQ && (unsigned)iw < (unsigned)s.W;
-                off[j] = base + D * k * s.C;
-            }
             for (int g = 0; g < ngrp; ++g) {
                 const int c = 64 * g + lane;
                 if (c >= s.C) break;
-                uint32_t v = 0;
+                uint32_t b8[4 * KQD];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (cok[j]) v |= (uint32_t)flat[off[j] + c] << (8 * j);
-                *reinterpret_cast<uint32_t *>(cm + ((long long)rr * s.C + c) * kqp + 4 * kd) = v;
+                for (int k = 0; k < 4 * KQD; ++k) {
+                    const int iw = iw0 + D * k;
+                    const bool ok = rok && k < KQ && (unsigned)iw < (unsigned)s.W;
+                    const uint32_t v = flat[ok ? base + k * DC + c : c];
+                    b8[k] = ok ? v : 0u;
+                }
+#pragma unroll
+                for (int kd = 0; kd < KQD; ++kd)
+                    *reinterpret_cast<uint32_t *>(cm + ((long long)rr * s.C + c) * kqp + 4 * kd) =
+                        b8[4 * kd] | (b8[4 * kd + 1] << 8) | (b8[4 * kd + 2] << 16) |
+                        (b8[4 * kd + 3] << 24);
             }
         }
     }
