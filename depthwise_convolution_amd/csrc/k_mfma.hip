@@ -654,6 +654,16 @@ static const MfmaEntry kMfma[] = {
     // filters of 33 to 64 taps: 32-column strips, one workgroup per CU
     MF(DT_F16, F16, 4, 2, 3, 0, 0),    MF(DT_F16, F16, 4, 2, 4, 0, 0),
     MF(DT_BF16, BF16, 4, 2, 3, 0, 0),  MF(DT_BF16, BF16, 4, 2, 4, 0, 0),
+    // 32-column strips for outputs whose width 64-column strips would pad
+    // more (OW = 32: half of a 64-column strip would be padding)
+    MFA(DT_F16, F16, 8, 2, 1, 8, 7, true),   MFA(DT_BF16, BF16, 8, 2, 1, 8, 7, true),
+    MFA(DT_F16, F16, 4, 2, 2, 0, 31, true),  MFA(DT_BF16, BF16, 4, 2, 2, 0, 31, true),
+    MF(DT_F16, F16, 8, 2, 1, 8, 0),    MF(DT_F16, F16, 8, 2, 1, 0, 0),
+    MF(DT_F16, F16, 8, 2, 2, 0, 0),    MF(DT_F16, F16, 4, 2, 1, 0, 0),
+    MF(DT_F16, F16, 4, 2, 2, 0, 0),
+    MF(DT_BF16, BF16, 8, 2, 1, 8, 0),  MF(DT_BF16, BF16, 8, 2, 1, 0, 0),
+    MF(DT_BF16, BF16, 8, 2, 2, 0, 0),  MF(DT_BF16, BF16, 4, 2, 1, 0, 0),
+    MF(DT_BF16, BF16, 4, 2, 2, 0, 0),
 };
 #undef MF
 #undef MFA
@@ -663,27 +673,37 @@ bool plan_mfma(Plan &p) {
     if (p.s.S != 1 || p.s.D != 1) return false;
     const int nfrag = (p.s.FW + 15) / 16;
     // DWCONV_MFMA_CS=4|8|16 picks the channel slice (a tuning hook)
-    int want_cs = 0, want_al = -1;
+    int want_cs = 0, want_al = -1, want_nb = 0;
     if (const char *env = getenv("DWCONV_MFMA_CS")) want_cs = atoi(env);
     // DWCONV_MFMA_AL=0|1: A windows by DPP row shift / from LDS for every lane
     if (const char *env = getenv("DWCONV_MFMA_AL")) want_al = atoi(env);
+    // DWCONV_MFMA_NB=2|4: strips of 32 / 64 output columns
+    if (const char *env = getenv("DWCONV_MFMA_NB")) want_nb = atoi(env);
+    // strips of 64 columns unless 32-column strips cover the output width
+    // with fewer padded columns; the other width if nothing fits
+    const int pad4 = (p.s.OW + 63) / 64 * 64, pad2 = (p.s.OW + 31) / 32 * 32;
+    const int nb_pref = want_nb ? want_nb : pad2 < pad4 ? 2 : 4;
     const MfmaEntry *e = nullptr;
     int lds = 0;
-    for (const auto &k : kMfma) {
-        if (k.dtype != p.dtype || k.nfrag != nfrag || p.s.C % k.cs != 0) continue;
-        if (k.fhk && p.s.FH > k.fhk) continue;
-        if (k.fht && p.s.FH != k.fht) continue;
-        if (want_cs && k.cs != want_cs) continue;
-        if (want_al >= 0 && k.al != want_al) continue;
-        const int need = k.lds(p.s);
-        // 16-channel slices run one 8-wavefront workgroup per CU; narrower
-        // ones aim for at least two per CU unless nothing else fits
-        const bool last = k.cs == 4 || want_cs;
-        const int cap = k.cs == 16 || last ? 160 * 1024 : 64 * 1024;
-        if (need <= cap) {
-            e = &k;
-            lds = need;
-            break;
+    for (int pass = 0; pass < 2 && !e; ++pass) {
+        for (const auto &k : kMfma) {
+            if ((pass == 0) != (k.nb == nb_pref)) continue;
+            if (want_nb && k.nb != want_nb) continue;
+            if (k.dtype != p.dtype || k.nfrag != nfrag || p.s.C % k.cs != 0) continue;
+            if (k.fhk && p.s.FH > k.fhk) continue;
+            if (k.fht && p.s.FH != k.fht) continue;
+            if (want_cs && k.cs != want_cs) continue;
+            if (want_al >= 0 && k.al != want_al) continue;
+            const int need = k.lds(p.s);
+            // 16-channel slices run one 8-wavefront workgroup per CU; narrower
+            // ones aim for at least two per CU unless nothing else fits
+            const bool last = k.cs == 4 || want_cs;
+            const int cap = k.cs == 16 || last ? 160 * 1024 : 64 * 1024;
+            if (need <= cap) {
+                e = &k;
+                lds = need;
+                break;
+            }
         }
     }
     if (!e) return false;  // tall filters: the tile does not fit LDS

@@ -369,6 +369,31 @@ def test_each_mfma_channel_slice(cs, al, monkeypatch):
             assert_matches_oracle(y, x, w, b, shape, fmt, f"mfma cs{cs} {shape}")
 
 
+@pytest.mark.parametrize("nb", [2, 4])
+def test_mfma_strip_widths(nb, monkeypatch):
+    """Strips of 32 and 64 output columns (forced through DWCONV_MFMA_NB)
+    for the compiled 7x7 and 31x31 entries and runtime filter heights with
+    one and two fragments, against the oracle; widths that leave a ragged
+    last strip and an output narrower than one strip."""
+    monkeypatch.setenv("DWCONV_MFMA_NB", str(nb))
+    rng = np.random.default_rng(60 + nb)
+    for fmt, F in [("f16", 7), ("bf16", 31), ("bf16", 5), ("f16", 17)]:
+        for (N, H, W, C) in [(1, 20, 45, 16), (2, 17, 13, 8)]:
+            shape = (N, H, W, C, F, F, 1, 1, F // 2)
+            wl = synth.Workload("mfma", fmt, *shape, ("normal", 0.0, 1.0),
+                                ("normal", 0.0, 1.0 / F), ("uniform", -0.1, 0.1),
+                                int(rng.integers(0, 2**31)))
+            x, w, b = make_inputs(wl)
+            h = dw.dwconv_create_variant(*shape, fmt, "mfma")
+            desc = dw.dwconv_plan_describe(h)
+            dw.dwconv_destroy(h)
+            assert f"strips of {16 * nb} cols" in desc, desc
+            say(f"[gpu] mfma strips of {16 * nb} columns, {fmt} shape {shape}")
+            y, used = run(x, w, b, shape, fmt, "mfma", guard=512)
+            assert used == "mfma", used
+            assert_matches_oracle(y, x, w, b, shape, fmt, f"mfma nb{nb} {shape}")
+
+
 # --------------------------------------------- tensors at the size limit
 
 # just under 2^31 elements (the largest tensors a plan accepts): per-image
