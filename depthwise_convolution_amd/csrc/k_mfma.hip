@@ -679,10 +679,13 @@ bool plan_mfma(Plan &p) {
     if (const char *env = getenv("DWCONV_MFMA_AL")) want_al = atoi(env);
     // DWCONV_MFMA_NB=2|4: strips of 32 / 64 output columns
     if (const char *env = getenv("DWCONV_MFMA_NB")) want_nb = atoi(env);
-    // strips of 64 columns unless 32-column strips cover the output width
-    // with fewer padded columns; the other width if nothing fits
+    // the strip width that pads fewer output columns; on a tie 32-column
+    // strips for one fragment and at least 7 filter rows (measured: 7x7 up to
+    // 5 % and 13x13 up to 40 % faster, 9x9 equal, 5x5 and two or more
+    // fragments slower), else 64; the other width if nothing fits
     const int pad4 = (p.s.OW + 63) / 64 * 64, pad2 = (p.s.OW + 31) / 32 * 32;
-    const int nb_pref = want_nb ? want_nb : pad2 < pad4 ? 2 : 4;
+    const bool tie2 = nfrag == 1 && p.s.FH >= 7;
+    const int nb_pref = want_nb ? want_nb : pad2 < pad4 || (pad2 == pad4 && tie2) ? 2 : 4;
     const MfmaEntry *e = nullptr;
     int lds = 0;
     for (int pass = 0; pass < 2 && !e; ++pass) {

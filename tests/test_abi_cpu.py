@@ -90,7 +90,7 @@ def test_output_dims_and_plan():
 
 @pytest.mark.parametrize("shape,fmt,variant,tile", [
     ((64, 56, 56, 128, 3, 3, 1, 1, 1), "f32", "auto", (14, 4, 4)),     # column stream
-    ((64, 56, 56, 96, 7, 7, 1, 1, 3), "f16", "auto", (56, 64, 8)),     # matrix-core strip
+    ((64, 56, 56, 96, 7, 7, 1, 1, 3), "f16", "auto", (56, 32, 8)),     # matrix-core strip
     ((16, 112, 112, 61, 5, 5, 2, 2, 4), "i8", "auto", (7, 16, 61)),    # int8 LDS tile
     ((2, 20, 20, 16, 5, 5, 1, 1, 2), "f32", "rowwin", (16, 4, 2)),     # column stream 5x5
     ((2, 20, 20, 16, 7, 7, 1, 1, 3), "f16", "rowwin", (1, 4, 8)),      # row window
