@@ -345,3 +345,39 @@ def test_bwd_filter_column_stream(monkeypatch):
         dwv, desc = run_bwf(x, dy, shape, "f32")
         assert desc.startswith("bwf:"), desc
         check_bwf(dwv, x, dy, shape, "f32", f"bwf vec {shape}")
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16"])
+def test_module_wrapper_all_passes(fmt):
+    """DepthwiseConv2d (the Python wrapper over one plan) runs the forward
+    pass, the fused prologue, the input gradient and the filter gradient,
+    each against the oracle."""
+    shape = (2, 14, 19, 16, 5, 5, 1, 1, 2)
+    N, H, W, C, FH, FW, S, D, P = shape
+    rng = np.random.default_rng({"f32": 71, "bf16": 72}[fmt])
+    x = synth.to_storage(rng.standard_normal((N, H, W, C)), fmt)
+    w = synth.to_storage(rng.normal(0.0, 0.2, (FH, FW, C)), fmt)
+    b = synth.to_storage(rng.uniform(-0.1, 0.1, C), "f32")
+    s = rng.uniform(0.5, 1.5, C).astype(np.float32)
+    t = rng.normal(0.0, 0.5, C).astype(np.float32)
+    conv = dw.DepthwiseConv2d(*shape, dtype=fmt)
+    try:
+        xd, wd, bd = to_dev(x, fmt), to_dev(w, fmt), to_dev(b, "f32")
+        y = conv(xd, wd, bd)
+        y2 = conv.forward_bn_act(xd, wd, torch.from_numpy(s).to(DEV),
+                                 torch.from_numpy(t).to(DEV), act="relu6", bias=bd)
+        dy, _ = grads(shape, fmt, 73)
+        dyd = to_dev(dy, fmt)
+        dx = conv.backward_data(dyd, wd)
+        dW = conv.backward_filter(xd, dyd)
+        torch.cuda.synchronize()
+        host = {k: (v.view(torch.int16).cpu().numpy().view(np.uint16) if v.dtype == torch.bfloat16
+                    else v.cpu().numpy()) for k, v in dict(y=y, y2=y2, dx=dx).items()}
+    finally:
+        conv.close()
+    ref, scale = oracle.fwd(x, w, b, S, D, P, fmt, threads=8)
+    check.assert_float(host["y"], fmt, ref, scale, f"module fwd {fmt}")
+    ref, scale = oracle.fwd_bn_act(x, w, b, s, t, "relu6", S, D, P, fmt, threads=8)
+    check.assert_float(host["y2"], fmt, ref, scale, f"module fwd_bn_act {fmt}")
+    check_bwd(host["dx"], dy, w, shape, fmt, f"module bwd_data {fmt}")
+    check_bwf(dW.cpu().numpy(), x, dy, shape, fmt, f"module bwd_filter {fmt}")
