@@ -236,24 +236,26 @@ REG_TILES = {
 }
 
 
-def test_column_stream_5x5():
-    """The fp32 5x5 column stream (two channels per lane): ragged row strips
-    and column groups, an image shorter than a strip, odd channel-vector
-    counts, padding 0 to 4, against the oracle."""
-    rng = np.random.default_rng(86)
-    for shape in [(2, 30, 19, 16, 5, 5, 1, 1, 2), (1, 5, 57, 8, 5, 5, 1, 1, 2),
-                  (1, 33, 16, 6, 5, 5, 1, 1, 0), (1, 17, 17, 10, 5, 5, 1, 1, 4),
-                  (3, 40, 41, 2, 5, 5, 1, 1, 1)]:
-        wl = synth.Workload("cs5", "f32", *shape, ("normal", 0.0, 1.0), ("normal", 0.0, 1 / 25),
-                            ("uniform", -0.1, 0.1), int(rng.integers(0, 2**31)))
+@pytest.mark.parametrize("F", [5, 7])
+def test_column_stream_wide_filters(F):
+    """The fp32 5x5 and 7x7 column streams (two channels per lane): ragged
+    row strips and column groups, an image shorter than a strip, odd
+    channel-vector counts, padding from 0 to F - 1, against the oracle."""
+    rng = np.random.default_rng(86 + F)
+    for shape in [(2, 30, 19, 16, F, F, 1, 1, F // 2), (1, 5, 57, 8, F, F, 1, 1, F // 2),
+                  (1, 33, 16, 6, F, F, 1, 1, 0), (1, 17, 17, 10, F, F, 1, 1, F - 1),
+                  (3, 40, 41, 2, F, F, 1, 1, 1)]:
+        wl = synth.Workload("csw", "f32", *shape, ("normal", 0.0, 1.0),
+                            ("normal", 0.0, 1 / F**2), ("uniform", -0.1, 0.1),
+                            int(rng.integers(0, 2**31)))
         x, w, b = make_inputs(wl)
         h = dw.dwconv_create(*shape, "f32")
         desc = dw.dwconv_plan_describe(h)
         dw.dwconv_destroy(h)
-        assert desc.startswith("colstream"), desc
-        say(f"[gpu] column stream 5x5 {shape}")
+        assert desc.startswith("colstream") and f"{F}x{F}" in desc, desc
+        say(f"[gpu] column stream {F}x{F} {shape}")
         y, used = run(x, w, b, shape, "f32", "auto", guard=512)
-        assert_matches_oracle(y, x, w, b, shape, "f32", f"cs5 {shape}")
+        assert_matches_oracle(y, x, w, b, shape, "f32", f"cs{F} {shape}")
 
 
 @pytest.mark.parametrize("fmt", sorted(REG_TILES))
