@@ -587,9 +587,13 @@ static const RegTile kTiles[] = {
     // 5x5: two channels per lane keep the 5 x 5 filter and 5 rows of
     // accumulators in registers (measured 18-32 % faster than the row window)
     CS(DT_F32, F32, 5, 5, 1, 2, 4, 16, 2, 1, 0),
-    // 7x7 the same way (256 registers; measured 26-28 against 20 TFLOP/s for
-    // the row window on the 128-image maps)
-    CS(DT_F32, F32, 7, 7, 1, 2, 4, 16, 2, 1, 0),
+    // 7x7 and 9x9 with one channel per lane, four columns and 16 rows (202
+    // and 256 registers; measured 36-38 and 31 TFLOP/s on the 128-image maps
+    // against 26 for two channels per lane at 7x7, 20 for the 7x7 row window
+    // and 22 for 9x9 row chunks; 11x11 and 13x13 were no faster than row
+    // chunks)
+    CS(DT_F32, F32, 7, 7, 1, 1, 4, 16, 2, 1, 0),
+    CS(DT_F32, F32, 9, 9, 1, 1, 4, 16, 2, 1, 0),
     CS(DT_F32, F32, 3, 3, 1, 4, 2, 28, 2, 1, 0),
     CS(DT_F32, F32, 3, 3, 1, 4, 4, 8, 2, 1, 0),
     CS(DT_F16, F16, 3, 3, 1, 8, 2, 14, 2, 1, 0),

@@ -236,9 +236,10 @@ REG_TILES = {
 }
 
 
-@pytest.mark.parametrize("F", [5, 7])
+@pytest.mark.parametrize("F", [5, 7, 9])
 def test_column_stream_wide_filters(F):
-    """The fp32 5x5 and 7x7 column streams (two channels per lane): ragged
+    """The fp32 5x5 (two channels per lane), 7x7 and 9x9 (one) column
+    streams: ragged
     row strips and column groups, an image shorter than a strip, odd
     channel-vector counts, padding from 0 to F - 1, against the oracle."""
     rng = np.random.default_rng(86 + F)
