@@ -231,8 +231,8 @@ def test_repeat_runs_bitwise_identical_and_stream():
 
 REG_TILES = {
     "f32": ["4x14p2ni", "4x14p2n", "2x28p2n", "4x8p2n"],
-    "f16": ["2x14p2n"],
-    "bf16": ["2x14p2n"],
+    "f16": ["4x14p2n", "2x14p2n"],
+    "bf16": ["4x14p2n", "2x14p2n"],
 }
 
 
