@@ -112,6 +112,13 @@ EDGE = [
     (1, 30, 30, 32, 3, 3, 2, 1, 1),
     (1, 8, 8, 16, 3, 3, 1, 1, 6),         # padding wider than the filter
     (3, 14, 14, 48, 5, 5, 1, 1, 2),
+    (1, 9, 11, 16, 1, 1, 1, 1, 0),        # 1x1 filter
+    (2, 12, 13, 8, 1, 7, 1, 1, 3),        # 1x7: the first and last 3 output rows see padding only
+    (1, 13, 10, 24, 7, 1, 1, 1, 0),       # 7x1
+    (1, 10, 10, 1, 3, 3, 1, 1, 1),        # one channel
+    (1, 2, 2, 8, 3, 3, 1, 1, 2),          # outputs whose taps are all padding
+    (1, 5, 6, 8, 3, 3, 1, 3, 3),          # dilation wider than the image
+    (1, 7, 7, 16, 3, 3, 3, 1, 0),         # stride equal to the filter
 ]
 
 
