@@ -94,7 +94,7 @@ def test_output_dims_and_plan():
     ((16, 112, 112, 61, 5, 5, 2, 2, 4), "i8", "auto", (7, 16, 61)),    # int8 LDS tile
     ((2, 20, 20, 16, 5, 5, 1, 1, 2), "f32", "rowwin", (16, 4, 2)),     # column stream 5x5
     ((2, 20, 20, 16, 7, 7, 1, 1, 3), "f16", "rowwin", (1, 4, 8)),      # row window
-    ((2, 20, 20, 16, 11, 11, 1, 1, 5), "f32", "rowwin", (1, 8, 4)),    # row chunks
+    ((2, 20, 20, 16, 11, 11, 1, 1, 5), "f32", "rowwin", (1, 12, 4)),   # row chunks
     ((2, 9, 7, 5, 4, 2, 3, 2, 1), "bf16", "direct", (1, 1, 1)),
 ])
 def test_plan_tile(shape, fmt, variant, tile):

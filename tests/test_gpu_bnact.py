@@ -79,13 +79,13 @@ def test_workload_bn_act(name):
 
 
 # one shape per fused family: column stream (3x3, fp32 5x5 and 7x7), compiled row
-# window (strided), row chunks (9x9), direct (a channel count with no 16-byte
+# window (strided), row chunks (11x11), direct (a channel count with no 16-byte
 # vectors)
 FAMILY_SHAPES = [((2, 30, 19, 16, 3, 3, 1, 1, 1), "colstream"),
                  ((1, 33, 29, 8, 5, 5, 1, 1, 2), "colstream"),
                  ((1, 26, 23, 8, 7, 7, 1, 1, 3), "colstream"),
                  ((2, 33, 35, 16, 5, 5, 2, 2, 4), "rowwin"),
-                 ((1, 24, 31, 16, 9, 9, 1, 1, 4), "rowchunk"),
+                 ((1, 24, 31, 16, 11, 11, 1, 1, 5), "rowchunk"),
                  ((2, 13, 17, 13, 3, 3, 1, 1, 1), "direct"),
                  ((1, 20, 20, 16, 31, 31, 1, 1, 15), "rowwin")]
 

@@ -492,13 +492,16 @@ def test_size_limit_sampled(case):
 
 # ------------------------------------------- filters of any size (row chunks)
 
-@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
-def test_row_chunks_any_filter(fmt):
+@pytest.mark.parametrize("fmt", ["f32", "f32-tm8", "f16", "bf16"])
+def test_row_chunks_any_filter(fmt, monkeypatch):
     """The row-chunk kernel (stride 1, dilation 1, any filter the compiled
     tilings do not cover): chunk-boundary widths (8, 9, 15, 16, 17), tall
     and flat filters, padding below, at and past half the filter, ragged
     widths, against the whole-tensor oracle."""
-    rng = np.random.default_rng({"f32": 81, "f16": 82, "bf16": 83}[fmt])
+    rng = np.random.default_rng({"f32": 81, "f32-tm8": 84, "f16": 82, "bf16": 83}[fmt])
+    if fmt == "f32-tm8":  # the 8-wide fp32 tiling (DWCONV_CHUNK_TM tuning hook)
+        monkeypatch.setenv("DWCONV_CHUNK_TM", "8")
+        fmt = "f32"
     vec = 4 if fmt == "f32" else 8
     cases = [(2, 23, 37, 2 * vec, 9, 9, 4), (1, 20, 41, vec, 8, 8, 3), (1, 17, 30, 3 * vec, 15, 16, 7),
              (1, 33, 35, vec, 17, 17, 8), (1, 12, 51, vec, 1, 33, 16), (1, 40, 20, 2 * vec, 33, 2, 1),
