@@ -28,9 +28,11 @@
 // Workgroup (4 wavefronts): one image, CS channels (CS / 4 per wavefront) and
 // a chunk of output rows, walked 16 rows at a time.  The padded input rows a
 // block needs sit in an LDS ring, channel-major, as in the forward kernel:
-// A lane's row advances by one per output row, so the A operands of row
-// oh + 1 are those of row oh moved down one lane (DPP row_shl:1) and only
-// lane 15 of each row group reads its new row.  The block's 16 gradient rows
+// a lane's row advances by one per output row, and every lane reads its A
+// windows of each output row from the ring (measured 5-8 % faster than
+// moving row oh's operands down one lane with a DPP row shift and reading
+// only the new row); the row pitch of 16 (mod 32) elements puts the 16 rows
+// of an A read on distinct LDS banks.  The block's 16 gradient rows
 // sit in LDS too, with 16 zero columns in front, and a lane's 8 entries of
 // B are 8 consecutive elements at a fixed per-lane offset, read as five
 // dwords and a funnel shift.  The next block's input and gradient rows are
@@ -80,7 +82,7 @@ template <int CS, int NI, int NT, int WN>
 struct BwfTile {
     static constexpr int XR = 16 * NI + 15;             // ring rows
     static constexpr int XW = 16 * (NT - 1) + 32 * WN;  // ring columns (padded input)
-    static constexpr int PITCH = XW + 8;                // the 16 rows of an A read on distinct banks
+    static constexpr int PITCH = XW % 32 == 16 ? XW : XW + 16;  // see the header
     static constexpr int GW = 32 * WN;                  // gradient columns per row
     static constexpr int GPITCH = GW + 24;              // 16 zero columns in front, slack behind
     static constexpr int ELEMS = CS * XR * PITCH + CS * 16 * GPITCH;
@@ -270,28 +272,6 @@ k_bwf_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dy,
                             *reinterpret_cast<const bf_u32x4 *>(xr + 16 * tt + 32 * m);
             }
     };
-    auto next_a = [&](Ops &o, const Ops &p, int L) {
-#pragma unroll
-        for (int ci = 0; ci < NCH; ++ci)
-#pragma unroll
-            for (int I = 0; I < NI; ++I) {
-#pragma unroll
-                for (int w = 0; w < NWIN; ++w)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        o.A[ci][I][w][q] = __builtin_amdgcn_update_dpp(
-                            0, (int)p.A[ci][I][w][q], 0x101, 0xf, 0xf, true);
-                if (t16 == 15) {
-                    const uint16_t *xr = xc[ci] + ((L + 16 * I + 15) % XR) * PITCH;
-#pragma unroll
-                    for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                        for (int m = 0; m < WN; ++m)
-                            o.A[ci][I][tt * WN + m] =
-                                *reinterpret_cast<const bf_u32x4 *>(xr + 16 * tt + 32 * m);
-                }
-            }
-    };
     auto load_b = [&](Ops &o, int srow) {
 #pragma unroll
         for (int ci = 0; ci < NCH; ++ci)
@@ -353,7 +333,7 @@ k_bwf_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dy,
         for (int st = 0; st < 16; ++st) {
             if (st < nst) {  // rows past the chunk's last are skipped (uniform)
                 if (st + 1 < 16) {
-                    next_a(o[(st + 1) & 1], o[st & 1], 16 * blk + st + 1);
+                    full_a(o[(st + 1) & 1], 16 * blk + st + 1);
                     load_b(o[(st + 1) & 1], st + 1);
                 }
                 mfmas(o[st & 1]);
