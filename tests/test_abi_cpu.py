@@ -246,3 +246,42 @@ def test_fwd_bn_act_support_and_errors():
     finally:
         dw.dwconv_destroy(g)
         dw.dwconv_destroy(i)
+
+
+def test_plans_from_many_host_threads():
+    """Plans are host-side and immutable: creating, describing and
+    destroying them from several threads at once gives each thread the same
+    answers as a single thread."""
+    import threading
+    shapes = [((64, 56, 56, 128, 3, 3, 1, 1, 1), "f32"), ((64, 56, 56, 96, 7, 7, 1, 1, 3), "f16"),
+              ((32, 56, 56, 128, 31, 31, 1, 1, 15), "bf16"), ((16, 112, 112, 61, 5, 5, 2, 2, 4), "i8"),
+              ((2, 9, 7, 5, 4, 2, 3, 2, 1), "bf16")]
+
+    def describe(shape, fmt):
+        h = dw.dwconv_create(*shape, fmt)
+        try:
+            return (dw.dwconv_plan_describe(h), dw.dwconv_plan_tile(h), dw.dwconv_output_dims(h),
+                    dw.dwconv_bwd_data_describe(h), dw.dwconv_bwd_filter_describe(h),
+                    dw.dwconv_fwd_bn_act_describe(h))
+        finally:
+            dw.dwconv_destroy(h)
+
+    want = [describe(*c) for c in shapes]
+    errors = []
+
+    def worker(k):
+        try:
+            for r in range(50):
+                i = (k + r) % len(shapes)
+                got = describe(*shapes[i])
+                if got != want[i]:
+                    errors.append((k, r, got, want[i]))
+        except Exception as e:  # noqa: BLE001 -- reported below
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
