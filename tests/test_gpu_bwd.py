@@ -381,3 +381,34 @@ def test_module_wrapper_all_passes(fmt):
     check.assert_float(host["y2"], fmt, ref, scale, f"module fwd_bn_act {fmt}")
     check_bwd(host["dx"], dy, w, shape, fmt, f"module bwd_data {fmt}")
     check_bwf(dW.cpu().numpy(), x, dy, shape, fmt, f"module bwd_filter {fmt}")
+
+
+def test_one_plan_on_two_streams_at_once():
+    """One handle used on two streams concurrently (the forward pass and the
+    filter gradient, each stream with its own buffers and workspace): every
+    result equals the same call made alone on the default stream."""
+    shape = (4, 30, 29, 32, 7, 7, 1, 1, 3)
+    N, H, W, C, FH, FW, S, D, P = shape
+    rng = np.random.default_rng(91)
+    xs = [synth.to_storage(rng.standard_normal((N, H, W, C)), "f16") for _ in range(2)]
+    w = synth.to_storage(rng.normal(0.0, 1 / 7, (FH, FW, C)), "f16")
+    conv = dw.DepthwiseConv2d(*shape, dtype="f16")
+    try:
+        xd = [to_dev(x, "f16") for x in xs]
+        wd = to_dev(w, "f16")
+        ref_y = [conv(x, wd) for x in xd]
+        ref_dw = [conv.backward_filter(x, y) for x, y in zip(xd, ref_y)]
+        torch.cuda.synchronize()
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        out_y, out_dw = [None, None], [None, None]
+        for rep in range(3):
+            for k, st in enumerate(streams):
+                with torch.cuda.stream(st):
+                    out_y[k] = conv(xd[k], wd, stream=st)
+                    out_dw[k] = conv.backward_filter(xd[k], out_y[k], stream=st)
+            torch.cuda.synchronize()
+            for k in range(2):
+                assert torch.equal(out_y[k].view(torch.int16), ref_y[k].view(torch.int16)), (rep, k)
+                assert torch.equal(out_dw[k], ref_dw[k]), (rep, k)
+    finally:
+        conv.close()
