@@ -104,10 +104,19 @@ struct MfmaTile {
 // FHK > 0: filters of at most FHK rows and one fragment keep every B operand
 // of the wavefront's channels in registers for the whole strip.
 // AL: every lane reads its A windows of each filter row from LDS (no DPP)
-template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL = false>
+// NS > 1: the fused prologue.  Each input value x becomes
+// U = act(x * bn_scale[c] + bn_shift[c]) in fp32 as the ring is written
+// (padding stays zero), and U is held as NS parts of the input format,
+// U = U_0 + U_1 (+ U_2), each the rounded remainder of the ones before: two
+// fp16 parts keep 22 of U's bits, three bf16 parts 24.  Each A window is
+// multiplied by the same B once per part, so the sum is that of U * w to
+// fp32 precision.  The chain is folded into an fp32 total every FP filter
+// rows (at most 64 MFMAs per chain).
+template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL = false, int NS = 1>
 __global__ void __launch_bounds__(CS >= 16 ? 512 : 256, 2)  // at most 256 registers
 k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-       const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int ncs, int nct) {
+       const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int ncs, int nct,
+       const float *__restrict__ bns, const float *__restrict__ bnb, int act) {
     using T = MfmaTile<CS, NB, NFRAG>;
     constexpr int XW = T::XW, PITCH = T::PITCH, ZLEN = T::ZLEN;
     constexpr int NW = T::NW, NT = T::NT;
@@ -116,6 +125,8 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     constexpr int NWIN = NB + NFRAG - 1;    // distinct A windows per filter row
     static_assert(FHK == 0 || NFRAG == 1, "kept B operands: one fragment");
     static_assert(FHT == 0 || FHK == 0 || FHT <= FHK, "kept B operands cover the filter");
+    static_assert(NS == 1 || (AL && FHT == 0 && NFRAG <= 2 && NS <= 3),
+                  "the fused prologue: LDS-read A windows, runtime filter height");
     // FHT > 0: the filter height is a compile-time constant and the
     // filter-row loop is fully unrolled, so the accumulators keep fixed
     // registers (a runtime loop made the compiler rotate them)
@@ -123,8 +134,9 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
 
     const int FH = FHT > 0 ? FHT : s.FH;            // filter height
     const int XR = 16 + FH - 1;                     // ring rows
-    uint16_t *xt = lds;                             // [CS][XR][PITCH]
-    uint16_t *zt = xt + CS * XR * PITCH;            // [CS][FH][NFRAG][ZLEN]
+    const int RING = CS * XR * PITCH;               // elements of one ring
+    uint16_t *xt = lds;                             // [NS][CS][XR][PITCH]
+    uint16_t *zt = xt + NS * RING;                  // [CS][FH][NFRAG][ZLEN]
     uint16_t *ot = zt + CS * FH * NFRAG * ZLEN;     // [16][16*NB][CS]
 
     // workgroup -> (image, column strip, channel slice); channel slices vary
@@ -178,6 +190,15 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     };
     // channel-major scatter into the ring, one dword (two columns) per
     // channel: padded row R lives in slot R mod XR
+    // the fused prologue's per-channel scale and shift of the slice's channels
+    float bnsc[NS > 1 ? CS : 1], bnsh[NS > 1 ? CS : 1];
+    if constexpr (NS > 1) {
+#pragma unroll
+        for (int c = 0; c < CS; ++c) {
+            bnsc[c] = bns[c0 + c];
+            bnsh[c] = bnb[c0 + c];
+        }
+    }
     auto scatter = [&](const PixV(&v)[NEWP][2], int R0, int rlimit) {
         const int r0m = R0 % XR;
 #pragma unroll
@@ -186,13 +207,43 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
             int slot = r0m + crow[u];
             slot -= slot >= XR ? XR : 0;
             uint16_t *dst = xt + slot * PITCH + ccol[u];
+            if constexpr (NS == 1) {
 #pragma unroll
-            for (int k = 0; k < CS / 2; ++k) {
-                const uint32_t a = v[u][0][k], b = v[u][1][k];
-                *reinterpret_cast<uint32_t *>(dst + (2 * k) * XR * PITCH) =
-                    (a & 0xffffu) | (b << 16);
-                *reinterpret_cast<uint32_t *>(dst + (2 * k + 1) * XR * PITCH) =
-                    (a >> 16) | (b & 0xffff0000u);
+                for (int k = 0; k < CS / 2; ++k) {
+                    const uint32_t a = v[u][0][k], b = v[u][1][k];
+                    *reinterpret_cast<uint32_t *>(dst + (2 * k) * XR * PITCH) =
+                        (a & 0xffffu) | (b << 16);
+                    *reinterpret_cast<uint32_t *>(dst + (2 * k + 1) * XR * PITCH) =
+                        (a >> 16) | (b & 0xffff0000u);
+                }
+            } else {
+                // in-image values become U; the generated padding stays zero
+                const int ih = R0 + crow[u] - s.P;
+                const bool rok = (unsigned)ih < (unsigned)s.H;
+                const bool in0 = rok && cok0[u], in1 = rok && cok1[u];
+#pragma unroll
+                for (int c = 0; c < CS; ++c) {
+                    const int sh16 = 16 * (c & 1);
+                    uint32_t parts[2][NS];
+#pragma unroll
+                    for (int col = 0; col < 2; ++col) {
+                        const uint16_t xb = (uint16_t)(v[u][col][c / 2] >> sh16);
+                        float rem = (col ? in1 : in0)
+                                        ? bn_act(DT::widen(__builtin_bit_cast(typename DT::X, xb)),
+                                                 bnsc[c], bnsh[c], act)
+                                        : 0.0f;
+#pragma unroll
+                        for (int j = 0; j < NS; ++j) {
+                            const auto h = DT::narrow(rem);
+                            parts[col][j] = __builtin_bit_cast(uint16_t, h);
+                            rem -= DT::widen(h);
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < NS; ++j)
+                        *reinterpret_cast<uint32_t *>(dst + j * RING + c * XR * PITCH) =
+                            parts[0][j] | (parts[1][j] << 16);
+                }
             }
         }
     };
@@ -323,7 +374,11 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         // More than two fragments (filters wider than 32 taps): the chain of
         // 16 filter rows (at most 64 MFMAs) is added into a separate fp32
         // total, which the bias seeds, and restarts from zero.
-        constexpr bool FOLD = NFRAG > 2;
+        constexpr bool FOLD = NFRAG > 2 || NS > 1;
+        // filter rows per folded chain: 16 (three or four fragments), or as
+        // many as keep a chain within 64 MFMAs with the prologue's parts
+        constexpr int FPR = NS > 1 ? 64 / (NFRAG * NS) : 16;
+        constexpr int FP = FPR > 2 ? (FPR & ~1) : 2;
         f32x4 tot[FOLD ? NCH : 1][FOLD ? NB : 1];
         auto fold = [&]() {
             if constexpr (FOLD) {
@@ -352,7 +407,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         // from LDS.  B operands (unless kept) and the next windows are
         // produced before the MFMAs of row fh issue.
         struct Ops {
-            u32x4 A[NCH][NWIN];
+            u32x4 A[NS][NCH][NWIN];
             u32x4 B[NCH][FHK > 0 ? 1 : NFRAG];
         };
         auto full_a = [&](Ops &o) {
@@ -360,8 +415,11 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
             for (int ci = 0; ci < NCH; ++ci) {
                 const uint16_t *xr = xc[ci] + slot0 * PITCH;
 #pragma unroll
-                for (int win = 0; win < NWIN; ++win)
-                    o.A[ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
+                for (int j = 0; j < NS; ++j)
+#pragma unroll
+                    for (int win = 0; win < NWIN; ++win)
+                        o.A[j][ci][win] =
+                            *reinterpret_cast<const u32x4 *>(xr + j * RING + 16 * win);
             }
         };
         auto next_a = [&](Ops &o, const Ops &prev, int fh) {
@@ -373,21 +431,24 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                 if constexpr (AL) {
                     const uint16_t *xr = xc[ci] + slot * PITCH;
 #pragma unroll
-                    for (int win = 0; win < NWIN; ++win)
-                        o.A[ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
+                    for (int j = 0; j < NS; ++j)
+#pragma unroll
+                        for (int win = 0; win < NWIN; ++win)
+                            o.A[j][ci][win] =
+                                *reinterpret_cast<const u32x4 *>(xr + j * RING + 16 * win);
                     continue;
                 }
 #pragma unroll
                 for (int win = 0; win < NWIN; ++win)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        o.A[ci][win][q] = __builtin_amdgcn_update_dpp(
-                            0, (int)prev.A[ci][win][q], 0x101, 0xf, 0xf, true);
+                        o.A[0][ci][win][q] = __builtin_amdgcn_update_dpp(
+                            0, (int)prev.A[0][ci][win][q], 0x101, 0xf, 0xf, true);
                 if (t16 == 15) {
                     const uint16_t *xr = xc[ci] + slot * PITCH;
 #pragma unroll
                     for (int win = 0; win < NWIN; ++win)
-                        o.A[ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
+                        o.A[0][ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
                 }
             }
         };
@@ -415,7 +476,9 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                         } else {
                             bb = o.B[ci][f];
                         }
-                        acc[ci][b] = MfmaOp<DT>::run(o.A[ci][b + f], bb, acc[ci][b]);
+#pragma unroll
+                        for (int j = 0; j < NS; ++j)
+                            acc[ci][b] = MfmaOp<DT>::run(o.A[j][ci][b + f], bb, acc[ci][b]);
                     }
         };
 
@@ -473,10 +536,10 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     for (int win = 0; win < NWIN; ++win)
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
-                            n.A[ci][win][q] =
+                            n.A[0][ci][win][q] =
                                 AL ? Lw[fh & 1][ci][win][q]
                                    : __builtin_amdgcn_update_dpp((int)Lw[fh & 1][ci][win][q],
-                                                                 (int)p.A[ci][win][q], 0x101, 0xf,
+                                                                 (int)p.A[0][ci][win][q], 0x101, 0xf,
                                                                  0xf, false);
                 {
 #pragma unroll
@@ -524,7 +587,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     load_bs(o0, fh + 2);
                 }
                 mfmas(o1, fh + 1);
-                if (FOLD && (fh + 2) % 16 == 0) fold();
+                if (FOLD && (fh + 2) % FP == 0) fold();
             }
             if (fh < FH) mfmas(o0, fh);
         }
@@ -604,7 +667,35 @@ static hipError_t launch_mfma(const Plan &p, const void *x, const void *w, const
     hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL>), dim3(p.grid),
                        dim3(MfmaTile<CS, NB, NFRAG>::NT), p.lds_bytes, st,
                        (const uint16_t *)x, (const uint16_t *)w, (const float *)bias,
-                       (uint16_t *)y, p.s, p.aux0, p.aux1);
+                       (uint16_t *)y, p.s, p.aux0, p.aux1, nullptr, nullptr, 0);
+    return hipGetLastError();
+}
+
+// LDS of a tile with NS rings (the fused prologue's parts of U)
+template <int CS, int NB, int NFRAG, int NS>
+static int mfma_lds_bytes_ns(const Shape &s) {
+    using T = MfmaTile<CS, NB, NFRAG>;
+    const int XR = 16 + s.FH - 1;
+    return 2 * (NS * CS * XR * T::PITCH + CS * s.FH * NFRAG * T::ZLEN + 16 * T::ORS);
+}
+
+// The fused prologue on the same tiling as the plan's forward kernel (same
+// grid and launch shape); the tile's LDS grows by the extra rings.
+template <class DT, int CS, int NB, int NFRAG, int FHK, int NS>
+static hipError_t launch_mfma_bn(const Plan &p, const void *x, const void *w, const void *bias,
+                                 const float *bn_scale, const float *bn_shift, int act, void *y,
+                                 hipStream_t st) {
+    const int lds = mfma_lds_bytes_ns<CS, NB, NFRAG, NS>(p.s);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, 0, true, NS>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, 0, true, NS>), dim3(p.grid),
+                       dim3(MfmaTile<CS, NB, NFRAG>::NT), lds, st, (const uint16_t *)x,
+                       (const uint16_t *)w, (const float *)bias, (uint16_t *)y, p.s, p.aux0,
+                       p.aux1, bn_scale, bn_shift, act);
     return hipGetLastError();
 }
 
@@ -667,6 +758,40 @@ static const MfmaEntry kMfma[] = {
 #undef MF
 #undef MFA
 
+// The fused prologue: two fp16 parts or three bf16 parts of U, for filters
+// of at most two fragments; FHK = 8 keeps the B operands of filters of up
+// to 8 rows in registers.  The tilings whose extra A operands would spill
+// registers (8 channels on 64-column strips; 8 bf16 channels with two
+// fragments) are left out.
+struct MfmaBnEntry {
+    int dtype, cs, nb, nfrag, fhk;
+    LaunchBnFn fn;
+    int (*lds)(const Shape &);
+};
+#define MBH(CS_, NB_, NF_, FHK_)                                                    \
+    {DT_F16, CS_, NB_, NF_, FHK_, launch_mfma_bn<F16, CS_, NB_, NF_, FHK_, 2>,      \
+     mfma_lds_bytes_ns<CS_, NB_, NF_, 2>}
+#define MBB(CS_, NB_, NF_, FHK_)                                                    \
+    {DT_BF16, CS_, NB_, NF_, FHK_, launch_mfma_bn<BF16, CS_, NB_, NF_, FHK_, 3>,    \
+     mfma_lds_bytes_ns<CS_, NB_, NF_, 3>}
+static const MfmaBnEntry kMfmaBn[] = {
+    MBH(8, 2, 1, 8), MBB(8, 2, 1, 8), MBH(8, 2, 1, 0), MBB(8, 2, 1, 0), MBH(8, 2, 2, 0),
+    MBH(4, 4, 1, 0), MBB(4, 4, 1, 0), MBH(4, 4, 2, 0), MBB(4, 4, 2, 0),
+    MBH(4, 2, 1, 0), MBB(4, 2, 1, 0), MBH(4, 2, 2, 0), MBB(4, 2, 2, 0),
+};
+#undef MBH
+#undef MBB
+
+// The strip width (in 16-column blocks) that pads fewer output columns; on a
+// tie 32-column strips for one fragment and at least 7 filter rows
+// (measured: 7x7 up to 5 % and 13x13 up to 40 % faster, 9x9 equal, 5x5 and
+// two or more fragments slower), else 64.
+static int strip_blocks(const Shape &s, int nfrag) {
+    const int pad4 = (s.OW + 63) / 64 * 64, pad2 = (s.OW + 31) / 32 * 32;
+    const bool tie2 = nfrag == 1 && s.FH >= 7;
+    return pad2 < pad4 || (pad2 == pad4 && tie2) ? 2 : 4;
+}
+
 bool plan_mfma(Plan &p) {
     if (p.dtype != DT_F16 && p.dtype != DT_BF16) return false;
     if (p.s.S != 1 || p.s.D != 1) return false;
@@ -678,13 +803,7 @@ bool plan_mfma(Plan &p) {
     if (const char *env = getenv("DWCONV_MFMA_AL")) want_al = atoi(env);
     // DWCONV_MFMA_NB=2|4: strips of 32 / 64 output columns
     if (const char *env = getenv("DWCONV_MFMA_NB")) want_nb = atoi(env);
-    // the strip width that pads fewer output columns; on a tie 32-column
-    // strips for one fragment and at least 7 filter rows (measured: 7x7 up to
-    // 5 % and 13x13 up to 40 % faster, 9x9 equal, 5x5 and two or more
-    // fragments slower), else 64; the other width if nothing fits
-    const int pad4 = (p.s.OW + 63) / 64 * 64, pad2 = (p.s.OW + 31) / 32 * 32;
-    const bool tie2 = nfrag == 1 && p.s.FH >= 7;
-    const int nb_pref = want_nb ? want_nb : pad2 < pad4 || (pad2 == pad4 && tie2) ? 2 : 4;
+    const int nb_pref = want_nb ? want_nb : strip_blocks(p.s, nfrag);
     const MfmaEntry *e = nullptr;
     int lds = 0;
     for (int pass = 0; pass < 2 && !e; ++pass) {
@@ -732,6 +851,53 @@ bool plan_mfma(Plan &p) {
              "time, %d fragment(s) of 16 taps, A by %s, LDS %d B, %u x %d",
              16 * e->nb, e->cs, nfrag, e->al ? "LDS reads" : "DPP row shift", lds, p.grid,
              p.block);
+    return true;
+}
+
+// The forward pass with the fused prologue on the matrix cores, for a plan
+// whose forward pass runs there: the preferred strip width, 8-channel slices
+// before 4, the first tiling whose rings fit LDS.  Its own grid and launch
+// shape; the forward launchers are not used.
+bool plan_mfma_bn(Plan &b, const Plan &f) {
+    if (f.variant != V_MFMA) return false;
+    const int nfrag = (f.s.FW + 15) / 16;
+    if (nfrag > 2) return false;
+    const int nb_pref = strip_blocks(f.s, nfrag);
+    const MfmaBnEntry *e = nullptr;
+    int lds = 0;
+    for (int pass = 0; pass < 2 && !e; ++pass) {
+        for (const auto &k : kMfmaBn) {
+            if ((pass == 0) != (k.nb == nb_pref)) continue;
+            if (k.dtype != f.dtype || k.nfrag != nfrag || f.s.C % k.cs != 0) continue;
+            if (k.fhk && f.s.FH > k.fhk) continue;
+            const int need = k.lds(f.s);
+            if (need > 160 * 1024) continue;
+            e = &k;
+            lds = need;
+            break;
+        }
+    }
+    if (!e) return false;
+    const int ncs = f.s.C / e->cs;
+    const int nct = (f.s.OW + 16 * e->nb - 1) / (16 * e->nb);
+    const long long blocks = (long long)ncs * nct * f.s.N;
+    if (blocks >= (1LL << 31)) return false;
+    b = f;
+    b.cs = e->cs;
+    b.tile_w = 16 * e->nb;
+    b.tile_c = e->cs;
+    b.aux0 = ncs;
+    b.aux1 = nct;
+    b.block = 256;
+    b.grid = (uint32_t)blocks;
+    b.lds_bytes = lds;
+    b.launch = nullptr;
+    b.bn_launch = e->fn;
+    snprintf(b.desc, sizeof(b.desc),
+             "mfma with the prologue fused: strips of %d cols x %d ch, %d fragment(s), U in "
+             "%s, LDS %d B, %u x %d",
+             16 * e->nb, e->cs, nfrag, f.dtype == DT_F16 ? "2 fp16 parts" : "3 bf16 parts", lds,
+             b.grid, b.block);
     return true;
 }
 

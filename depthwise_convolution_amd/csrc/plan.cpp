@@ -83,8 +83,11 @@ bool plan_bn_act(Plan &b, const Plan &f) {
         b = f;
         return true;
     }
-    // the matrix-core and LDS-tile families do not: the row window / row
-    // chunks where they apply, else the direct family
+    // the matrix-core family, where the forward pass runs there and the
+    // prologue's extra rings fit LDS
+    if (plan_mfma_bn(b, f)) return true;
+    // else the row window / row chunks where they apply, else the direct
+    // family (the LDS-tile family does not fuse the prologue)
     const Shape &s = f.s;
     for (int v : {V_ROWWIN, V_DIRECT}) {
         if (make_plan(b, s.N, s.H, s.W, s.C, s.FH, s.FW, s.S, s.D, s.P, f.dtype, v) ==

@@ -99,5 +99,6 @@ bool plan_bn_act(Plan &b, const Plan &forward);
 bool plan_rowwin(Plan &p);
 bool plan_ldstile(Plan &p);
 bool plan_mfma(Plan &p);
+bool plan_mfma_bn(Plan &b, const Plan &forward);
 
 }  // namespace dw

@@ -128,9 +128,11 @@ dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
  * folded by the caller (scale = gamma / sqrt(var + eps), shift = beta -
  * mean * scale) -- owned by the caller, any 4-byte alignment.  x, w, bias and
  * y as for dwconv_fwd; the same tolerance as the forward pass applies, stated
- * against sum |x*s + b| * |w|.  Small filters run on the register families
- * with the prologue fused (the matrix-core and LDS-tile families do not fuse
- * it; their shapes run a row-window, row-chunk or direct kernel here).
+ * against sum |x*s + b| * |w|.  The register families and the matrix-core
+ * family fuse the prologue; the matrix cores hold U as two fp16 or three
+ * bf16 parts (U to fp32 precision), which for fp16 needs |x*s + b| within
+ * the fp16 range (65504).  LDS-tile shapes run a row-window, row-chunk or
+ * direct kernel here.
  * Enqueued on `stream` without waiting.  Returns DWCONV_ERR_INVALID_ARG for a
  * NULL handle, x, w, y, bn_scale or bn_shift or an unknown activation,
  * DWCONV_ERR_UNSUPPORTED for int8 and DWCONV_ERR_HIP if the launch fails. */

@@ -151,3 +151,26 @@ def test_identity_prologue_matches_plain_forward(fmt):
         y1, _ = run_bnact(x, w, bias, np.ones(C, np.float32), np.zeros(C, np.float32), "none",
                           shape, fmt, guard=64)
         assert np.array_equal(y0.view(np.uint8), y1.view(np.uint8)), shape
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_mfma_fused_prologue(fmt):
+    """The prologue fused into the matrix-core kernel (U held as two fp16 or
+    three bf16 parts): filters kept in registers (5x5, 7x7), runtime heights
+    whose chains are folded (31x31, a 25-row filter), ragged strips, several
+    channel slices and every activation, against the oracle."""
+    rng = np.random.default_rng({"f16": 311, "bf16": 312}[fmt])
+    for shape in [(2, 23, 37, 16, 7, 7, 1, 1, 3), (1, 30, 45, 8, 5, 5, 1, 1, 2),
+                  (1, 40, 33, 8, 13, 13, 1, 1, 6), (1, 26, 19, 8, 31, 31, 1, 1, 15),
+                  (1, 35, 20, 8, 25, 9, 1, 1, 4), (1, 17, 70, 24, 7, 7, 1, 1, 3)]:
+        N, H, W, C, FH, FW, S, D, P = shape
+        wl = synth.Workload("bn", fmt, *shape, ("normal", 0.0, 1.0),
+                            ("normal", 0.0, 1.0 / (FH * FW)), ("uniform", -0.1, 0.1),
+                            int(rng.integers(0, 2**31)))
+        x, w, bias = make_inputs(wl)
+        s, b = bn_params(C, int(rng.integers(0, 2**31)))
+        for act in ("none", "relu", "relu6"):
+            say(f"[gpu] bn+act on the matrix cores {fmt} {shape} {act}")
+            y, desc = run_bnact(x, w, bias, s, b, act, shape, fmt)
+            assert desc.startswith("mfma with the prologue fused"), desc
+            check_bnact(y, x, w, bias, s, b, act, shape, fmt, f"bnact mfma {fmt} {shape} {act}")
