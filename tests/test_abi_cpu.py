@@ -285,3 +285,24 @@ def test_plans_from_many_host_threads():
     for t in threads:
         t.join()
     assert not errors, errors[:3]
+
+
+@pytest.mark.parametrize("shape,fmt,family", [
+    ((64, 56, 56, 96, 7, 7, 1, 1, 3), "f16", "mfma with the prologue fused"),
+    ((32, 56, 56, 128, 31, 31, 1, 1, 15), "bf16", "mfma with the prologue fused"),
+    ((1, 20, 20, 16, 41, 41, 1, 1, 20), "f16", "rowchunk"),      # three fragments: VALU
+    ((64, 56, 56, 128, 3, 3, 1, 1, 1), "f32", "colstream"),
+    ((16, 112, 112, 61, 5, 5, 2, 2, 4), "f16", "direct"),        # no 16-byte vectors
+])
+def test_fused_prologue_family(shape, fmt, family):
+    """Which kernel runs the fused-prologue pass: the forward family where
+    it fuses the prologue, the matrix cores with U split into parts for their
+    shapes of at most two fragments, else a vector kernel."""
+    h = dw.dwconv_create(*shape, fmt)
+    try:
+        desc = dw.dwconv_fwd_bn_act_describe(h)
+    finally:
+        dw.dwconv_destroy(h)
+    assert desc.startswith(family), desc
+    if family.startswith("mfma"):
+        assert ("2 fp16 parts" if fmt == "f16" else "3 bf16 parts") in desc, desc
