@@ -707,7 +707,12 @@ bool plan_rowwin(Plan &p) {
     int owg_n = (p.s.OW + e->tm - 1) / e->tm;
     long long rows = e->th > 0 ? (long long)(p.s.OH + e->th - 1) / e->th : p.s.OH;
     long long total = (long long)ncv * owg_n * rows * p.s.N;
-    long long blocks = (total + 255) / 256;
+    // fp32 column streams launch one-wavefront workgroups: with four
+    // wavefronts per group the 3x3 layer's 448 groups left some CUs two and
+    // others one, and the single-wavefront launch measured 2-10 % faster on
+    // fp32 3x3 to 9x9 (fp16/bf16 3x3 measured no gain and keeps 256)
+    const int bs = e->th > 0 && p.elem_bytes == 4 ? 64 : 256;
+    long long blocks = (total + bs - 1) / bs;
     if (blocks >= (1LL << 31)) return false;
     p.variant = V_ROWWIN;
     p.vec = e->vec;
@@ -716,7 +721,7 @@ bool plan_rowwin(Plan &p) {
     p.tile_h = e->th > 0 ? e->th : 1;
     p.tile_w = e->tm;
     p.tile_c = e->vec;
-    p.block = 256;
+    p.block = bs;
     p.grid = (uint32_t)blocks;
     p.aux0 = ncv;
     p.aux1 = owg_n;
