@@ -117,6 +117,28 @@ def test_plan_tile(shape, fmt, variant, tile):
         raise dw.DwconvError(rc, "dwconv_plan_tile") if rc == 1 else AssertionError(rc)
 
 
+@pytest.mark.parametrize("shape,fmt,block", [
+    ((64, 56, 56, 128, 3, 3, 1, 1, 1), "f32", 64),
+    ((4, 30, 30, 64, 9, 9, 1, 1, 4), "f32", 64),
+    ((64, 56, 56, 128, 3, 3, 1, 1, 1), "f16", 256),
+    ((4, 30, 30, 64, 3, 3, 1, 1, 1), "bf16", 256),
+])
+def test_column_stream_launch_shape(shape, fmt, block):
+    """fp32 column streams launch one-wavefront workgroups, fp16/bf16 ones
+    four-wavefront groups; either way the grid covers every lane's strip
+    (channel vectors x column strips x row bands x images) exactly once."""
+    h = dw.dwconv_create(*shape, fmt)
+    try:
+        desc = dw.dwconv_plan_describe(h)
+        th, tm, vec = dw.dwconv_plan_tile(h)
+    finally:
+        dw.dwconv_destroy(h)
+    assert desc.startswith("colstream"), desc
+    N, H, W, C = shape[:4]
+    lanes = (C // vec) * -(-W // tm) * -(-H // th) * N
+    assert desc.endswith(f"{-(-lanes // block)} x {block}"), (desc, lanes)
+
+
 def test_forced_variants():
     # the direct family takes every shape
     h = dw.dwconv_create_variant(2, 9, 7, 5, 4, 2, 3, 2, 1, "bf16", "direct")
