@@ -139,6 +139,24 @@ def test_column_stream_launch_shape(shape, fmt, block):
     assert desc.endswith(f"{-(-lanes // block)} x {block}"), (desc, lanes)
 
 
+@pytest.mark.parametrize("shape,family", [
+    ((64, 56, 56, 96, 5, 5, 1, 1, 2), "colstream: VEC=2"),
+    ((16, 112, 112, 64, 5, 5, 1, 1, 2), "colstream: VEC=2"),
+    ((2, 30, 30, 32, 5, 5, 1, 1, 2), "mfma"),      # few lanes: the matrix cores
+    ((64, 56, 56, 96, 7, 7, 1, 1, 3), "mfma"),
+])
+def test_fp16_5x5_family(shape, family):
+    """fp16 5x5 at stride 1 on a map of at least 64K lanes runs the column
+    stream with paired taps; smaller maps and other filters keep their
+    families."""
+    h = dw.dwconv_create(*shape, "f16")
+    try:
+        desc = dw.dwconv_plan_describe(h)
+    finally:
+        dw.dwconv_destroy(h)
+    assert desc.startswith(family), desc
+
+
 def test_forced_variants():
     # the direct family takes every shape
     h = dw.dwconv_create_variant(2, 9, 7, 5, 4, 2, 3, 2, 1, "bf16", "direct")
