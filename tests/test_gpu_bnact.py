@@ -174,3 +174,19 @@ def test_mfma_fused_prologue(fmt):
             y, desc = run_bnact(x, w, bias, s, b, act, shape, fmt)
             assert desc.startswith("mfma with the prologue fused"), desc
             check_bnact(y, x, w, bias, s, b, act, shape, fmt, f"bnact mfma {fmt} {shape} {act}")
+
+
+def test_fp16_5x5_column_stream_prologue():
+    """A large fp16 5x5 map plans the column stream, so the fused pass runs
+    its prologue variant (widened inputs, one fma per tap) there, for every
+    activation, against the oracle."""
+    shape = (16, 112, 112, 64, 5, 5, 1, 1, 2)
+    wl = synth.Workload("bn", "f16", *shape, ("normal", 0.0, 1.0), ("normal", 0.0, 1 / 25),
+                        ("uniform", -0.1, 0.1), 331)
+    x, w, bias = make_inputs(wl)
+    s, b = bn_params(64, 332)
+    for act in ("relu", "relu6", "none"):
+        say(f"[gpu] bn+act fp16 5x5 column stream {act}")
+        y, desc = run_bnact(x, w, bias, s, b, act, shape, "f16")
+        assert desc.startswith("colstream: VEC=2"), desc
+        check_bnact(y, x, w, bias, s, b, act, shape, "f16", f"bnact f16 5x5 {act}")
