@@ -432,20 +432,40 @@ __device__ __forceinline__ void colstream_walk(const typename DT::X *xn,
     }
 }
 
-// fp16 filters of five or more taps: the taps of a filter row are taken two
-// at a time along the width, (fw, fw+1), against the input pair (x[j],
-// x[j+D]) of the same channel, with v_dot2_f32_f16 (two exact fp16 products
-// added into an fp32 sum): half the VALU operations of widening every input
-// and using one fma per tap.  An odd filter width pairs its last tap with a
-// zero tap (and a zero input past the window).  Same walk, accumulator
-// rotation and row partials as colstream_walk.
+// fp16 / bf16 filters of five or more taps: the taps of a filter row are
+// taken two at a time along the width, (fw, fw+1), against the input pair
+// (x[j], x[j+D]) of the same channel, with v_dot2_f32_f16 / v_dot2_f32_bf16
+// (two exact products added into an fp32 sum): half the VALU operations of
+// widening every input and using one fma per tap.  An odd filter width pairs
+// its last tap with a zero tap (and a zero input past the window).  Same
+// walk, accumulator rotation and row partials as colstream_walk.
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-template <int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, int NTL, bool UP>
-__device__ __forceinline__ void colstream_walk_dot2(const _Float16 *xn,
-                                                    const half2_t (&wp)[FH][(FW + 1) / 2][VEC],
-                                                    const float (&b0)[VEC], _Float16 *yn,
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <class DT>
+struct Dot2;
+template <>
+struct Dot2<F16> {
+    static __device__ __forceinline__ float dot(uint32_t a, uint32_t b, float c) {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b),
+                                      c, false);
+    }
+};
+template <>
+struct Dot2<BF16> {
+    static __device__ __forceinline__ float dot(uint32_t a, uint32_t b, float c) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                               __builtin_bit_cast(bf16x2_t, b), c, false);
+    }
+};
+template <class DT, int VEC, int FH, int FW, int TM, int TH, int D, int PF, bool NT, int NTL,
+          bool UP>
+__device__ __forceinline__ void colstream_walk_dot2(const typename DT::X *xn,
+                                                    const uint32_t (&wp)[FH][(FW + 1) / 2][VEC],
+                                                    const float (&b0)[VEC], typename DT::Y *yn,
                                                     const Shape &s, int ih0, int iw0, int oh0,
                                                     int ow0) {
+    using X = typename DT::X;
+    using Y = typename DT::Y;
     static_assert(VEC % 2 == 0, "channel pairs are whole dwords");
     constexpr int VD = VEC / 2;                 // dwords (channel pairs) per pixel
     constexpr int NWIN = TM + (FW - 1) * D;
@@ -457,7 +477,7 @@ __device__ __forceinline__ void colstream_walk_dot2(const _Float16 *xn,
     // columns outside the image are read from a clamped address and zeroed
     auto fetch = [&](uint32_t (&e)[NWIN][VD], int ih) {
         const int ihc = (unsigned)ih < (unsigned)s.H ? ih : 0;
-        const _Float16 *xr = xn + (long long)ihc * s.W * s.C;
+        const X *xr = xn + (long long)ihc * s.W * s.C;
 #pragma unroll
         for (int j = 0; j < NWIN; ++j) {
             const int iw = iw0 + j;
@@ -485,15 +505,14 @@ __device__ __forceinline__ void colstream_walk_dot2(const _Float16 *xn,
         // input pairs (x[j], x[j + D]) of each channel: the low halves of
         // the two dwords for the pair's first channel, the high halves for
         // its second
-        half2_t pr[NWIN][VEC];
+        uint32_t pr[NWIN][VEC];
 #pragma unroll
         for (int j = 0; j < NWIN; ++j)
 #pragma unroll
             for (int u = 0; u < VD; ++u) {
                 const uint32_t a = xv[j][u], b = j + D < NWIN ? xv[j + D][u] : 0u;
-                pr[j][2 * u] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(b, a, 0x05040100u));
-                pr[j][2 * u + 1] =
-                    __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(b, a, 0x07060302u));
+                pr[j][2 * u] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+                pr[j][2 * u + 1] = __builtin_amdgcn_perm(b, a, 0x07060302u);
             }
 #pragma unroll
         for (int q = 0; q < FH; ++q) {
@@ -511,8 +530,7 @@ __device__ __forceinline__ void colstream_walk_dot2(const _Float16 *xn,
                 for (int t = 0; t < TM; ++t)
 #pragma unroll
                     for (int v = 0; v < VEC; ++v)
-                        part[t][v] = __builtin_amdgcn_fdot2(pr[t + 2 * kp * D][v], wp[fh][kp][v],
-                                                            part[t][v], false);
+                        part[t][v] = Dot2<DT>::dot(pr[t + 2 * kp * D][v], wp[fh][kp][v], part[t][v]);
             const bool first = UP ? fh == FH - 1 : fh == 0;
             const bool last = UP ? fh == 0 : fh == FH - 1;
 #pragma unroll
@@ -524,10 +542,10 @@ __device__ __forceinline__ void colstream_walk_dot2(const _Float16 *xn,
 #pragma unroll
                 for (int t = 0; t < TM; ++t) {
                     if (ow0 + t < s.OW) {
-                        _Float16 ov[VEC];
+                        Y ov[VEC];
 #pragma unroll
-                        for (int v = 0; v < VEC; ++v) ov[v] = F16::narrow(acc[o][t][v]);
-                        store_out<_Float16, VEC, NT>(yn + ((long long)o * s.OW + t) * s.C, ov);
+                        for (int v = 0; v < VEC; ++v) ov[v] = DT::narrow(acc[o][t][v]);
+                        store_out<Y, VEC, NT>(yn + ((long long)o * s.OW + t) * s.C, ov);
                     }
                 }
             }
@@ -566,11 +584,12 @@ k_colstream(const typename DT::X *__restrict__ x, const typename DT::X *__restri
     const X *xn = x + (n * s.H) * (long long)s.W * s.C + c0;
 
     typename DT::Y *yn = y + ((n * s.OH + oh0) * (long long)s.OW + ow0) * s.C + c0;
-    // fp16, five or more taps, no prologue: taps paired for v_dot2_f32_f16
-    constexpr bool DOT2 = __is_same(DT, F16) && FW >= 5 && VEC % 2 == 0 && !BN;
+    // fp16 / bf16, five or more taps, no prologue: taps paired for v_dot2
+    constexpr bool DOT2 =
+        (__is_same(DT, F16) || __is_same(DT, BF16)) && FW >= 5 && VEC % 2 == 0 && !BN;
     if constexpr (DOT2) {
         constexpr int NP = (FW + 1) / 2;
-        half2_t wp[FH][NP][VEC];
+        uint32_t wp[FH][NP][VEC];
 #pragma unroll
         for (int fh = 0; fh < FH; ++fh)
 #pragma unroll
@@ -581,16 +600,19 @@ k_colstream(const typename DT::X *__restrict__ x, const typename DT::X *__restri
                     load_vec<X, VEC>(e1, w + (long long)tap_index(s, fh, 2 * kp + 1) * s.C + c0);
 #pragma unroll
                 for (int v = 0; v < VEC; ++v)
-                    wp[fh][kp][v] = (half2_t){e0[v], 2 * kp + 1 < FW ? e1[v] : (X)0};
+                    wp[fh][kp][v] = (uint32_t)__builtin_bit_cast(uint16_t, e0[v]) |
+                                    (2 * kp + 1 < FW
+                                         ? (uint32_t)__builtin_bit_cast(uint16_t, e1[v]) << 16
+                                         : 0u);
             }
         float bd[VEC];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) bd[v] = bias ? bias[c0 + v] : 0.0f;
         if (ohg & 1)
-            colstream_walk_dot2<VEC, FH, FW, TM, TH, D, PF, NT, NTL, true>(
+            colstream_walk_dot2<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL, true>(
                 xn, wp, bd, yn, s, ih0, iw0, oh0, ow0);
         else
-            colstream_walk_dot2<VEC, FH, FW, TM, TH, D, PF, NT, NTL, false>(
+            colstream_walk_dot2<DT, VEC, FH, FW, TM, TH, D, PF, NT, NTL, false>(
                 xn, wp, bd, yn, s, ih0, iw0, oh0, ow0);
         return;
     }
@@ -719,6 +741,11 @@ static const RegTile kTiles[] = {
     // faster on the largest maps (DWCONV_TILE=8x16p2n)
     CS(DT_F16, F16, 5, 5, 1, 2, 4, 14, 1, 1, 0),
     CS(DT_F16, F16, 5, 5, 1, 2, 8, 16, 2, 1, 0),
+    // bf16 5x5 (v_dot2_f32_bf16): faster than the matrix cores only on some
+    // maps (by 30 % on 128x32x32x1024, 25 % slower on 64x56x56x96), so the
+    // planner keeps bf16 on the matrix cores; this tiling is the row-window
+    // family's pick when that family is asked for
+    CS(DT_BF16, BF16, 5, 5, 1, 2, 4, 14, 1, 1, 0),
     CS(DT_F32, F32, 3, 3, 1, 4, 4, 14, 2, 1, 2),
     CS(DT_F32, F32, 3, 3, 1, 4, 4, 14, 2, 1, 0),
     // 5x5: two channels per lane keep the 5 x 5 filter and 5 rows of

@@ -143,13 +143,15 @@ def test_column_stream_launch_shape(shape, fmt, block):
     ((64, 56, 56, 96, 5, 5, 1, 1, 2), "colstream: VEC=2"),
     ((16, 112, 112, 64, 5, 5, 1, 1, 2), "colstream: VEC=2"),
     ((2, 30, 30, 32, 5, 5, 1, 1, 2), "mfma"),      # few lanes: the matrix cores
+    ((64, 56, 56, 96, 5, 5, 1, 1, 2, "bf16"), "mfma"),  # bf16 stays on the matrix cores
     ((64, 56, 56, 96, 7, 7, 1, 1, 3), "mfma"),
 ])
 def test_fp16_5x5_family(shape, family):
     """fp16 5x5 at stride 1 on a map of at least 64K lanes runs the column
-    stream with paired taps; smaller maps and other filters keep their
+    stream with paired taps; smaller maps, other filters and bf16 keep their
     families."""
-    h = dw.dwconv_create(*shape, "f16")
+    fmt = shape[9] if len(shape) > 9 else "f16"
+    h = dw.dwconv_create(*shape[:9], fmt)
     try:
         desc = dw.dwconv_plan_describe(h)
     finally:

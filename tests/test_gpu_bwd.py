@@ -414,17 +414,18 @@ def test_one_plan_on_two_streams_at_once():
         conv.close()
 
 
-def test_fp16_paired_tap_backward_data():
-    """The fp16 5x5 column stream with paired taps reading the filter rotated
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_paired_tap_backward_data(fmt):
+    """The fp16 / bf16 5x5 column stream with paired taps reading the filter rotated
     (backward data at stride 1), against the oracle's scatter form."""
     rng = np.random.default_rng(97)
     for shape in [(2, 23, 37, 16, 5, 5, 1, 1, 2), (1, 31, 20, 6, 5, 5, 1, 1, 4)]:
         N, H, W, C, FH, FW, S, D, P = shape
         OH = (H + 2 * P - (FH - 1) * D - 1) // S + 1
         OW = (W + 2 * P - (FW - 1) * D - 1) // S + 1
-        dy = synth.to_storage(rng.normal(0.0, 1.0, (N, OH, OW, C)), "f16")
-        w = synth.to_storage(rng.normal(0.0, 1 / 25, (FH, FW, C)), "f16")
+        dy = synth.to_storage(rng.normal(0.0, 1.0, (N, OH, OW, C)), fmt)
+        w = synth.to_storage(rng.normal(0.0, 1 / 25, (FH, FW, C)), fmt)
         say(f"[gpu] bwd data paired taps {shape}")
-        dx, desc = run_bwd(dy, w, shape, "f16", "rowwin")
+        dx, desc = run_bwd(dy, w, shape, fmt, "rowwin")
         assert desc.startswith("colstream: VEC=2"), desc
-        check_bwd(dx, dy, w, shape, "f16", f"bwd dot2 {shape}")
+        check_bwd(dx, dy, w, shape, fmt, f"bwd dot2 {fmt} {shape}")

@@ -291,31 +291,36 @@ def test_each_column_stream_tiling(fmt, monkeypatch):
             assert desc.startswith("colstream"), desc
 
 
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("tile", ["4x14p1n", "8x16p2n"])
-def test_fp16_paired_tap_column_stream(tile, monkeypatch):
-    """fp16 5x5 with the taps of each filter row paired for v_dot2_f32_f16
+def test_paired_tap_column_stream(tile, fmt, monkeypatch):
+    """fp16 / bf16 5x5 with the taps of each filter row paired for v_dot2
     (the fifth tap paired with a zero), each compiled tiling: ragged row and
     column strips, two channels (one channel pair per lane), padding 0 to 4,
     no bias, against the oracle; and the planner's pick of this family for a
     large map."""
+    if fmt == "bf16" and tile != "4x14p1n":
+        pytest.skip("bf16 compiles one paired-tap tiling")
     rng = np.random.default_rng(95)
     monkeypatch.setenv("DWCONV_TILE", tile)
     for shape, bias in [((2, 23, 37, 16, 5, 5, 1, 1, 2), True), ((1, 30, 19, 2, 5, 5, 1, 1, 0), True),
                         ((3, 17, 29, 6, 5, 5, 1, 1, 1), False), ((1, 40, 33, 10, 5, 5, 1, 1, 4), True),
                         ((1, 9, 70, 64, 5, 5, 1, 1, 3), True)]:
-        wl = synth.Workload("dot2", "f16", *shape, ("normal", 0.0, 1.0), ("normal", 0.0, 1 / 25),
+        wl = synth.Workload("dot2", fmt, *shape, ("normal", 0.0, 1.0), ("normal", 0.0, 1 / 25),
                             ("uniform", -0.1, 0.1), int(rng.integers(0, 2**31)))
         x, w, b = make_inputs(wl)
         if not bias:
             b = None
         say(f"[gpu] paired-tap column stream {tile} {shape}")
-        y, used = run(x, w, b, shape, "f16", "rowwin", guard=512)
-        assert_matches_oracle(y, x, w, b, shape, "f16", f"dot2 {tile} {shape}")
-        h = dw.dwconv_create_variant(*shape, "f16", "rowwin")
+        y, used = run(x, w, b, shape, fmt, "rowwin", guard=512)
+        assert_matches_oracle(y, x, w, b, shape, fmt, f"dot2 {fmt} {tile} {shape}")
+        h = dw.dwconv_create_variant(*shape, fmt, "rowwin")
         desc = dw.dwconv_plan_describe(h)
         dw.dwconv_destroy(h)
         assert desc.startswith("colstream: VEC=2") and "5x5" in desc, desc
     monkeypatch.delenv("DWCONV_TILE")
+    if fmt != "f16" or tile != "4x14p1n":
+        return
     shape = (16, 112, 112, 64, 5, 5, 1, 1, 2)
     wl = synth.Workload("dot2", "f16", *shape, ("normal", 0.0, 1.0), ("normal", 0.0, 1 / 25),
                         ("uniform", -0.1, 0.1), 96)
