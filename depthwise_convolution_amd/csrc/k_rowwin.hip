@@ -736,11 +736,11 @@ struct RegTile {
 
 static const RegTile kTiles[] = {
     // fp16 5x5: taps paired for v_dot2_f32_f16, two channels per lane.
-    // 4 x 14 outputs per lane with one row prefetched measured within 10 %
-    // of the best of six tilings on every map tried; 8 x 16 is up to 8 %
-    // faster on the largest maps (DWCONV_TILE=8x16p2n)
+    // 4 x 14 outputs per lane with one row prefetched measured within 15 %
+    // of the best of six tilings on every map tried (8 x 16, up to 14 %
+    // faster on the largest maps, needs more than 256 registers in the walk
+    // shared with bf16)
     CS(DT_F16, F16, 5, 5, 1, 2, 4, 14, 1, 1, 0),
-    CS(DT_F16, F16, 5, 5, 1, 2, 8, 16, 2, 1, 0),
     // bf16 5x5 (v_dot2_f32_bf16): faster than the matrix cores only on some
     // maps (by 30 % on 128x32x32x1024, 25 % slower on 64x56x56x96), so the
     // planner keeps bf16 on the matrix cores; this tiling is the row-window

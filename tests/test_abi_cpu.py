@@ -141,6 +141,8 @@ def test_column_stream_launch_shape(shape, fmt, block):
 
 @pytest.mark.parametrize("shape,family", [
     ((64, 56, 56, 96, 5, 5, 1, 1, 2), "colstream: VEC=2"),
+    ((128, 64, 64, 256, 5, 5, 1, 1, 2), "colstream: VEC=2 ch/lane, TM=4 x TH=14"),
+    ((16, 112, 112, 64, 5, 5, 1, 1, 2), "colstream: VEC=2 ch/lane, TM=4 x TH=14"),
     ((16, 112, 112, 64, 5, 5, 1, 1, 2), "colstream: VEC=2"),
     ((2, 30, 30, 32, 5, 5, 1, 1, 2), "mfma"),      # few lanes: the matrix cores
     ((64, 56, 56, 96, 5, 5, 1, 1, 2, "bf16"), "mfma"),  # bf16 stays on the matrix cores

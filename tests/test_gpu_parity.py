@@ -292,15 +292,13 @@ def test_each_column_stream_tiling(fmt, monkeypatch):
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-@pytest.mark.parametrize("tile", ["4x14p1n", "8x16p2n"])
+@pytest.mark.parametrize("tile", ["4x14p1n"])
 def test_paired_tap_column_stream(tile, fmt, monkeypatch):
     """fp16 / bf16 5x5 with the taps of each filter row paired for v_dot2
     (the fifth tap paired with a zero), each compiled tiling: ragged row and
     column strips, two channels (one channel pair per lane), padding 0 to 4,
     no bias, against the oracle; and the planner's pick of this family for a
     large map."""
-    if fmt == "bf16" and tile != "4x14p1n":
-        pytest.skip("bf16 compiles one paired-tap tiling")
     rng = np.random.default_rng(95)
     monkeypatch.setenv("DWCONV_TILE", tile)
     for shape, bias in [((2, 23, 37, 16, 5, 5, 1, 1, 2), True), ((1, 30, 19, 2, 5, 5, 1, 1, 0), True),
@@ -319,7 +317,7 @@ def test_paired_tap_column_stream(tile, fmt, monkeypatch):
         dw.dwconv_destroy(h)
         assert desc.startswith("colstream: VEC=2") and "5x5" in desc, desc
     monkeypatch.delenv("DWCONV_TILE")
-    if fmt != "f16" or tile != "4x14p1n":
+    if fmt != "f16":
         return
     shape = (16, 112, 112, 64, 5, 5, 1, 1, 2)
     wl = synth.Workload("dot2", "f16", *shape, ("normal", 0.0, 1.0), ("normal", 0.0, 1 / 25),
