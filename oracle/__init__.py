@@ -54,9 +54,10 @@ def bind(path):
     lib.dwref_points_i8.restype = I
     lib.dwref_bwd_data_f64.argtypes = [P, P, P, P] + [I] * 11
     lib.dwref_bwd_data_f64.restype = I
-    lib.dwref_bwd_filter_f64.argtypes = [P, P, P, P] + [I] * 9
-    lib.dwref_fwd_bnact_f64.argtypes = [P, P, P, P, P, I, P, P] + [I] * 11
+    lib.dwref_bwd_filter_f64.argtypes = [P, P, P, P] + [I] * 11
     lib.dwref_bwd_filter_f64.restype = I
+    lib.dwref_fwd_bnact_f64.argtypes = [P, P, P, P, P, I, P, P] + [I] * 11
+    lib.dwref_fwd_bnact_f64.restype = I
     return lib
 
 
@@ -208,12 +209,13 @@ def bwd_data(dy, w, shape, dtype, threads=1, lib=None):
     return dx, scale
 
 
-def bwd_filter(x, dy, shape, dtype, lib=None):
+def bwd_filter(x, dy, shape, dtype, threads=1, lib=None):
     """Gradient with respect to the filter, from its definition ("Flash-DWC",
     section 5.1).  ``shape`` is the forward operation (N, H, W, C, FH, FW,
     stride, dilation, pad); x is N x H x W x C and dy N x OH x OW x C in
     ``dtype`` (a float format).  Returns ``(dw, scale)`` in fp64, FH x FW x C,
-    scale the sum of |x*dy| per tap."""
+    scale the sum of |x*dy| per tap.  ``threads`` > 1 splits the channels over
+    threads (channels are independent, so the result is identical)."""
     if dtype not in ("f32", "f16", "bf16"):
         raise ValueError("backward filter is defined here for float dtypes")
     N, H, W, C, FH, FW, S, D, P = shape
@@ -228,9 +230,18 @@ def bwd_filter(x, dy, shape, dtype, lib=None):
         raise ValueError("x must be N x H x W x C and dy N x OH x OW x C")
     dw = np.empty((FH, FW, C), np.float64)
     scale = np.empty((FH, FW, C), np.float64)
-    rc = lib.dwref_bwd_filter_f64(_ptr(xx), _ptr(gg), _ptr(dw), _ptr(scale),
-                                  N, H, W, C, FH, FW, S, D, P)
-    if rc:
+
+    def run(c0, c1):
+        return lib.dwref_bwd_filter_f64(_ptr(xx), _ptr(gg), _ptr(dw), _ptr(scale),
+                                        N, H, W, C, FH, FW, S, D, P, c0, c1)
+    threads = max(1, min(int(threads), C))
+    if threads == 1:
+        rcs = [run(0, C)]
+    else:
+        bounds = np.linspace(0, C, threads + 1).astype(int)
+        with ThreadPoolExecutor(threads) as ex:
+            rcs = list(ex.map(run, bounds[:-1], bounds[1:]))
+    if any(rcs):
         raise ValueError("oracle rejected the shape")
     return dw, scale
 

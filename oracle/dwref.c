@@ -259,34 +259,48 @@ int dwref_bwd_data_f64(const double *dy, const double *w, double *dx, double *sc
  * Convolution Compute-Efficient on GPUs", section 5.1: the filter gradient
  * is a convolution of the input with the output gradient, a reduction over
  * the batch and the output positions).  x: N*H*W*C, dy: N*OH*OW*C,
- * dw and scale: FH*FW*C (scale = sum |x*dy| per tap, may be NULL).  Plain
- * loop, one filter tap of one channel at a time, fp64.  Returns 0, or -1 on
- * a bad shape. */
+ * dw and scale: FH*FW*C (scale = sum |x*dy| per tap, may be NULL).
+ *
+ * Only channels [c0, c1) are computed (channels are independent, so callers
+ * may split the channels over threads; every other element of dw and scale
+ * is left untouched).  Every dW[fh,fw,c] starts at zero and receives its
+ * products in the order of (n, oh, ow), the order of the sum above; the
+ * outputs are visited in that order and each one adds its products to the
+ * taps it touched, so the inputs are read along C.  fp64.  Returns 0, or -1
+ * on a bad shape or channel range. */
 int dwref_bwd_filter_f64(const double *x, const double *dy, double *dw, double *scale,
-                         int N, int H, int W, int C, int FH, int FW, int S, int D, int P)
+                         int N, int H, int W, int C, int FH, int FW, int S, int D, int P,
+                         int c0, int c1)
 {
     int OH, OW;
     if (!shape_ok(N, H, W, C, FH, FW, S, D, P, &OH, &OW)) return -1;
+    if (c0 < 0 || c1 > C || c0 > c1) return -1;
     for (int fh = 0; fh < FH; ++fh)
         for (int fw = 0; fw < FW; ++fw)
-            for (int c = 0; c < C; ++c) {
-                double acc = 0.0, sabs = 0.0;
-                for (long long n = 0; n < N; ++n)
-                    for (int oh = 0; oh < OH; ++oh) {
-                        int ih = oh * S - P + fh * D;
-                        if (ih < 0 || ih >= H) continue;      /* padding: no input */
-                        for (int ow = 0; ow < OW; ++ow) {
-                            int iw = ow * S - P + fw * D;
-                            if (iw < 0 || iw >= W) continue;
-                            double prod = x[((n * H + ih) * (long long)W + iw) * C + c] *
-                                          dy[((n * OH + oh) * (long long)OW + ow) * C + c];
-                            acc += prod;
-                            sabs += fabs(prod);
+            for (int c = c0; c < c1; ++c) {
+                long long o = ((long long)fh * FW + fw) * C + c;
+                dw[o] = 0.0;
+                if (scale) scale[o] = 0.0;
+            }
+    for (long long n = 0; n < N; ++n)
+        for (int oh = 0; oh < OH; ++oh)
+            for (int ow = 0; ow < OW; ++ow) {
+                const double *g = dy + ((n * OH + oh) * (long long)OW + ow) * C;
+                for (int fh = 0; fh < FH; ++fh) {
+                    int ih = oh * S - P + fh * D;
+                    if (ih < 0 || ih >= H) continue;          /* padding: no input */
+                    for (int fw = 0; fw < FW; ++fw) {
+                        int iw = ow * S - P + fw * D;
+                        if (iw < 0 || iw >= W) continue;
+                        const double *xi = x + ((n * H + ih) * (long long)W + iw) * C;
+                        long long o = ((long long)fh * FW + fw) * C;
+                        for (int c = c0; c < c1; ++c) {
+                            double prod = xi[c] * g[c];
+                            dw[o + c] += prod;
+                            if (scale) scale[o + c] += fabs(prod);
                         }
                     }
-                long long o = ((long long)fh * FW + fw) * C + c;
-                dw[o] = acc;
-                if (scale) scale[o] = sabs;
+                }
             }
     return 0;
 }

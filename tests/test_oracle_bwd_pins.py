@@ -264,11 +264,11 @@ BWF_MUTANTS = {
     "pad_sign": ("int ih = oh * S - P + fh * D;", "int ih = oh * S + P + fh * D;"),
     "no_width_dilation": ("int iw = ow * S - P + fw * D;", "int iw = ow * S - P + fw;"),
     "no_height_stride": ("int ih = oh * S - P + fh * D;", "int ih = oh - P + fh * D;"),
-    "tap_transposed": ("long long o = ((long long)fh * FW + fw) * C + c;",
-                       "long long o = ((long long)(FH - 1 - fh) * FW + (FW - 1 - fw)) * C + c;"),
-    "dy_transposed": ("dy[((n * OH + oh) * (long long)OW + ow) * C + c];",
-                      "dy[((n * OW + ow) * (long long)OH + oh) * C + c];"),
-    "scale_signed": ("sabs += fabs(prod);", "sabs += prod;"),
+    "tap_transposed": ("long long o = ((long long)fh * FW + fw) * C;",
+                       "long long o = ((long long)(FH - 1 - fh) * FW + (FW - 1 - fw)) * C;"),
+    "dy_transposed": ("dy + ((n * OH + oh) * (long long)OW + ow) * C;",
+                      "dy + ((n * OW + ow) * (long long)OH + oh) * C;"),
+    "scale_signed": ("scale[o + c] += fabs(prod);", "scale[o + c] += prod;"),
 }
 
 
