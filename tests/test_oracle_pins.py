@@ -91,6 +91,73 @@ def test_toeplitz_density():
 # output extent
 # ----------------------------------------------------------------------------
 
+def test_dwc_flops_filter_growth():
+    """Flash-DWC, section 6.1 (CUDA-core evaluation, small filters): going from
+    a 3x3 to a 7x7 filter raises the FLOP count about 5.44-fold."""
+    for n, oh, ow, c in [(1, 7, 9, 3), (128, 64, 64, 256)]:
+        r = forms.dwc_flops(n, oh, ow, c, 7, 7) / forms.dwc_flops(n, oh, ow, c, 3, 3)
+        assert round(r, 2) == 5.44
+
+
+def _count_macs_and_elements(n, ih, iw, c, fh, fw, s, d, p):
+    """Brute force: every (n, oh, ow, c, fh, fw) visit of the loop nest that
+    defines the operation, and the set of distinct input and weight elements
+    those visits name (padding positions name no element)."""
+    oh_n, ow_n = oracle.out_dim(ih, fh, s, d, p), oracle.out_dim(iw, fw, s, d, p)
+    macs = 0
+    xs, ws = set(), set()
+    for b in range(n):
+        for oh in range(oh_n):
+            for ow in range(ow_n):
+                for ch in range(c):
+                    for i in range(fh):
+                        for j in range(fw):
+                            macs += 1
+                            ws.add((i, j, ch))
+                            y, x = oh * s - p + i * d, ow * s - p + j * d
+                            if 0 <= y < ih and 0 <= x < iw:
+                                xs.add((b, y, x, ch))
+    return macs, oh_n, ow_n, xs, ws
+
+
+def test_dwc_flops_and_intensity_brute_force():
+    """Flash-DWC, section 2.2: the FLOP count is two per multiply-add of the
+    loop nest (the bias add is not counted), and the intensity bound divides
+    it by the elements read once -- every input element and every weight.
+    Brute force on shapes whose every input element is read (no stride gaps),
+    so the distinct-element counts equal N*IH*IW*C and C*FH*FW."""
+    for shape in [(1, 5, 6, 2, 3, 3, 1, 1, 1), (2, 4, 7, 3, 2, 3, 1, 1, 0),
+                  (1, 6, 6, 1, 5, 5, 1, 1, 2), (2, 5, 5, 2, 3, 3, 1, 2, 2)]:
+        n, ih, iw, c, fh, fw, s, d, p = shape
+        macs, oh, ow, xs, ws = _count_macs_and_elements(*shape)
+        assert len(xs) == n * ih * iw * c and len(ws) == c * fh * fw
+        assert forms.dwc_flops(n, oh, ow, c, fh, fw) == 2 * macs
+        assert forms.dwc_intensity_bound(n, ih, iw, c, oh, ow, fh, fw) == \
+            pytest.approx(2 * macs / (len(xs) + len(ws)), rel=1e-15)
+
+
+def test_dwc_intensity_vs_standard_convolution():
+    """Flash-DWC, section 2.2: a standard convolution with IC input channels
+    does IC times the work on the same input and IC times the weights, so its
+    bound is etaS = IC * flops / (N*IH*IW*IC + OC*FH*FW*IC); for large batch
+    and resolution etaD -> etaS / IC."""
+    ih = iw = 56
+    c, f = 128, 3
+    prev = None
+    for n in [1, 8, 64, 512, 4096]:
+        eta_d = forms.dwc_intensity_bound(n, ih, iw, c, ih, iw, f, f)
+        flops_std = c * forms.dwc_flops(n, ih, iw, c, f, f)   # every output sums IC channels
+        eta_s = flops_std / (n * ih * iw * c + c * f * f * c)
+        gap = abs(eta_d * c / eta_s - 1)
+        assert prev is None or gap < prev
+        prev = gap
+    assert prev < 1e-3
+    # and etaD stays near 2*FH*FW (= 18) for a 3x3 'same' layer, orders of
+    # magnitude below etaS (section 2.2: low reuse per input element)
+    assert 17 < forms.dwc_intensity_bound(64, 56, 56, 128, 56, 56, 3, 3) < 18
+    assert eta_s > 100 * eta_d
+
+
 def test_out_dim_is_span_inverse():
     for size in range(1, 30):
         for f in range(1, 8):
