@@ -44,8 +44,8 @@ def run_bwd(dy, w, shape, fmt, variant="auto", guard=512):
         dw.dwconv_destroy(h)
 
 
-def check_bwd(dx, dy, w, shape, fmt, what):
-    ref, scale = oracle.bwd_data(dy, w, shape, fmt, threads=8)
+def check_bwd(dx, dy, w, shape, fmt, what, threads=8):
+    ref, scale = oracle.bwd_data(dy, w, shape, fmt, threads=threads)
     return check.assert_float(dx, fmt, ref, scale, what)
 
 
@@ -85,15 +85,17 @@ def test_workload_bwd(name):
         say(f"      ok ({desc[:50]}) {rep}")
 
 
-def test_largekernel_bwd_two_images():
-    """The 31x31 bf16 layer's shape on two images (the oracle's full pass over
-    all 32 would take minutes)."""
+def test_largekernel_bwd():
+    """The 31x31 bf16 layer at its full size (32 images), every input
+    gradient element against the oracle."""
     wl = WORKLOADS["largekernel_bf16_31x31"]
-    shape = (2, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
+    shape = (wl.N, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
     dy, w = grads(shape, wl.dtype, 104)
-    say(f"[gpu] bwd largekernel x2")
+    say(f"[gpu] bwd largekernel N={wl.N}")
     dx, desc = run_bwd(dy, w, shape, wl.dtype)
-    check_bwd(dx, dy, w, shape, wl.dtype, "bwd largekernel")
+    say(f"[gpu] bwd largekernel: oracle pass ({desc[:50]})")
+    rep = check_bwd(dx, dy, w, shape, wl.dtype, "bwd largekernel", threads=16)
+    say(f"      ok {rep}")
 
 
 @pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
@@ -215,7 +217,7 @@ def run_bwf(x, dy, shape, fmt, ws_offset=0):
 
 
 def check_bwf(dwv, x, dy, shape, fmt, what):
-    ref, scale = oracle.bwd_filter(x, dy, shape, fmt)
+    ref, scale = oracle.bwd_filter(x, dy, shape, fmt, threads=16)
     return check.assert_float(dwv, "f32", ref, scale, what)
 
 
@@ -232,7 +234,7 @@ def bwf_inputs(shape, fmt, seed):
                                   "largekernel_bf16_31x31"])
 def test_workload_bwd_filter(name):
     wl = WORKLOADS[name]
-    N = wl.N if wl.FH < 31 else 2   # the oracle's 31x31 pass on 32 images takes minutes
+    N = wl.N
     shape = (N, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
     x, dy = bwf_inputs(shape, wl.dtype, 200 + wl.seed)
     say(f"[gpu] bwd filter {name} N={N}")
