@@ -38,12 +38,14 @@
 // dwords and a funnel shift.  The next block's input and gradient rows are
 // loaded while the current block runs.
 //
-// Rounding: each MFMA adds its 32 products exactly and rounds once (measured
-// on gfx950).  The MFMA chain of a block holds at most 16 * WN <= 64 MFMAs;
-// its result is added to a per-chunk fp32 total, at most 64 blocks per chunk;
-// the chunk totals go to the workspace and are merged pairwise by pass 2.
-// The worst-case error is therefore about (64 + 64 + log2 Z + 4) * 2^-24 *
-// sum |x * dy|, below 1e-5 * sum |x * dy|.
+// Rounding: each MFMA cuts the products of each of its four groups of 8
+// toward zero at 2^-24 of the group's largest, adds the groups and the
+// accumulator exactly and rounds once (measured on gfx950).  The MFMA chain
+// of a block holds at most 16 * WN <= 64 MFMAs; its result is added to a
+// per-chunk fp32 total, at most 64 blocks per chunk; the chunk totals go to
+// the workspace and are merged pairwise by pass 2.  The worst-case error is
+// therefore about (64 + 64 + 7 + log2 Z + 4) * 2^-24 * sum |x * dy|, below
+// 1e-5 * sum |x * dy| for every Z < 2^24.
 #include "plan.h"
 
 #include <stdio.h>

@@ -434,11 +434,18 @@ __device__ __forceinline__ void colstream_walk(const typename DT::X *xn,
 
 // fp16 / bf16 filters of five or more taps: the taps of a filter row are
 // taken two at a time along the width, (fw, fw+1), against the input pair
-// (x[j], x[j+D]) of the same channel, with v_dot2_f32_f16 / v_dot2_f32_bf16
-// (two exact products added into an fp32 sum): half the VALU operations of
-// widening every input and using one fma per tap.  An odd filter width pairs
-// its last tap with a zero tap (and a zero input past the window).  Same
-// walk, accumulator rotation and row partials as colstream_walk.
+// (x[j], x[j+D]) of the same channel, with v_dot2(c)_f32_f16 /
+// v_dot2_f32_bf16 (two products added into an fp32 sum): half the VALU
+// operations of widening every input and using one fma per tap.  The
+// instruction is not one rounding of the exact sum: on 2^20 random operand
+// sets per format (subnormals included) it stayed within
+// 4 * 2^-24 * (|c| + |a0*b0| + |a1*b1|), plus at most 7e-10 absolute for
+// fp16 with a subnormal operand.  A 5-tap row partial is a chain of three,
+// so an output of FH such partials errs by at most about
+// (12 + FH) * 2^-24 * sum|x*w| + 3 FH * 7e-10, well inside the bound.  An odd
+// filter width pairs its last tap with a zero tap and a zero input, so an
+// Inf or NaN just past an output's window stays out of its sum.  Same walk,
+// accumulator rotation and row partials as colstream_walk.
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 template <class DT>
@@ -529,8 +536,18 @@ __device__ __forceinline__ void colstream_walk_dot2(const typename DT::X *xn,
 #pragma unroll
                 for (int t = 0; t < TM; ++t)
 #pragma unroll
-                    for (int v = 0; v < VEC; ++v)
-                        part[t][v] = Dot2<DT>::dot(pr[t + 2 * kp * D][v], wp[fh][kp][v], part[t][v]);
+                    for (int v = 0; v < VEC; ++v) {
+                        // an odd width's last tap is paired with a zero tap:
+                        // its input pair carries a zero too, so an Inf or NaN
+                        // just past the output's window stays out of the sum
+                        const int j = t + 2 * kp * D;
+                        const uint32_t a =
+                            (FW & 1) && kp == NP - 1
+                                ? __builtin_amdgcn_perm(0u, xv[j][v / 2],
+                                                        (v & 1) ? 0x0c0c0302u : 0x0c0c0100u)
+                                : pr[j][v];
+                        part[t][v] = Dot2<DT>::dot(a, wp[fh][kp][v], part[t][v]);
+                    }
             const bool first = UP ? fh == FH - 1 : fh == 0;
             const bool last = UP ? fh == 0 : fh == FH - 1;
 #pragma unroll
