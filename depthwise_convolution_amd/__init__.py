@@ -25,13 +25,14 @@ import torch  # noqa: E402,F401
 
 __all__ = [
     "DWCONV_F32", "DWCONV_F16", "DWCONV_BF16", "DWCONV_I8",
-    "VARIANTS", "DwconvError", "DepthwiseConv2d", "library_path",
+    "DWCONV_SCRATCH_BYTES", "VARIANTS", "DwconvError", "DepthwiseConv2d", "library_path",
     "dwconv_create", "dwconv_create_variant", "dwconv_fwd", "dwconv_destroy",
     "dwconv_output_dims", "dwconv_plan_variant", "dwconv_plan_describe",
     "dwconv_plan_tile", "dwconv_status_string",
 ]
 
 DWCONV_F32, DWCONV_F16, DWCONV_BF16, DWCONV_I8 = 0, 1, 2, 3
+DWCONV_SCRATCH_BYTES = 64 << 20  # include/dwconv.h
 VARIANTS = {"auto": 0, "direct": 1, "rowwin": 2, "ldstile": 3, "mfma": 4}
 _VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 _DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}
@@ -81,6 +82,8 @@ _lib.dwconv_bwd_filter_workspace.argtypes = [_H, ctypes.POINTER(ctypes.c_size_t)
 _lib.dwconv_bwd_filter_workspace.restype = _I
 _lib.dwconv_bwd_filter.argtypes = [_H, _H, _H, _H, _H, _H]
 _lib.dwconv_bwd_filter.restype = _I
+_lib.dwconv_bwd_filter_noalloc.argtypes = [_H, _H, _H, _H, _H]
+_lib.dwconv_bwd_filter_noalloc.restype = _I
 _lib.dwconv_bwd_filter_describe.argtypes = [_H]
 _lib.dwconv_bwd_filter_describe.restype = ctypes.c_char_p
 
@@ -242,6 +245,15 @@ def dwconv_bwd_filter(h, x, dy, dw, workspace, stream=None) -> None:
                                 _stream(stream, x))
     if rc != 0:
         raise DwconvError(rc, "dwconv_bwd_filter")
+
+
+def dwconv_bwd_filter_noalloc(h, x, dy, dw, stream=None) -> None:
+    """dwconv_bwd_filter with the library's own scratch array as the workspace
+    (no allocation); DwconvError status 5 when the plan's workspace exceeds
+    DWCONV_SCRATCH_BYTES.  Calls that overlap on one GPU share the array."""
+    rc = _lib.dwconv_bwd_filter_noalloc(h, _ptr(x), _ptr(dy), _ptr(dw), _stream(stream, x))
+    if rc != 0:
+        raise DwconvError(rc, "dwconv_bwd_filter_noalloc")
 
 
 def dwconv_bwd_filter_describe(h) -> str:

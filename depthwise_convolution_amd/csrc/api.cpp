@@ -1,4 +1,5 @@
 // api.cpp -- the extern "C" entry points declared in include/dwconv.h.
+#include <mutex>
 #include <new>
 #include <stdint.h>
 
@@ -40,6 +41,35 @@ static bool plan_bwd_data(dw::Plan &b, const dw::Plan &f, int variant) {
     return dw::plan_bwd_direct(b, f);
 }
 
+// The filter gradient's workspace for callers that cannot allocate
+// (dwconv_bwd_filter_noalloc): one array per GPU, in the library's code
+// object, alive until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is a stand-in, not a device address); it
+// asks the runtime for this device's copy once, with the device current,
+// and keeps the address per device.
+static __device__ __align__(256) unsigned char scratch[DWCONV_SCRATCH_BYTES];
+
+static hipError_t scratch_address(void **out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
 extern "C" {
 
 dwconv_status_t dwconv_create_variant(dwconv_handle_t *out, int N, int H, int W, int C,
@@ -68,8 +98,6 @@ dwconv_status_t dwconv_create(dwconv_handle_t *out, int N, int H, int W, int C, 
     return dwconv_create_variant(out, N, H, W, C, FH, FW, stride, dilation, pad, dtype,
                                  DWCONV_VARIANT_AUTO);
 }
-
-static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
                            const void *bias, void *y, hipStream_t stream) {
@@ -129,21 +157,37 @@ dwconv_status_t dwconv_bwd_filter_workspace(dwconv_handle_t h, size_t *bytes) {
     return DWCONV_OK;
 }
 
-dwconv_status_t dwconv_bwd_filter(dwconv_handle_t h, const void *x, const void *dy,
-                                  float *dw, void *workspace, hipStream_t stream) {
-    if (!h || !x || !dy || !dw || !workspace) return DWCONV_ERR_INVALID_ARG;
-    if (!h->has_bwf) return DWCONV_ERR_UNSUPPORTED;
-    const dw::BwfPlan &b = h->bwf;
-    // the 16-byte channel vectors need aligned x and dy (the matrix-core
-    // pass also a 16-byte aligned workspace); the workspace and dw are
-    // written as floats
-    if (((uintptr_t)workspace & 3u) != 0 || ((uintptr_t)dw & 3u) != 0)
-        return DWCONV_ERR_INVALID_ARG;
+// Pass 1 (into the workspace) and pass 2 (the merge into dw) of the filter
+// gradient.  The 16-byte channel vectors need aligned x and dy (the
+// matrix-core pass also a 16-byte aligned workspace).
+static dwconv_status_t run_bwd_filter(const dw::BwfPlan &b, const void *x, const void *dy,
+                                      float *dw, void *workspace, hipStream_t stream) {
     dw::BwfLaunchFn fn = b.one_launch;
     if (aligned16(x) && aligned16(dy))
         fn = b.mfma_launch && aligned16(workspace) ? b.mfma_launch : b.vec_launch;
     hipError_t e = fn(b, x, dy, dw, workspace, stream);
     return e == hipSuccess ? DWCONV_OK : DWCONV_ERR_HIP;
+}
+
+dwconv_status_t dwconv_bwd_filter(dwconv_handle_t h, const void *x, const void *dy,
+                                  float *dw, void *workspace, hipStream_t stream) {
+    if (!h || !x || !dy || !dw || !workspace) return DWCONV_ERR_INVALID_ARG;
+    if (!h->has_bwf) return DWCONV_ERR_UNSUPPORTED;
+    // the workspace and dw are written as floats
+    if (((uintptr_t)workspace & 3u) != 0 || ((uintptr_t)dw & 3u) != 0)
+        return DWCONV_ERR_INVALID_ARG;
+    return run_bwd_filter(h->bwf, x, dy, dw, workspace, stream);
+}
+
+dwconv_status_t dwconv_bwd_filter_noalloc(dwconv_handle_t h, const void *x, const void *dy,
+                                          float *dw, hipStream_t stream) {
+    if (!h || !x || !dy || !dw) return DWCONV_ERR_INVALID_ARG;
+    if (!h->has_bwf) return DWCONV_ERR_UNSUPPORTED;
+    if (((uintptr_t)dw & 3u) != 0) return DWCONV_ERR_INVALID_ARG;
+    if (h->bwf.ws_bytes > (size_t)DWCONV_SCRATCH_BYTES) return DWCONV_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return DWCONV_ERR_HIP;
+    return run_bwd_filter(h->bwf, x, dy, dw, ws, stream);
 }
 
 const char *dwconv_bwd_filter_describe(dwconv_handle_t h) {
@@ -183,6 +227,7 @@ const char *dwconv_status_string(dwconv_status_t s) {
         case DWCONV_ERR_UNSUPPORTED: return "unsupported";
         case DWCONV_ERR_HIP: return "HIP runtime error";
         case DWCONV_ERR_ALLOC: return "out of host memory";
+        case DWCONV_ERR_SCRATCH: return "workspace larger than the library's scratch array";
     }
     return "unknown status";
 }

@@ -34,8 +34,9 @@
  *
  * Ownership: the caller allocates and owns every buffer (device memory),
  * including the backward-filter workspace.  The library allocates no device
- * memory.  A handle holds host-side plan data
- * only, is immutable after creation, and may be used from several host
+ * memory; its code object holds one scratch array of DWCONV_SCRATCH_BYTES per
+ * GPU, used only by dwconv_bwd_filter_noalloc.  A handle holds host-side plan
+ * data only, is immutable after creation, and may be used from several host
  * threads and on several streams at once.
  *
  * Errors: every function returns a status and never throws.  Nothing here
@@ -62,8 +63,13 @@ typedef enum {
     DWCONV_ERR_INVALID_ARG = 1,  /* bad shape, dtype, pointer or variant       */
     DWCONV_ERR_UNSUPPORTED = 2,  /* valid operation this build cannot run      */
     DWCONV_ERR_HIP = 3,          /* the HIP runtime reported an error          */
-    DWCONV_ERR_ALLOC = 4         /* host memory for the plan could not be had  */
+    DWCONV_ERR_ALLOC = 4,        /* host memory for the plan could not be had  */
+    DWCONV_ERR_SCRATCH = 5       /* needs more than DWCONV_SCRATCH_BYTES        */
 } dwconv_status_t;
+
+/* Size of the library's own scratch array per GPU, used by
+ * dwconv_bwd_filter_noalloc. */
+#define DWCONV_SCRATCH_BYTES (64u << 20)
 
 /* Kernel families.  AUTO lets the planner choose; the others force one (for
  * testing and A/B timing) and make dwconv_create fail with
@@ -198,6 +204,26 @@ const char *dwconv_bwd_data_describe(dwconv_handle_t h);
 dwconv_status_t dwconv_bwd_filter_workspace(dwconv_handle_t h, size_t *bytes);
 dwconv_status_t dwconv_bwd_filter(dwconv_handle_t h, const void *x, const void *dy,
                                   float *dw, void *workspace, hipStream_t stream);
+
+/* Backward filter for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): dwconv_bwd_filter with the workspace taken from an array of
+ * DWCONV_SCRATCH_BYTES (64 MiB) that the library's code object holds on every
+ * GPU it runs on, until the process ends.  The same kernels and the same
+ * result as dwconv_bwd_filter.  Allocates nothing and calls no allocating
+ * routine; the first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress) with the device current.
+ *   x, dy, dw   as for dwconv_bwd_filter (caller-owned device memory)
+ * The array needs no clearing: pass 1 writes every value pass 2 reads.
+ * Every call on one GPU shares that GPU's array, so calls that overlap on
+ * one GPU (on different streams, or from several host threads without
+ * ordering) race and give undefined results; calls in one stream order do
+ * not.  Returns DWCONV_ERR_INVALID_ARG for a NULL argument or a misaligned
+ * dw, DWCONV_ERR_UNSUPPORTED for int8, DWCONV_ERR_SCRATCH (before touching
+ * the GPU) when dwconv_bwd_filter_workspace() exceeds DWCONV_SCRATCH_BYTES,
+ * and DWCONV_ERR_HIP if the lookup or a launch fails. */
+dwconv_status_t dwconv_bwd_filter_noalloc(dwconv_handle_t h, const void *x, const void *dy,
+                                          float *dw, hipStream_t stream);
 
 /* A one-line description of the backward-filter kernels ("" if none). */
 const char *dwconv_bwd_filter_describe(dwconv_handle_t h);

@@ -8,6 +8,7 @@ import re
 import pytest
 
 import depthwise_convolution_amd as dw
+from synth import WORKLOADS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -262,6 +263,40 @@ def test_bwd_filter_workspace_and_errors():
     finally:
         dw.dwconv_destroy(h)
         dw.dwconv_destroy(q)
+
+
+def test_bwd_filter_noalloc_errors():
+    """The no-allocation filter gradient refuses, before touching the GPU, a
+    plan whose workspace exceeds the library's scratch array, and NULL or
+    misaligned arguments and int8 plans like dwconv_bwd_filter."""
+    lib = dw._lib
+    big = dw.dwconv_create(128, 128, 128, 128, 31, 31, 1, 1, 15, "f16")
+    h = dw.dwconv_create(2, 9, 9, 8, 3, 3, 1, 1, 1, "f32")
+    q = dw.dwconv_create(2, 9, 9, 8, 3, 3, 1, 1, 1, "i8")
+    try:
+        assert dw.dwconv_bwd_filter_workspace(big) > dw.DWCONV_SCRATCH_BYTES
+        assert dw.dwconv_bwd_filter_workspace(h) <= dw.DWCONV_SCRATCH_BYTES
+        fake = 1 << 40
+        assert lib.dwconv_bwd_filter_noalloc(big, fake, fake, fake, None) == 5
+        assert dw.dwconv_status_string(5) == "workspace larger than the library's scratch array"
+        assert lib.dwconv_bwd_filter_noalloc(None, fake, fake, fake, None) == 1
+        assert lib.dwconv_bwd_filter_noalloc(h, None, fake, fake, None) == 1
+        assert lib.dwconv_bwd_filter_noalloc(h, fake, fake, None, None) == 1
+        assert lib.dwconv_bwd_filter_noalloc(h, fake, fake, fake + 2, None) == 1  # dw misaligned
+        assert lib.dwconv_bwd_filter_noalloc(q, fake, fake, fake, None) == 2
+        # the five workloads' filter gradients fit the array
+        for wl in WORKLOADS.values():
+            if wl.dtype == "i8":
+                continue
+            g = dw.dwconv_create(wl.N, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride,
+                                 wl.dilation, wl.pad, wl.dtype)
+            try:
+                assert dw.dwconv_bwd_filter_workspace(g) <= dw.DWCONV_SCRATCH_BYTES, wl.name
+            finally:
+                dw.dwconv_destroy(g)
+    finally:
+        for x in (big, h, q):
+            dw.dwconv_destroy(x)
 
 
 def test_fwd_bn_act_support_and_errors():
