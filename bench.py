@@ -12,7 +12,11 @@ that no step finds its input in the 256 MB Infinity Cache (MALL) or in L2
 from an earlier step, the bench keeps several copies of x and y, at least
 1 GiB in all, and steps walk through them in turn.
 
-Prints one JSON line:
+Prints one JSON line.  The top-level fields are the named workload's (by
+default the fp32 3x3 MobileNet-shaped layer); with no --workload, --op or
+--variant the line also holds "workloads": the same record for each of the
+five workloads (tiny fp32 3x3, MobileNet fp32 3x3, ConvNeXt fp16 7x7,
+large-kernel bf16 31x31, strided int8 5x5), timed in the same run.
   value           algorithmic GB/s of K back-to-back steps (bytes / time per step)
   roofline        the kernel's average duration (HIP events around the K
                   back-to-back steps, one launch each) against the roof that
@@ -25,7 +29,10 @@ Prints one JSON line:
   kernel          plan, average, and the spread of single launches (a second
                   pass with an event pair around each launch: mean, median,
                   min, p90; each pair adds the event packets' own time)
-  copy_ceiling    torch's device copy of the same byte count, back to back
+  copy_ceiling    a hand-written HBM copy (depthwise_convolution_amd/ceiling,
+                  four 16-byte loads in flight per lane, non-temporal stores)
+                  of the same byte count, back to back; torch_copy is torch's
+                  device-to-device copy timed the same way
   cpu_baseline    the CPU oracle timed on this host's cores on a sample
 Algorithmic bytes count x, w, bias and y once each; halo re-reads and
 padding are not counted.  FLOPs are 2 per tap per output.
@@ -57,6 +64,12 @@ HBM_PEAK_GBS = 8000.0
 # 2.4 GHz = 78.6 TFLOP/s; int32 multiply-add runs at the same rate.
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
 VALU_PEAK_TFLOPS = 78.6
+# Vector dot-product instructions do more per lane and cycle, at the same
+# issue rate: v_dot2_f32_{f16,bf16} two multiply-adds (4 flop), v_dot4_i32_i8
+# four (8 ops): 157.3 TFLOP/s and 314.6 TOP/s over the chip.
+VALU_PEAKS = {"fma": VALU_PEAK_TFLOPS, "dot2": 2 * VALU_PEAK_TFLOPS,
+              "dot4": 4 * VALU_PEAK_TFLOPS}
+MAX_BUFFER_SETS = 64
 MALL_FLUSH_BYTES = 1 << 30
 XB = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
 YB = {"f32": 4, "f16": 2, "bf16": 2, "i8": 4}
@@ -94,15 +107,28 @@ def tile_model(wl, tile, OH, OW):
             "write_bytes": writes, "bytes": reads + writes}
 
 
-def roofline(wl, variant, nbytes, flops, kernel_s, traffic):
+def valu_class(plan, dtype):
+    """The vector instruction a non-matrix-core plan does its multiply-adds
+    with: v_dot4_i32_i8 (int8 tap-packed tile), v_dot2_f32_{f16,bf16} (the
+    fp16 / bf16 column stream with paired taps: two channels per lane, five or
+    more taps), else one fma (or 24-bit integer multiply-add) per tap."""
+    if "tap-packed" in plan or "v_dot4" in plan:
+        return "dot4"
+    if dtype in ("f16", "bf16") and plan.startswith("colstream: VEC=2"):
+        return "dot2"
+    return "fma"
+
+
+def roofline(wl, variant, nbytes, flops, kernel_s, traffic, plan=""):
     """The roof that binds this kernel: HBM unless the arithmetic at the peak
-    of the units the kernel uses (matrix cores for the mfma family, VALU
-    otherwise) takes longer than moving the algorithmic bytes at 8 TB/s."""
+    of the units the kernel uses (matrix cores for the mfma family, else the
+    VALU rate of its instruction class) takes longer than moving the
+    algorithmic bytes at 8 TB/s."""
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     if variant in ("mfma", "bwf_mfma"):
         bound, peak = "mfma", MFMA_PEAK_TFLOPS[wl.dtype]
     else:
-        bound, peak = "alu", VALU_PEAK_TFLOPS
+        bound, peak = "alu", VALU_PEAKS[valu_class(plan, wl.dtype)]
     t_cmp = flops / (peak * 1e12)
     if t_hbm >= t_cmp:
         achieved = nbytes / kernel_s / 1e9
@@ -145,29 +171,57 @@ def stored_traffic(workload, variant):
     return rec.get("hbm_bytes_per_launch")
 
 
-def copy_ceiling(torch, dev, stream, nbytes, sets, K, warmup):
-    """A plain device-to-device copy that reads nbytes/2 and writes nbytes/2
-    (the same total as one forward pass), over the same number of rotating
-    buffer sets, timed the same way.  It is the practical HBM ceiling on this
-    GPU, and the known-size kernel that calibrates the traffic counters."""
-    half = nbytes // 2
+def _copy_lib():
+    import ctypes
+    path = os.path.join(ROOT, "depthwise_convolution_amd", "libdwcopy.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.dwcopy_nt.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                              ctypes.c_void_p]
+    lib.dwcopy_nt.restype = ctypes.c_int
+    return lib
+
+
+def copy_ceiling(torch, dev, stream, nbytes, sets, K, warmup, kind="nt"):
+    """A plain copy that reads nbytes/2 and writes nbytes/2 (the same total as
+    one pass), over the same number of rotating buffer sets, timed the same
+    way: the practical HBM ceiling on this GPU, and the known-size kernel
+    that calibrates the traffic counters.  kind "nt": the hand-written
+    non-temporal copy (libdwcopy.so); "torch": torch's copy_."""
+    half = nbytes // 2 // 16 * 16
+    lib = _copy_lib() if kind == "nt" else None
+    if kind == "nt" and lib is None:
+        return None
     src = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(sets)]
     dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(sets)]
     for t in src:
         t.fill_(1)
+
+    def one(i):
+        if lib is not None:
+            rc = lib.dwcopy_nt(src[i % sets].data_ptr(), dst[i % sets].data_ptr(), half,
+                               stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"dwcopy_nt failed ({rc})")
+        else:
+            dst[i % sets].copy_(src[i % sets])
     for i in range(warmup):
-        dst[i % sets].copy_(src[i % sets])
+        one(i)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(K):
-        dst[i % sets].copy_(src[i % sets])
+        one(i)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
     return {"gbs": round(2 * half / (ms * 1e-3) / 1e9, 2), "avg_us": round(ms * 1e3, 3),
-            "bytes": 2 * half, "kind": "torch copy_ (device to device), back to back"}
+            "bytes": 2 * half,
+            "kind": ("hand-written copy: 2048 workgroups, 16 KiB chunks, 4 x 16-byte loads in flight per lane, "
+                     "non-temporal stores, back to back") if lib is not None
+            else "torch copy_ (device to device), back to back"}
 
 
 def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd", bn=None):
@@ -176,12 +230,13 @@ def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd", bn=None):
     after a one-image probe.  For the backward-data pass x holds dy; for the
     fused-prologue pass bn is (scale, shift) as numpy fp32 arrays."""
     import oracle
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    host_cores = len(os.sched_getaffinity(0))
+    threads = max(1, min(16, host_cores))
 
     def run(n, t):
         if op == "bwd_filter":
             shape = (n, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
-            oracle.bwd_filter(x[:n], w[:n], shape, wl.dtype)
+            oracle.bwd_filter(x[:n], w[:n], shape, wl.dtype, threads=t)
         elif op == "bwd_data":
             shape = (n, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride, wl.dilation, wl.pad)
             oracle.bwd_data(x[:n], w, shape, wl.dtype, threads=t)
@@ -190,6 +245,11 @@ def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd", bn=None):
                               wl.pad, wl.dtype, threads=t)
         else:
             oracle.fwd(x[:n], w, b, wl.stride, wl.dilation, wl.pad, wl.dtype, threads=t)
+
+    def used(n):
+        # the oracle splits the batch over threads (channels for the filter
+        # gradient), so at most that many run
+        return min(threads, wl.C if op == "bwd_filter" else n)
 
     def op_bytes(n):
         # algorithmic bytes of the pass over n images
@@ -202,6 +262,7 @@ def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd", bn=None):
             nbytes += 2 * wl.C * 4
         return nbytes, flops
 
+    run(1, 1)   # untimed: loads the oracle library and touches the inputs
     t0 = time.perf_counter()
     run(1, 1)
     per_image_1t = time.perf_counter() - t0
@@ -218,12 +279,14 @@ def cpu_baseline(wl, x, w, b, budget_s=20.0, op="fwd", bn=None):
             break
     dt = (time.perf_counter() - t0) / reps
     nbytes, flops = op_bytes(n)
-    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": used(n),
+            "host_cores": host_cores, "kind": "oracle",
+            "gflops": round(flops / dt / 1e9, 3),
             "single_thread": {"value": round(op_bytes(1)[0] / per_image_1t / 1e9, 4),
-                              "unit": "GB/s", "sample": f"1 image, {per_image_1t:.4f} s"},
+                              "unit": "GB/s",
+                              "sample": f"1 image, {per_image_1t:.4f} s (after one untimed run)"},
             "sample": f"{n} of {wl.N} images of {wl.name} ({op}; fp64/int64 loop nest, "
-                      f"{dt:.3f} s per run, mean of {reps}, {flops / dt / 1e9:.2f} GFLOP/s)"}
+                      f"{used(n)} threads, {dt:.3f} s per run, mean of {reps})"}
 
 
 # The pages' kernel sweep: square filters of growing size on three NHWC
@@ -281,7 +344,7 @@ def run_sweep(args):
                 flops = 2 * N * H * W * C * F * F
                 nbytes = 2 * N * H * W * C * XB[fmt] + F * F * C * XB[fmt] + C * 4
                 mfma = plan.startswith("mfma")
-                peak = MFMA_PEAK_TFLOPS[fmt] if mfma else VALU_PEAK_TFLOPS
+                peak = MFMA_PEAK_TFLOPS[fmt] if mfma else VALU_PEAKS[valu_class(plan, fmt)]
                 bound = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (peak * 1e12) else (
                     "mfma" if mfma else "alu")
                 rec = {"sweep": "filter size", "shape": [N, H, W, C], "dtype": fmt, "F": F,
@@ -300,50 +363,17 @@ def run_sweep(args):
     return summary
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--variant", default="auto")
-    ap.add_argument("--op", default="fwd",
-                    choices=["fwd", "bwd_data", "bwd_filter", "fwd_bn_act"],
-                    help="the forward pass (default), backward data or backward filter")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--warm-cache", action="store_true",
-                    help="also time K steps on one buffer set (labelled warm cache)")
-    ap.add_argument("--no-copy", action="store_true",
-                    help="skip the device-to-device copy ceiling measurement")
-    ap.add_argument("--sweep", action="store_true",
-                    help="the filter-size sweep instead of the bench line: TFLOP/s against "
-                         "F on three NHWC maps of 128 images (one JSON line per point)")
-    ap.add_argument("--sweep-filters", default=SWEEP_FILTERS)
-    ap.add_argument("--sweep-dtypes", default="f32,f16")
-    ap.add_argument("--sweep-shapes", type=int, default=len(SWEEP_SHAPES),
-                    help="how many of the three feature maps to sweep")
-    ap.add_argument("--sweep-seconds", type=float, default=0.3,
-                    help="timed launches per point: about this many seconds, 1 to 20")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
-              "supported (shard over the batch: one process per GPU, no exchange)",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.sweep:
-        run_sweep(args)
-        return
-
-    import torch
-    import depthwise_convolution_amd as dw
-    from synth import WORKLOADS, make_inputs
-
-    wl = WORKLOADS[args.workload]
+def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=True,
+            warm_cache=False):
+    """Times one workload's pass (op) and returns its record: value, kernel
+    average and spread, roofline, copy ceilings and the CPU oracle baseline
+    (cpu_budget seconds of host work; 0 skips it)."""
+    from synth import make_inputs
     nbytes, flops, OH, OW = work(wl)
-    bwd = args.op == "bwd_data"
-    bwf = args.op == "bwd_filter"
-    bna = args.op == "fwd_bn_act"
-    print(f"[bench] {wl.name} ({args.op}): generating inputs", file=sys.stderr, flush=True)
+    bwd = op == "bwd_data"
+    bwf = op == "bwd_filter"
+    bna = op == "fwd_bn_act"
+    print(f"[bench] {wl.name} ({op}): generating inputs", file=sys.stderr, flush=True)
     x, w, b = make_inputs(wl)
     if bna:
         # the forward pass plus the per-channel scale and shift it reads
@@ -367,6 +397,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
 
     def to_dev(a, fmt):
         if a is None:
@@ -379,7 +410,10 @@ def main():
     ydt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
            "i8": torch.int32}[wl.dtype]
     set_bytes = nbytes
-    sets = max(2, -(-MALL_FLUSH_BYTES // set_bytes))
+    # enough rotating copies that no step finds its input in the MALL or L2
+    # (a workload of a few KB stays cache-resident whatever is done: it is
+    # reported as latency only)
+    sets = min(MAX_BUFFER_SETS, max(2, -(-MALL_FLUSH_BYTES // set_bytes)))
     xd0 = to_dev(x, wl.dtype)
     xs = [xd0] + [xd0.clone() for _ in range(sets - 1)]
     yshape = (wl.N, wl.H, wl.W, wl.C) if bwd else (wl.N, OH, OW, wl.C)
@@ -394,13 +428,12 @@ def main():
     torch.cuda.synchronize()
 
     h = dw.dwconv_create_variant(wl.N, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride,
-                                 wl.dilation, wl.pad, wl.dtype, args.variant)
+                                 wl.dilation, wl.pad, wl.dtype, variant_req)
+    bn_s = bn_b = None
     if bwf:
         desc = dw.dwconv_bwd_filter_describe(h)
         if not desc:
-            print(f"bench.py: {wl.name} has no backward-filter pass in this build",
-                  file=sys.stderr)
-            sys.exit(2)
+            raise SystemExit(f"bench.py: {wl.name} has no backward-filter pass in this build")
         variant = "bwf_mfma" if desc.startswith("bwf mfma") else "bwf"
         wsb = torch.empty(dw.dwconv_bwd_filter_workspace(h), dtype=torch.uint8, device=dev)
 
@@ -408,9 +441,7 @@ def main():
             dw.dwconv_bwd_filter(h, xs[i % sets], dys[i % sets], ys[i % sets], wsb, stream)
     elif bwd:
         if not dw.dwconv_bwd_data_supported(h):
-            print(f"bench.py: {wl.name} has no backward-data pass in this build",
-                  file=sys.stderr)
-            sys.exit(2)
+            raise SystemExit(f"bench.py: {wl.name} has no backward-data pass in this build")
         desc = dw.dwconv_bwd_data_describe(h)
         variant = next(v for v in ("mfma", "ldstile", "direct", "rowwin", "colstream")
                        if desc.startswith(v))
@@ -421,8 +452,7 @@ def main():
     elif bna:
         desc = dw.dwconv_fwd_bn_act_describe(h)
         if not desc:
-            print(f"bench.py: {wl.name} has no fused-prologue pass", file=sys.stderr)
-            sys.exit(2)
+            raise SystemExit(f"bench.py: {wl.name} has no fused-prologue pass")
         variant = next(v for v in ("mfma", "ldstile", "direct", "rowwin", "colstream",
                                    "rowchunk") if desc.startswith(v))
         variant = "rowwin" if variant in ("colstream", "rowchunk") else variant
@@ -439,15 +469,14 @@ def main():
 
         def step(i):
             dw.dwconv_fwd(h, xs[i % sets], wd, bd, ys[i % sets], stream)
-    stream = torch.cuda.current_stream(dev)
     print(f"[bench] plan: {desc}; {sets} buffer sets of {set_bytes / 1e6:.1f} MB",
           file=sys.stderr, flush=True)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
-    K = args.steps
     # pass 1: K steps back to back, bracketed by synchronisation (one GPU:
-    # no barrier needed) -> whole-job throughput
+    # no barrier needed) -> whole-job throughput, and (one launch per step)
+    # the kernel's average duration, from HIP events on the launch stream
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -471,10 +500,10 @@ def main():
         ev1[i].record(stream)
     torch.cuda.synchronize()
     kern_ms = np.array([a.elapsed_time(z) for a, z in zip(ev0, ev1)])
-    # pass 3 (--warm-cache), labelled: the same buffer set every step, so up
+    # pass 3 (warm_cache), labelled: the same buffer set every step, so up
     # to 256 MB of it can stay in the MALL (not the headline figure)
     warm = None
-    if args.warm_cache:
+    if warm_cache:
         w0 = torch.cuda.Event(enable_timing=True)
         w1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -485,58 +514,51 @@ def main():
         torch.cuda.synchronize()
         warm = {"avg_us": round(w0.elapsed_time(w1) / K * 1e3, 3),
                 "note": "one buffer set reused every step; not the headline"}
-    tmodel = tile_model(wl, dw.dwconv_plan_tile(h), OH, OW) if args.op == "fwd" else None
+    tmodel = tile_model(wl, dw.dwconv_plan_tile(h), OH, OW) if op == "fwd" else None
     dw.dwconv_destroy(h)
 
-    # one launch per step: the kernel's average duration is the timed
-    # region's average
     ms_per_step = total_ms / K
     kavg_ms = ms_per_step
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    achieved = nbytes / (kavg_ms * 1e-3) / 1e9
-    traffic = stored_traffic(wl.name + (f":{args.op}" if args.op != "fwd" else ""), variant)
-    print(f"[bench] kernel avg {kavg_ms * 1e3:.2f} us over the timed region; single "
-          f"launches with events: mean {kern_ms.mean() * 1e3:.2f}, median "
+    traffic = stored_traffic(wl.name + (f":{op}" if op != "fwd" else ""), variant)
+    print(f"[bench] {wl.name}: kernel avg {kavg_ms * 1e3:.2f} us over the timed region; "
+          f"single launches with events: mean {kern_ms.mean() * 1e3:.2f}, median "
           f"{np.median(kern_ms) * 1e3:.2f}, min {kern_ms.min() * 1e3:.2f}, p90 "
-          f"{np.percentile(kern_ms, 90) * 1e3:.2f} us; host wall {t_wall * 1e3 / K:.2f} us/step",
+          f"{np.percentile(kern_ms, 90) * 1e3:.2f} us; host wall {t_wall * 1e3 / K:.2f} ms/step",
           file=sys.stderr, flush=True)
 
-    copy = None
-    if not args.no_copy:
-        copy = copy_ceiling(torch, dev, stream, nbytes, sets, K, args.warmup)
-        print(f"[bench] copy ceiling: {copy['gbs']:.0f} GB/s "
-              f"({copy['avg_us']:.2f} us per {nbytes / 2e6:.1f} MB read + write)",
-              file=sys.stderr, flush=True)
+    copy = tcopy = None
+    if with_copy:
+        copy = copy_ceiling(torch, dev, stream, nbytes, sets, K, warmup, "nt")
+        tcopy = copy_ceiling(torch, dev, stream, nbytes, sets, K, warmup, "torch")
+        for c in (copy, tcopy):
+            if c:
+                print(f"[bench] copy ceiling ({c['kind'][:22]}): {c['gbs']:.0f} GB/s "
+                      f"({c['avg_us']:.2f} us per {nbytes / 2e6:.1f} MB read + write)",
+                      file=sys.stderr, flush=True)
     del xs, ys
 
     cpu = None
-    if not args.no_cpu:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, x, w, b, op=args.op,
+    if cpu_budget > 0:
+        print(f"[bench] {wl.name}: timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, x, w, b, budget_s=cpu_budget, op=op,
                            bn=(bn_s.cpu().numpy(), bn_b.cpu().numpy()) if bna else None)
-
-    rec = {
-        "metric": {"fwd": METRIC, "bwd_data": METRIC_BWD, "bwd_filter": METRIC_BWF,
-                   "fwd_bn_act": METRIC_BNACT}[args.op],
+    ceiling = copy or tcopy
+    return {
+        "workload": wl.name,
+        "op": op,
+        "dtype": wl.dtype,
         "value": round(value, 2),
         "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": wl.dtype,
-        "data": "synthetic",
-        "config": {"workload": wl.name, "op": args.op, "N": wl.N, "H": wl.H, "W": wl.W, "C": wl.C,
-                   "FH": wl.FH, "FW": wl.FW, "stride": wl.stride,
-                   "dilation": wl.dilation, "pad": wl.pad, "bias": wl.b_dist is not None,
-                   "layout": "NHWC", "parallelism": "single GPU"},
         "gflops": round(flops / (ms_per_step * 1e-3) / 1e9, 2),
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": nbytes,
         "flops": flops,
+        "config": {"workload": wl.name, "op": op, "N": wl.N, "H": wl.H, "W": wl.W,
+                   "C": wl.C, "FH": wl.FH, "FW": wl.FW, "stride": wl.stride,
+                   "dilation": wl.dilation, "pad": wl.pad, "bias": wl.b_dist is not None,
+                   "layout": "NHWC", "parallelism": "single GPU"},
         "kernel": {"variant": variant, "plan": desc,
                    "avg_us": round(kavg_ms * 1e3, 3),
                    "single_launch_us": {
@@ -548,10 +570,91 @@ def main():
         "warm_cache": warm,
         "tile_model": tmodel,
         "copy_ceiling": copy,
-        "frac_of_copy": None if copy is None else round(achieved / copy["gbs"], 4),
-        "roofline": roofline(wl, variant, nbytes, flops, kavg_ms * 1e-3, traffic),
+        "torch_copy": tcopy,
+        "frac_of_copy": None if ceiling is None else round(value / ceiling["gbs"], 4),
+        "roofline": roofline(wl, variant, nbytes, flops, kavg_ms * 1e-3, traffic, desc),
         "cpu_baseline": cpu,
     }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None,
+                    help=f"one workload (default {DEFAULT_WORKLOAD}, plus the other four in "
+                         "the line's 'workloads')")
+    ap.add_argument("--variant", default="auto")
+    ap.add_argument("--op", default="fwd",
+                    choices=["fwd", "bwd_data", "bwd_filter", "fwd_bn_act"],
+                    help="the forward pass (default), backward data or backward filter")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="host seconds for the headline workload's CPU oracle sample "
+                         "(a third of it for each other workload)")
+    ap.add_argument("--warm-cache", action="store_true",
+                    help="also time K steps on one buffer set (labelled warm cache)")
+    ap.add_argument("--no-copy", action="store_true",
+                    help="skip the copy ceiling measurements")
+    ap.add_argument("--sweep", action="store_true",
+                    help="the filter-size sweep instead of the bench line: TFLOP/s against "
+                         "F on three NHWC maps of 128 images (one JSON line per point)")
+    ap.add_argument("--sweep-filters", default=SWEEP_FILTERS)
+    ap.add_argument("--sweep-dtypes", default="f32,f16")
+    ap.add_argument("--sweep-shapes", type=int, default=len(SWEEP_SHAPES),
+                    help="how many of the three feature maps to sweep")
+    ap.add_argument("--sweep-seconds", type=float, default=0.3,
+                    help="timed launches per point: about this many seconds, 1 to 20")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (shard over the batch: one process per GPU, no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.sweep:
+        run_sweep(args)
+        return
+
+    import torch
+    import depthwise_convolution_amd as dw
+    from synth import WORKLOADS
+
+    all_five = args.workload is None and args.op == "fwd" and args.variant == "auto"
+    name = args.workload or DEFAULT_WORKLOAD
+    cpu_s = 0.0 if args.no_cpu else args.cpu_seconds
+    head = measure(torch, dw, WORKLOADS[name], args.op, args.variant, args.steps,
+                   args.warmup, cpu_s, not args.no_copy, args.warm_cache)
+    others = {}
+    if all_five:
+        for other in WORKLOADS.values():
+            if other.name == name:
+                continue
+            others[other.name] = measure(torch, dw, other, "fwd", "auto", args.steps,
+                                         args.warmup, cpu_s / 3, not args.no_copy)
+    rec = {
+        "metric": {"fwd": METRIC, "bwd_data": METRIC_BWD, "bwd_filter": METRIC_BWF,
+                   "fwd_bn_act": METRIC_BNACT}[args.op],
+        "value": head["value"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": head["config"],
+    }
+    rec.update({k: v for k, v in head.items()
+                if k not in ("workload", "op", "dtype", "value", "unit", "ms_per_step",
+                             "config")})
+    if all_five:
+        rec["workloads"] = {name: {k: v for k, v in head.items() if k != "config"}}
+        rec["workloads"].update({k: {kk: vv for kk, vv in r.items() if kk != "config"}
+                                 for k, r in others.items()})
     print(json.dumps(rec), flush=True)
 
 

@@ -16,6 +16,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdwconv.so")
+# the bench's copy-ceiling kernel: its own small library, outside the C ABI
+COPY_SRC = os.path.join(HERE, "ceiling", "copy_ceiling.hip")
+COPY_LIB = os.path.join(HERE, "libdwcopy.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
 ARCH = "gfx950"
@@ -69,6 +72,11 @@ def build(verbose=False, jobs=None):
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
+    copy_obj = _compile(COPY_SRC, verbose)
+    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", COPY_LIB + ".tmp",
+           copy_obj]
+    subprocess.check_call(cmd)
+    os.replace(COPY_LIB + ".tmp", COPY_LIB)
     return LIB
 
 
