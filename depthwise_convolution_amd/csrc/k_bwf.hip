@@ -488,7 +488,7 @@ bool plan_bwd_filter(BwfPlan &b, const Plan &f) {
     // input and gradient vector loaded once per strip) replaces the vector
     // pass 1 (fp16 / bf16 have the matrix-core pass)
     if (f.dtype == DT_F32 && vec_ok && slide && f.s.FH == 3 && f.s.FW == 3 &&
-        !getenv("DWCONV_BWF_NOCS")) {
+        tune_int("bwf_nocs", 0) == 0) {
         const int TM = 4, TH = 14;
         const int ncv = f.s.C / VEC;
         const int cg = ncv < 64 ? ncv : 64;

@@ -430,7 +430,7 @@ bool plan_bwf_mfma(BwfPlan &b) {
     b.mfma_launch = nullptr;
     if (b.dtype != DT_F16 && b.dtype != DT_BF16) return false;
     if (s.S != 1 || s.D != 1 || s.FH > 32 || s.FW > 32) return false;
-    if (getenv("DWCONV_BWF_VALU")) return false;  // tuning hook: VALU pass 1 only
+    if (tune_int("bwf_valu", 0)) return false;  // tuning choice: VALU pass 1 only
     const int ni = (s.FH + 15) / 16, nt = (s.FW + 15) / 16;
     const BwfMfmaEntry *e = nullptr;
     for (const auto &k : kBwfMfma) {

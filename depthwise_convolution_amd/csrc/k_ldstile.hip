@@ -403,7 +403,7 @@ static const TapEntry kTap[] = {
 #undef TT
 
 // Rows per tile: as many as fit lds_cap bytes of LDS while the grid keeps at
-// least min_grid workgroups; DWCONV_LDS_TB=n forces n rows (a tuning hook).
+// least min_grid workgroups; the tuning choice lds_tb=n forces n rows.
 template <class RowsFn>
 static int pick_tb(const Plan &p, int nct, long long row_bytes, RowsFn rows, int min_grid,
                    long long lds_cap) {
@@ -412,10 +412,9 @@ static int pick_tb(const Plan &p, int nct, long long row_bytes, RowsFn rows, int
     while (TB < 16 && TB < p.s.OH && (long long)rows(TB + 1) * row_bytes <= lds_cap &&
            grid_of(TB + 1) >= min_grid)
         ++TB;
-    if (const char *env = getenv("DWCONV_LDS_TB")) {
-        const int want = atoi(env);
-        if (want >= 1 && want <= 64) TB = want < p.s.OH ? want : p.s.OH;
-    }
+    // tuning choice lds_tb=1..64: the tile height
+    const int want = tune_int("lds_tb", 0);
+    if (want >= 1 && want <= 64) TB = want < p.s.OH ? want : p.s.OH;
     return TB;
 }
 

@@ -727,7 +727,7 @@ struct MfmaEntry {
 
 // Each configuration twice: A windows read from LDS by every lane first
 // (measured faster than the DPP row shift: 7x7, 31x31, and 41x41 / 51x51 by
-// 15-20 %), then the DPP row shift (DWCONV_MFMA_AL=0).
+// 15-20 %), then the DPP row shift (tuning choice mfma_al=0).
 #define MF2(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_) \
     MFA(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_, true), MF(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_)
 #define MF2D(CS_, NB_, NF_, FHK_, FHT_) \
@@ -741,7 +741,7 @@ static const MfmaEntry kMfma[] = {
     MF2D(8, 4, 1, 8, 7),
     MF2D(4, 4, 2, 0, 31),
     // 32-byte pixel slices, 8 wavefronts (measured slower on 7x7: kept for
-    // DWCONV_MFMA_CS=16)
+    // mfma_cs=16)
     MF(DT_F16, F16, 16, 4, 1, 8, 7),   MF(DT_BF16, BF16, 16, 4, 1, 8, 7),
     // any filter height
     MF2D(8, 4, 1, 8, 0), MF2D(8, 4, 1, 0, 0), MF2D(8, 4, 2, 0, 0),
@@ -800,14 +800,12 @@ static int strip_blocks(const Shape &s, int nfrag) {
 bool plan_mfma(Plan &p) {
     if (p.dtype != DT_F16 && p.dtype != DT_BF16) return false;
     if (p.s.S != 1 || p.s.D != 1) return false;
+    // tuning choices: mfma_cs=4|8|16 the channel slice, mfma_al=0|1 A
+    // windows by DPP row shift / from LDS for every lane, mfma_nb=2|4 strips
+    // of 32 / 64 output columns
+    const int want_cs = tune_int("mfma_cs", 0), want_al = tune_int("mfma_al", -1),
+              want_nb = tune_int("mfma_nb", 0);
     const int nfrag = (p.s.FW + 15) / 16;
-    // DWCONV_MFMA_CS=4|8|16 picks the channel slice (a tuning hook)
-    int want_cs = 0, want_al = -1, want_nb = 0;
-    if (const char *env = getenv("DWCONV_MFMA_CS")) want_cs = atoi(env);
-    // DWCONV_MFMA_AL=0|1: A windows by DPP row shift / from LDS for every lane
-    if (const char *env = getenv("DWCONV_MFMA_AL")) want_al = atoi(env);
-    // DWCONV_MFMA_NB=2|4: strips of 32 / 64 output columns
-    if (const char *env = getenv("DWCONV_MFMA_NB")) want_nb = atoi(env);
     const int nb_pref = want_nb ? want_nb : strip_blocks(p.s, nfrag);
     const MfmaEntry *e = nullptr;
     int lds = 0;

@@ -732,7 +732,7 @@ static hipError_t launch_colstream_bn(const Plan &p, const void *x, const void *
 
 // Compiled tilings.  th == 0: row window (any stride); th > 0: column stream
 // of th rows (stride 1, FH fixed at compile time).  The first entry that
-// matches a shape is the planner's choice; DWCONV_TILE="TMxTH[nt]" picks
+// matches a shape is the planner's choice; the tuning choice tile=TMxTH[...] picks
 // another compiled entry for the same filter (tuning sweeps).
 struct RegTile {
     int dtype, fh, fw, s, d, vec, tm, th, pf, nt, ntl;
@@ -814,11 +814,10 @@ static bool plan_rowchunk(Plan &p) {
     if (p.s.S != 1 || p.s.D != 1 || p.dtype == DT_I8) return false;
     const int VEC = 16 / p.elem_bytes;
     // fp32: 12 outputs per lane (measured 3-8 % faster than 8 on the sweep
-    // maps; 16 needed all 256 registers and was slower); DWCONV_CHUNK_TM=8
-    // picks 8 (a tuning hook)
+    // maps; 16 needed all 256 registers and was slower); the tuning choice
+    // chunk_tm=8 picks 8
     int TM = p.dtype == DT_F32 ? 12 : 4;
-    if (const char *env = getenv("DWCONV_CHUNK_TM"))
-        if (p.dtype == DT_F32 && atoi(env) == 8) TM = 8;
+    if (p.dtype == DT_F32 && tune_int("chunk_tm", 0) == 8) TM = 8;
     if (p.s.C % VEC != 0) return false;
     const int ncv = p.s.C / VEC;
     const int owg_n = (p.s.OW + TM - 1) / TM;
@@ -860,11 +859,12 @@ static bool plan_rowchunk(Plan &p) {
 
 bool plan_rowwin(Plan &p) {
     const RegTile *e = nullptr;
-    // DWCONV_TILE="TMxTH[pPF[flags]]", flags: n = non-temporal y stores,
-    // l = non-temporal x loads, i = non-temporal loads of the pixels no other
-    // strip reads (a tuning hook; the table order is the default)
+    // tuning choice tile=TMxTH[pPF[flags]], flags: n = non-temporal y
+    // stores, l = non-temporal x loads, i = non-temporal loads of the pixels
+    // no other strip reads (the table order is the default)
     int want_tm = 0, want_th = -1, want_pf = -1, want_nt = -1, want_ntl = -1;
-    if (const char *env = getenv("DWCONV_TILE")) {
+    char tbuf[32];
+    if (const char *env = tune("tile", tbuf, sizeof(tbuf))) {
         char rest[8] = {0};
         int got = sscanf(env, "%dx%dp%d%7s", &want_tm, &want_th, &want_pf, rest);
         if (got < 2) want_th = -1;

@@ -3,6 +3,7 @@
 #include "plan.h"
 
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/dwconv.h"
@@ -18,6 +19,30 @@ int out_extent(int in, int f, int s, int d, int p) {
     if (room < 0) return 0;
     long long o = room / s + 1;
     return o > 0x7fffffffLL ? 0 : (int)o;
+}
+
+const char *tune(const char *key, char *buf, int len) {
+    const char *env = getenv("DWCONV_TUNE");
+    if (!env || !key || len < 1) return nullptr;
+    const size_t kl = strlen(key);
+    for (const char *p = env; *p;) {
+        const char *end = strchr(p, ',');
+        if (!end) end = p + strlen(p);
+        if ((size_t)(end - p) > kl && strncmp(p, key, kl) == 0 && p[kl] == '=') {
+            const int vl = (int)(end - p - kl - 1) < len - 1 ? (int)(end - p - kl - 1) : len - 1;
+            memcpy(buf, p + kl + 1, vl);
+            buf[vl] = 0;
+            return buf;
+        }
+        p = *end ? end + 1 : end;
+    }
+    return nullptr;
+}
+
+int tune_int(const char *key, int dflt) {
+    char buf[32];
+    const char *v = tune(key, buf, sizeof(buf));
+    return v ? atoi(v) : dflt;
 }
 
 static int elem_bytes_of(int dtype) {

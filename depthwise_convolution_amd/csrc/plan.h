@@ -79,6 +79,13 @@ bool plan_bwf_mfma(BwfPlan &b);
 // Pass 2: dw[e] = pairwise sum over z < Z of ws[z * FH*FW*C + e].
 hipError_t launch_bwf_reduce(const Shape &s, const float *ws, float *dw, int Z, hipStream_t st);
 
+// Tuning choices for testing and A/B timing, read at plan creation from the
+// DWCONV_TUNE environment variable: comma-separated key=value pairs
+// (include/dwconv.h lists the keys).  tune() returns the value of `key` in a
+// caller buffer (NULL when absent), tune_int() its integer value or `dflt`.
+const char *tune(const char *key, char *buf, int len);
+int tune_int(const char *key, int dflt);
+
 // Output extent along one axis; 0 when not even one output fits.
 int out_extent(int in, int f, int s, int d, int p);
 

@@ -265,6 +265,32 @@ def test_bwd_filter_workspace_and_errors():
         dw.dwconv_destroy(q)
 
 
+def test_tuning_switch(monkeypatch):
+    """DWCONV_TUNE (read at plan creation, host only): keys pick a compiled
+    alternative, unknown keys and malformed entries are ignored, and a tiling
+    no compiled kernel provides makes the forced family unsupported."""
+    shape = (32, 56, 56, 128, 31, 31, 1, 1, 15)
+
+    def desc(variant="auto"):
+        h = dw.dwconv_create_variant(*shape, "bf16", variant)
+        try:
+            return dw.dwconv_plan_describe(h)
+        finally:
+            dw.dwconv_destroy(h)
+    monkeypatch.delenv("DWCONV_TUNE", raising=False)
+    assert "strips of 64 cols" in desc()
+    monkeypatch.setenv("DWCONV_TUNE", "nothing=1,mfma_nb=2")
+    assert "strips of 32 cols" in desc()
+    monkeypatch.setenv("DWCONV_TUNE", "mfma_al=0")
+    assert "DPP row shift" in desc()
+    monkeypatch.setenv("DWCONV_TUNE", "bogus,mfma_nb")
+    assert "strips of 64 cols" in desc()
+    monkeypatch.setenv("DWCONV_TUNE", "tile=99x99")
+    with pytest.raises(dw.DwconvError) as e:
+        dw.dwconv_create_variant(64, 56, 56, 128, 3, 3, 1, 1, 1, "f32", "rowwin")
+    assert e.value.status == 2
+
+
 def test_bwd_filter_noalloc_errors():
     """The no-allocation filter gradient refuses, before touching the GPU, a
     plan whose workspace exceeds the library's scratch array, and NULL or

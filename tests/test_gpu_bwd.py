@@ -332,7 +332,7 @@ def test_bwd_filter_column_stream(monkeypatch):
     channel vector (256 strips per workgroup), 12 vectors (21 strips, a tree
     over a count that is not a power of two), 65 vectors (two channel
     groups), padding past the filter; the same shapes through the vector
-    pass 1 it replaces (DWCONV_BWF_NOCS) also match the oracle."""
+    pass 1 it replaces (the bwf_nocs tuning choice) also match the oracle."""
     cases = [(3, 17, 23, 4, 3, 3, 1, 1, 1), (2, 29, 30, 48, 3, 3, 1, 1, 1),
              (1, 15, 9, 260, 3, 3, 1, 1, 0), (2, 12, 13, 16, 3, 3, 1, 1, 2)]
     for shape in cases:
@@ -341,7 +341,7 @@ def test_bwd_filter_column_stream(monkeypatch):
         say(f"[gpu] bwd filter colstream {shape} ({desc[:40]})")
         assert desc.startswith("bwf colstream"), desc
         check_bwf(dwv, x, dy, shape, "f32", f"bwf cs {shape}")
-    monkeypatch.setenv("DWCONV_BWF_NOCS", "1")
+    monkeypatch.setenv("DWCONV_TUNE", "bwf_nocs=1")
     for shape in cases:
         x, dy = bwf_inputs(shape, "f32", 77)
         dwv, desc = run_bwf(x, dy, shape, "f32")

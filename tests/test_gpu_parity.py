@@ -257,14 +257,14 @@ def test_column_stream_wide_filters(F):
 
 @pytest.mark.parametrize("fmt", sorted(REG_TILES))
 def test_each_column_stream_tiling(fmt, monkeypatch):
-    """Each compiled column-stream tiling (picked through the DWCONV_TILE
+    """Each compiled column-stream tiling (picked through the tile tuning choice
     tuning hook) against the oracle, on shapes with ragged row and column
     strips, an image shorter than a strip, and a batch."""
     rng = np.random.default_rng(9)
     shapes = [(2, 30, 19, 64, 3, 3, 1, 1, 1), (1, 5, 57, 32, 3, 3, 1, 1, 1),
               (3, 17, 16, 128, 3, 3, 1, 1, 0), (1, 56, 56, 128, 3, 3, 1, 1, 2)]
     for tile in REG_TILES[fmt]:
-        monkeypatch.setenv("DWCONV_TILE", tile)
+        monkeypatch.setenv("DWCONV_TUNE", f"tile={tile}")
         for shape in shapes:
             N, H, W, C, FH, FW, S, D, P = shape
             wl = synth.Workload("tile", fmt, *shape, ("normal", 0.0, 1.0),
@@ -289,7 +289,7 @@ def test_paired_tap_column_stream(tile, fmt, monkeypatch):
     no bias, against the oracle; and the planner's pick of this family for a
     large map."""
     rng = np.random.default_rng(95)
-    monkeypatch.setenv("DWCONV_TILE", tile)
+    monkeypatch.setenv("DWCONV_TUNE", f"tile={tile}")
     for shape, bias in [((2, 23, 37, 16, 5, 5, 1, 1, 2), True), ((1, 30, 19, 2, 5, 5, 1, 1, 0), True),
                         ((3, 17, 29, 6, 5, 5, 1, 1, 1), False), ((1, 40, 33, 10, 5, 5, 1, 1, 4), True),
                         ((1, 9, 70, 64, 5, 5, 1, 1, 3), True)]:
@@ -305,7 +305,7 @@ def test_paired_tap_column_stream(tile, fmt, monkeypatch):
         desc = dw.dwconv_plan_describe(h)
         dw.dwconv_destroy(h)
         assert desc.startswith("colstream: VEC=2") and "5x5" in desc, desc
-    monkeypatch.delenv("DWCONV_TILE")
+    monkeypatch.delenv("DWCONV_TUNE")
     if fmt != "f16":
         return
     shape = (16, 112, 112, 64, 5, 5, 1, 1, 2)
@@ -346,9 +346,9 @@ def test_each_lds_tile_entry(entry, monkeypatch):
               (1, 30, 7, 130, F, F, S, D, 1)]
     for tb in ("", "1", "3"):
         if tb:
-            monkeypatch.setenv("DWCONV_LDS_TB", tb)
+            monkeypatch.setenv("DWCONV_TUNE", f"lds_tb={tb}")
         else:
-            monkeypatch.delenv("DWCONV_LDS_TB", raising=False)
+            monkeypatch.delenv("DWCONV_TUNE", raising=False)
         for shape in shapes:
             N, H, W, C, FH, FW, S_, D_, P = shape
             if (H + 2 * P - D * (F - 1) - 1) < 0 or (W + 2 * P - D * (F - 1) - 1) < 0:
@@ -382,13 +382,12 @@ MFMA_SLICES = {  # channel slice -> (dtype, F) combinations it is compiled for
 @pytest.mark.parametrize("al", [0, 1])
 @pytest.mark.parametrize("cs", sorted(MFMA_SLICES))
 def test_each_mfma_channel_slice(cs, al, monkeypatch):
-    """Each MFMA channel slice (picked through the DWCONV_MFMA_CS tuning
-    hook) against the oracle: compiled and runtime filter heights, one and two
+    """Each MFMA channel slice (picked through the mfma_cs tuning
+    choice) against the oracle: compiled and runtime filter heights, one and two
     16-tap fragments, ragged strips, a short image and several slices; A
     windows by DPP row shift (al=0) and by LDS reads (al=1, the compiled
     7x7 and 31x31 entries)."""
-    monkeypatch.setenv("DWCONV_MFMA_CS", str(cs))
-    monkeypatch.setenv("DWCONV_MFMA_AL", str(al))
+    monkeypatch.setenv("DWCONV_TUNE", f"mfma_cs={cs},mfma_al={al}")
     rng = np.random.default_rng(31 + cs)
     for fmt, F in MFMA_SLICES[cs]:
         for (N, H, W, C) in [(1, 23, 37, 2 * cs), (2, 9, 70, cs), (1, 40, 17, 3 * cs)]:
@@ -411,11 +410,11 @@ def test_each_mfma_channel_slice(cs, al, monkeypatch):
 
 @pytest.mark.parametrize("nb", [2, 4])
 def test_mfma_strip_widths(nb, monkeypatch):
-    """Strips of 32 and 64 output columns (forced through DWCONV_MFMA_NB)
+    """Strips of 32 and 64 output columns (forced through the mfma_nb tuning choice)
     for the compiled 7x7 and 31x31 entries and runtime filter heights with
     one and two fragments, against the oracle; widths that leave a ragged
     last strip and an output narrower than one strip."""
-    monkeypatch.setenv("DWCONV_MFMA_NB", str(nb))
+    monkeypatch.setenv("DWCONV_TUNE", f"mfma_nb={nb}")
     rng = np.random.default_rng(60 + nb)
     for fmt, F in [("f16", 7), ("bf16", 31), ("bf16", 5), ("f16", 17)]:
         for (N, H, W, C) in [(1, 20, 45, 16), (2, 17, 13, 8)]:
@@ -432,6 +431,41 @@ def test_mfma_strip_widths(nb, monkeypatch):
             y, used = run(x, w, b, shape, fmt, "mfma", guard=512)
             assert used == "mfma", used
             assert_matches_oracle(y, x, w, b, shape, fmt, f"mfma nb{nb} {shape}")
+
+
+# wide filters on the matrix cores: the compiled 31-row entry, ragged row
+# blocks and strips, outputs narrower than one strip, non-square filters of
+# 17 to 33 taps, one output row
+WIDE = [((1, 56, 56, 8, 31, 31, 1, 1, 15), "bf16"),
+          ((2, 33, 65, 12, 31, 31, 1, 1, 15), "f16"),
+          ((1, 40, 20, 4, 17, 17, 1, 1, 8), "bf16"),
+          ((1, 31, 97, 8, 5, 33, 1, 1, 16), "f16"),
+          ((3, 70, 45, 4, 23, 19, 1, 1, 9), "bf16"),
+          ((1, 1, 40, 4, 1, 25, 1, 1, 12), "f16"),
+          ((1, 30, 30, 4, 31, 31, 1, 1, 1), "bf16"),
+          ((2, 64, 64, 16, 31, 17, 1, 1, 3), "f16")]
+
+
+@pytest.mark.parametrize("case", range(len(WIDE)))
+def test_wide_filter_shapes(case):
+    """Wide and non-square filters on the matrix cores, every output against
+    the oracle, with a NaN guard band around y."""
+    shape, fmt = WIDE[case]
+    N, H, W, C, FH, FW, S, D, P = shape
+    rng = np.random.default_rng(700 + case)
+    wl = synth.Workload("wide", fmt, *shape, ("normal", 0.0, 1.0),
+                        ("normal", 0.0, 1.0 / (FH * FW)), ("uniform", -0.1, 0.1),
+                        int(rng.integers(0, 2**31)))
+    x, w, b = make_inputs(wl)
+    h = dw.dwconv_create_variant(*shape, fmt, "auto")
+    desc = dw.dwconv_plan_describe(h)
+    dw.dwconv_destroy(h)
+    assert desc.startswith("mfma"), desc
+    say(f"[gpu] wide filter {fmt} shape {shape}: {desc}")
+    y, used = run(x, w, b, shape, fmt, "auto", guard=1024)
+    assert used == "mfma", used
+    rep = assert_matches_oracle(y, x, w, b, shape, fmt, f"wide {shape}")
+    say(f"      ok {rep}")
 
 
 # --------------------------------------------- tensors at the size limit
@@ -529,8 +563,8 @@ def test_row_chunks_any_filter(fmt, monkeypatch):
     and flat filters, padding below, at and past half the filter, ragged
     widths, against the whole-tensor oracle."""
     rng = np.random.default_rng({"f32": 81, "f32-tm8": 84, "f16": 82, "bf16": 83}[fmt])
-    if fmt == "f32-tm8":  # the 8-wide fp32 tiling (DWCONV_CHUNK_TM tuning hook)
-        monkeypatch.setenv("DWCONV_CHUNK_TM", "8")
+    if fmt == "f32-tm8":  # the 8-wide fp32 tiling (the chunk_tm tuning choice)
+        monkeypatch.setenv("DWCONV_TUNE", "chunk_tm=8")
         fmt = "f32"
     vec = 4 if fmt == "f32" else 8
     cases = [(2, 23, 37, 2 * vec, 9, 9, 4), (1, 20, 41, vec, 8, 8, 3), (1, 17, 30, 3 * vec, 15, 16, 7),
