@@ -149,6 +149,14 @@ dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
  * bf16 parts (U to fp32 precision), which for fp16 needs |x*s + b| within
  * the fp16 range (65504).  LDS-tile shapes run a row-window, row-chunk or
  * direct kernel here.
+ * Cost: on the vector families the prologue is nearly free (fp32 3x3: about
+ * 4 % over dwconv_fwd).  On the matrix cores each part of U is one more set
+ * of operands and instructions, and measured about 1.7x dwconv_fwd's time
+ * for fp16 7x7 (two parts) and 3.5x for bf16 31x31 (three parts); a widening
+ * vector kernel was slower still for those shapes.  A caller that accepts U
+ * rounded once to the storage format (as an unfused batch-normalization pass
+ * would leave it) gets that lower precision faster from its own elementwise
+ * pass into a buffer followed by dwconv_fwd.
  * Enqueued on `stream` without waiting.  Returns DWCONV_ERR_INVALID_ARG for a
  * NULL handle, x, w, y, bn_scale or bn_shift or an unknown activation,
  * DWCONV_ERR_UNSUPPORTED for int8 and DWCONV_ERR_HIP if the launch fails. */
