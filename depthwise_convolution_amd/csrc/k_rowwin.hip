@@ -318,9 +318,10 @@ k_rowchunk(const typename DT::X *__restrict__ x, const typename DT::X *__restric
 //
 // Loads run PF rows ahead of the arithmetic: the raw run of row i + PF is
 // requested before row i is used, so each wavefront keeps PF + 1 rows of
-// loads in flight instead of waiting on every row.  Rows and columns outside
-// the image are fetched from a clamped in-bounds address and zeroed by a
-// select, so the stream has no divergent branches.
+// loads in flight instead of waiting on every row.  A row outside the image
+// issues no loads (its run is zeros); columns outside it are fetched from a
+// clamped in-bounds address and zeroed by a select, so the column loop has no
+// divergent branches.
 // ---------------------------------------------------------------------------
 template <class E, int VEC>
 __device__ __forceinline__ void load_vec_nt(E (&dst)[VEC], const E *src) {
@@ -335,8 +336,14 @@ __device__ __forceinline__ void load_vec_nt(E (&dst)[VEC], const E *src) {
 template <class X, int VEC, int NWIN, int NTL, int NT0, int NT1>
 __device__ __forceinline__ void fetch_run(X (&e)[NWIN][VEC], const X *xn, int ih, int H,
                                           int iw0, int W, int C) {
-    const int ihc = (unsigned)ih < (unsigned)H ? ih : 0;
-    const X *xr = xn + (long long)ihc * W * C;
+    if ((unsigned)ih >= (unsigned)H) {  // generated zero row: nothing fetched
+#pragma unroll
+        for (int j = 0; j < NWIN; ++j)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) e[j][v] = X(0);
+        return;
+    }
+    const X *xr = xn + (long long)ih * W * C;
 #pragma unroll
     for (int j = 0; j < NWIN; ++j) {
         const int iw = iw0 + j;
@@ -480,11 +487,18 @@ __device__ __forceinline__ void colstream_walk_dot2(const typename DT::X *xn,
     constexpr int RING = PF + 1;
     constexpr int NP = (FW + 1) / 2;
     auto row_of = [](int k) { return UP ? NROW - 1 - k : k; };
-    // the raw run of one input row, kept as packed channel pairs; rows and
-    // columns outside the image are read from a clamped address and zeroed
+    // the raw run of one input row, kept as packed channel pairs; a row
+    // outside the image is not fetched, columns outside it are read from a
+    // clamped address and zeroed
     auto fetch = [&](uint32_t (&e)[NWIN][VD], int ih) {
-        const int ihc = (unsigned)ih < (unsigned)s.H ? ih : 0;
-        const X *xr = xn + (long long)ihc * s.W * s.C;
+        if ((unsigned)ih >= (unsigned)s.H) {  // generated zero row: nothing fetched
+#pragma unroll
+            for (int j = 0; j < NWIN; ++j)
+#pragma unroll
+                for (int u = 0; u < VD; ++u) e[j][u] = 0u;
+            return;
+        }
+        const X *xr = xn + (long long)ih * s.W * s.C;
 #pragma unroll
         for (int j = 0; j < NWIN; ++j) {
             const int iw = iw0 + j;
