@@ -78,19 +78,30 @@ struct MfmaOp<BF16> {
     }
 };
 
-// LDS geometry of one workgroup strip.
-template <int CS, int NB, int NFRAG>
+// LDS geometry of one workgroup strip.  PK = 1: K windows of 32 input
+// columns at steps of 16, NFRAG fragments of 16 taps per filter row.
+// PK > 1 (row packing): the K of one MFMA holds PK filter rows of
+// KW = 32 / PK input columns each, and NFRAG is the number J of KW-column
+// windows one 16-column output block reads per group of PK rows.
+template <int CS, int NB, int NFRAG, int PK = 1>
 struct MfmaTile {
-    static constexpr int XW = 16 * (NB + NFRAG);  // staged input columns
+    static constexpr int KW = 32 / PK;
+    // distinct A windows per filter row (PK = 1) or row group (PK > 1)
+    static constexpr int NWIN = PK == 1 ? NB + NFRAG - 1 : (PK / 2) * (NB - 1) + NFRAG;
+    static constexpr int XW = PK == 1 ? 16 * (NB + NFRAG) : KW * NWIN;  // staged columns
     // elements per staged row: 16 (mod 32), i.e. 8 (mod 16) dwords, for
     // which the 16-byte A reads of 16 rows count no LDS bank conflicts
     // (measured on gfx950; 4 (mod 16) dwords counts one conflict cycle per
     // read, 0 (mod 16) several)
-    static constexpr int PITCH = XW % 32 == 16 ? XW : XW + 16;
-    static constexpr int ZLEN = 48;               // padded fragment length
+    static constexpr int PITCH = XW + (48 - XW % 32) % 32;
+    static constexpr int ZLEN = 48;               // padded fragment length (PK = 1)
+    // PK > 1: one padded filter row -- 16 zeros, the FW taps, zeros -- long
+    // enough for the 5 dwords a lane reads from element
+    // 16 + KW*j + (8g mod KW) - t16 of its row, a multiple of 8 elements
+    static constexpr int ZS = (18 + KW * NFRAG + 7) / 8 * 8;
     static constexpr int NW = CS >= 16 ? 8 : 4;       // wavefronts per workgroup
     static constexpr int NT = 64 * NW;                 // threads per workgroup
-    static constexpr int NPAIR = 128 * (NB + NFRAG);   // column pairs in 16 rows
+    static constexpr int NPAIR = 8 * XW;               // column pairs in 16 rows
     static constexpr int NEWP = (NPAIR + NT - 1) / NT; // column pairs per thread
     // output tile: pixel stride (an odd number of dwords) and row stride (4
     // mod 16 elements) chosen so that the regrouping writes of a wavefront
@@ -116,32 +127,50 @@ struct MfmaTile {
 // multiplied by the same B once per part, so the sum is that of U * w to
 // fp32 precision.  The chain is folded into an fp32 total every FP filter
 // rows (at most 64 MFMAs per chain).
-template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL = false, int NS = 1>
+// PK > 1 (row packing): the filter rows are taken PK at a time.  The K
+// window of one MFMA is PK filter rows of KW = 32 / PK consecutive input
+// columns each: lane (g, t16) holds row fh0 + 8g/KW + t16 of the ring,
+// columns KW*h + (8g mod KW) .. +7, and
+//   B_j[k][t] = w[fh0 + k/KW][KW*j + k mod KW - t]   (zero off the filter)
+// so that the J = NFRAG windows h = (PK/2)*b + j, j < J, of output block b
+// give its 16 outputs every tap of the PK rows.  A band of 31 taps fills
+// 31 of each 48 K entries instead of 31 of 64 (one row per MFMA), and a
+// 7-tap band 7 of 24 instead of 7 of 32: fewer MFMAs, and each lane reads
+// one A window per group instead of one per row.  Rows past FH (the last
+// group of a filter whose height is not a multiple of PK) have zero taps,
+// and their A entries are set to zero, so an Inf or NaN in the ring does
+// not reach outputs through them.
+template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL = false, int NS = 1,
+          int PK = 1>
 __global__ void __launch_bounds__(CS >= 16 ? 512 : 256, 2)  // at most 256 registers
 k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
        const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int ncs, int nct,
        const float *__restrict__ bns, const float *__restrict__ bnb, int act) {
-    using T = MfmaTile<CS, NB, NFRAG>;
-    constexpr int XW = T::XW, PITCH = T::PITCH, ZLEN = T::ZLEN;
+    using T = MfmaTile<CS, NB, NFRAG, PK>;
+    constexpr int XW = T::XW, PITCH = T::PITCH, ZLEN = T::ZLEN, ZS = T::ZS, KW = T::KW;
     constexpr int NW = T::NW, NT = T::NT;
     static_assert(NT == (CS >= 16 ? 512 : 256), "launch bounds match the tile");
     constexpr int NCH = CS / NW;            // channels per wavefront
-    constexpr int NWIN = NB + NFRAG - 1;    // distinct A windows per filter row
-    static_assert(FHK == 0 || NFRAG == 1, "kept B operands: one fragment");
+    constexpr int NWIN = T::NWIN;           // distinct A windows per filter row / group
+    static_assert(FHK == 0 || NFRAG == 1 || PK > 1, "kept B operands: one fragment");
     static_assert(FHT == 0 || FHK == 0 || FHT <= FHK, "kept B operands cover the filter");
-    static_assert(NS == 1 || (AL && FHT == 0 && NFRAG <= 2 && NS <= 3),
+    static_assert(NS == 1 || (AL && FHT == 0 && NFRAG <= 2 && NS <= 3 && PK == 1),
                   "the fused prologue: LDS-read A windows, runtime filter height");
+    static_assert(PK == 1 || ((PK == 2 || PK == 4) && AL && NS == 1 && (FHK == 0 || FHT > 0)),
+                  "row packing: 2 or 4 rows, LDS-read A windows, kept B with a fixed height");
     // FHT > 0: the filter height is a compile-time constant and the
     // filter-row loop is fully unrolled, so the accumulators keep fixed
     // registers (a runtime loop made the compiler rotate them)
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
     const int FH = FHT > 0 ? FHT : s.FH;            // filter height
+    const int FHP = (FH + PK - 1) / PK * PK;        // filter rows staged (PK > 1)
     const int XR = 16 + FH - 1;                     // ring rows
     const int RING = CS * XR * PITCH;               // elements of one ring
     uint16_t *xt = lds;                             // [NS][CS][XR][PITCH]
-    uint16_t *zt = xt + NS * RING;                  // [CS][FH][NFRAG][ZLEN]
-    uint16_t *ot = zt + CS * FH * NFRAG * ZLEN;     // [16][16*NB][CS]
+    uint16_t *zt = xt + NS * RING;  // [CS][FH][NFRAG][ZLEN], PK > 1: [CS][FHP][ZS]
+    const int ZT = PK == 1 ? CS * FH * NFRAG * ZLEN : CS * FHP * ZS;
+    uint16_t *ot = zt + ZT;                         // [16][16*NB][CS]
 
     // workgroup -> (image, column strip, channel slice); channel slices vary
     // fastest so that the slices of one strip run together and share the L2
@@ -253,9 +282,11 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     };
 
     // ---- filter slice as padded fragments: fragment f of filter row fh of
-    // channel c is 16 zeros, its 16 taps (zero past FW), 16 zeros ----
+    // channel c is 16 zeros, its 16 taps (zero past FW), 16 zeros; with row
+    // packing, filter row fh is 16 zeros, its FW taps, zeros to ZS, and rows
+    // FH .. FHP-1 are zero ----
     {
-        const int zlen = CS * FH * NFRAG * ZLEN;
+        const int zlen = ZT;
         for (int e = 8 * tid; e < zlen; e += 8 * NT)   // zlen is a multiple of 8
             *reinterpret_cast<u32x4 *>(zt + e) = (u32x4){0u, 0u, 0u, 0u};
         __syncthreads();
@@ -278,7 +309,8 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     if (fh < FH) {
 #pragma unroll
                         for (int c = 0; c < CS; ++c)
-                            zt[((c * FH + fh) * NFRAG + f) * ZLEN + 16 + q] =
+                            zt[PK == 1 ? ((c * FH + fh) * NFRAG + f) * ZLEN + 16 + q
+                                       : (c * FHP + fh) * ZS + 16 + fw] =
                                 (uint16_t)(v[k][c / 2] >> (16 * (c & 1)));
                     }
                 }
@@ -302,8 +334,13 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const int t16 = lane & 15;  // row of A, column of B and D
     // This lane's 8 entries of B are elements 16 + 8g - t16 .. +7 of the
     // padded fragment: B[k][t] = tap k - t.  They are read from the dword
-    // holding element boff rounded down, shifted right by bsh bits.
-    const int boff = 16 + 8 * g - t16;
+    // holding element boff rounded down, shifted right by bsh bits.  With
+    // row packing the lane's k range 8g .. 8g+7 is filter row pr of the
+    // group, columns po .. po+7 of each KW-column window, and its B entries
+    // of window j are elements 16 + KW*j + po - t16 .. +7 of padded row pr.
+    const int pr = PK == 1 ? 0 : (8 * g) / KW;
+    const int po = PK == 1 ? 8 * g : (8 * g) % KW;
+    const int boff = PK == 1 ? 16 + 8 * g - t16 : 16 + po - t16;
     const int bsh = 16 * (boff & 1);
     const uint16_t *xc[NCH];
     const uint16_t *zc[NCH];
@@ -311,8 +348,8 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
 #pragma unroll
     for (int ci = 0; ci < NCH; ++ci) {
         const int c = wave + NW * ci;
-        xc[ci] = xt + c * XR * PITCH + 8 * g;
-        zc[ci] = zt + c * FH * NFRAG * ZLEN + (boff & ~1);
+        xc[ci] = xt + c * XR * PITCH + po;
+        zc[ci] = zt + (PK == 1 ? c * FH * NFRAG * ZLEN : (c * FHP + pr) * ZS) + (boff & ~1);
         bv[ci] = bias ? bias[c0 + c] : 0.0f;
     }
     auto load_b = [&](u32x4 &b, int ci, int fh, int f) {
@@ -324,9 +361,29 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
 #pragma unroll
         for (int q = 0; q < 4; ++q) b[q] = __builtin_amdgcn_alignbit(d[q + 1], d[q], bsh);
     };
-    constexpr int KB = FHT > 0 && FHK > 0 ? FHT : FHK > 0 ? FHK : 1;
+    // row packing: window j of the group whose first filter row is fh0
+    auto load_bp = [&](u32x4 &b, int ci, int fh0, int j) {
+        const uint32_t *zd = reinterpret_cast<const uint32_t *>(zc[ci] + fh0 * ZS + KW * j);
+        uint32_t d[5];
+#pragma unroll
+        for (int q = 0; q < 5; ++q) d[q] = zd[q];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) b[q] = __builtin_amdgcn_alignbit(d[q + 1], d[q], bsh);
+    };
+    // row packing with kept B operands: every group's J windows
+    constexpr int NGK = PK > 1 && FHK > 0 ? (FHT + PK - 1) / PK : 1;
+    u32x4 Bp[PK > 1 && FHK > 0 ? NCH : 1][NGK][PK > 1 && FHK > 0 ? NFRAG : 1];
+    if constexpr (PK > 1 && FHK > 0) {
+#pragma unroll
+        for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+            for (int gi = 0; gi < NGK; ++gi)
+#pragma unroll
+                for (int j = 0; j < NFRAG; ++j) load_bp(Bp[ci][gi][j], ci, PK * gi, j);
+    }
+    constexpr int KB = PK > 1 ? 1 : FHT > 0 && FHK > 0 ? FHT : FHK > 0 ? FHK : 1;
     u32x4 Bk[NCH][KB];
-    if constexpr (FHK > 0) {
+    if constexpr (FHK > 0 && PK == 1) {
 #pragma unroll
         for (int ci = 0; ci < NCH; ++ci)
 #pragma unroll
@@ -379,7 +436,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         // More than two fragments (filters wider than 32 taps): the chain of
         // 16 filter rows (at most 64 MFMAs) is added into a separate fp32
         // total, which the bias seeds, and restarts from zero.
-        constexpr bool FOLD = NFRAG > 2 || NS > 1;
+        constexpr bool FOLD = PK == 1 && (NFRAG > 2 || NS > 1);
         // filter rows per folded chain: 16 (three or four fragments), or as
         // many as keep a chain within 64 MFMAs with the prologue's parts
         constexpr int FPR = NS > 1 ? 64 / (NFRAG * NS) : 16;
@@ -487,7 +544,95 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     }
         };
 
-        if constexpr (FHT > 0 && FHK > 0) {
+        if constexpr (PK > 1) {
+            // Row packing: group gi covers filter rows PK*gi .. PK*gi+PK-1.
+            // The unit of the pipeline is one channel's group: the LDS reads
+            // of the next unit are issued before the MFMAs of the current
+            // one (two units of operands in registers).  At most 8 groups of
+            // 6 windows (FH <= 32, FW <= 33): a chain of at most 48 MFMAs
+            // per tile.
+            int slotp = 16 * rb + t16 + pr;  // ring slot of this lane's row at fh0 = 0
+            slotp %= XR;
+            struct OpsU {
+                u32x4 A[NWIN];
+                uint32_t R[FHK > 0 ? 1 : NFRAG][5];
+            };
+            auto load_unit = [&](OpsU &o, int ci, int fh0) {
+                int sl = slotp + fh0;
+                sl -= sl >= XR ? XR : 0;
+                // rows past FH: zero A entries (the taps there are zero too)
+                const bool full = FHT > 0 && fh0 + PK <= FHT;
+                const bool ok = full || fh0 + pr < FH;
+                const uint16_t *xr = xc[ci] + sl * PITCH;
+#pragma unroll
+                for (int h = 0; h < NWIN; ++h) {
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(xr + KW * h);
+                    o.A[h] = ok ? a : (u32x4){0u, 0u, 0u, 0u};
+                }
+                if constexpr (FHK == 0) {
+#pragma unroll
+                    for (int j = 0; j < NFRAG; ++j) {
+                        const uint32_t *zd =
+                            reinterpret_cast<const uint32_t *>(zc[ci] + fh0 * ZS + KW * j);
+#pragma unroll
+                        for (int q = 0; q < 5; ++q) o.R[j][q] = zd[q];
+                    }
+                }
+            };
+            auto mfmas_unit = [&](const OpsU &o, int ci, int gi) {
+                u32x4 bb[NFRAG];
+#pragma unroll
+                for (int j = 0; j < NFRAG; ++j) {
+                    if constexpr (FHK > 0) {
+                        bb[j] = Bp[ci][0][j];
+#pragma unroll
+                        for (int k = 1; k < NGK; ++k)
+                            if (gi == k) bb[j] = Bp[ci][k][j];
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            bb[j][q] = __builtin_amdgcn_alignbit(o.R[j][q + 1], o.R[j][q], bsh);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < NFRAG; ++j)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        acc[ci][b] = MfmaOp<DT>::run(o.A[(PK / 2) * b + j], bb[j], acc[ci][b]);
+            };
+            OpsU o[2];
+            load_unit(o[0], 0, 0);
+            if constexpr (FHT > 0) {
+                constexpr int NU = (FHT + PK - 1) / PK * NCH;
+#pragma unroll
+                for (int u = 0; u < NU; ++u) {
+                    if (u + 1 < NU) load_unit(o[(u + 1) & 1], (u + 1) % NCH, PK * ((u + 1) / NCH));
+                    mfmas_unit(o[u & 1], u % NCH, u / NCH);
+                    // keep the scheduler from hoisting later units' operands
+                    // (and their registers) above this unit's MFMAs
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                // groups two at a time, so that a unit's operand buffer is
+                // fixed at compile time (2 * NCH units per step)
+                const int NG = FHP / PK;
+                for (int gi0 = 0; gi0 < NG; gi0 += 2) {
+#pragma unroll
+                    for (int dg = 0; dg < 2; ++dg) {
+                        const int gi = gi0 + dg;
+                        if (gi >= NG) break;
+#pragma unroll
+                        for (int ci = 0; ci < NCH; ++ci) {
+                            const int u = dg * NCH + ci;
+                            const int nci = ci + 1 < NCH ? ci + 1 : 0;
+                            const int ngi = ci + 1 < NCH ? gi : gi + 1;
+                            if (ngi < NG) load_unit(o[(u + 1) & 1], nci, PK * ngi);
+                            mfmas_unit(o[u & 1], ci, gi);
+                        }
+                    }
+                }
+            }
+        } else if constexpr (FHT > 0 && FHK > 0) {
             // B operands kept in registers: one row of lookahead
             Ops o[2];
             full_a(o[0]);
@@ -660,17 +805,17 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     }
 }
 
-template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL>
+template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL, int PK>
 static hipError_t launch_mfma(const Plan &p, const void *x, const void *w, const void *bias,
                               void *y, hipStream_t st) {
     if (p.lds_bytes > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL>),
+            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL, 1, PK>),
             hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL>), dim3(p.grid),
-                       dim3(MfmaTile<CS, NB, NFRAG>::NT), p.lds_bytes, st,
+    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL, 1, PK>), dim3(p.grid),
+                       dim3(MfmaTile<CS, NB, NFRAG, PK>::NT), p.lds_bytes, st,
                        (const uint16_t *)x, (const uint16_t *)w, (const float *)bias,
                        (uint16_t *)y, p.s, p.aux0, p.aux1, nullptr, nullptr, 0);
     return hipGetLastError();
@@ -704,25 +849,32 @@ static hipError_t launch_mfma_bn(const Plan &p, const void *x, const void *w, co
     return hipGetLastError();
 }
 
-template <int CS, int NB, int NFRAG>
+template <int CS, int NB, int NFRAG, int PK>
 static int mfma_lds_bytes(const Shape &s) {
-    using T = MfmaTile<CS, NB, NFRAG>;
+    using T = MfmaTile<CS, NB, NFRAG, PK>;
     const int XR = 16 + s.FH - 1;
     const int xt = CS * XR * T::PITCH;
-    const int zt = CS * s.FH * NFRAG * T::ZLEN;
+    const int fhp = (s.FH + PK - 1) / PK * PK;
+    const int zt = PK == 1 ? CS * s.FH * NFRAG * T::ZLEN : CS * fhp * T::ZS;
     const int ot = 16 * T::ORS;
     return 2 * (xt + zt + ot);
 }
 
 struct MfmaEntry {
-    int dtype, cs, nb, nfrag, fhk, fht, al;
+    int dtype, cs, nb, nfrag, fhk, fht, al, pk;
     LaunchFn fn;
     int (*lds)(const Shape &);
 };
 
-#define MFA(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_, AL_)                                      \
-    {DTE, CS_, NB_, NF_, FHK_, FHT_, AL_, launch_mfma<DTT, CS_, NB_, NF_, FHK_, FHT_, AL_>, \
-     mfma_lds_bytes<CS_, NB_, NF_>}
+#define MFA(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_, AL_)                                 \
+    {DTE,      CS_, NB_, NF_, FHK_, FHT_, AL_, 1, launch_mfma<DTT, CS_, NB_, NF_, FHK_, FHT_, AL_, 1>, \
+     mfma_lds_bytes<CS_, NB_, NF_, 1>}
+// row packing: PK filter rows per MFMA, J windows of 32 / PK columns
+#define MFP(DTE, DTT, CS_, NB_, J_, FHK_, FHT_, PK_)                                   \
+    {DTE,      CS_, NB_, J_, FHK_, FHT_, true, PK_,                                     \
+     launch_mfma<DTT, CS_, NB_, J_, FHK_, FHT_, true, PK_>, mfma_lds_bytes<CS_, NB_, J_, PK_>}
+#define MFPD(CS_, NB_, J_, FHK_, FHT_, PK_) \
+    MFP(DT_F16, F16, CS_, NB_, J_, FHK_, FHT_, PK_), MFP(DT_BF16, BF16, CS_, NB_, J_, FHK_, FHT_, PK_)
 #define MF(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_) MFA(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_, false)
 
 // Each configuration twice: A windows read from LDS by every lane first
@@ -737,6 +889,16 @@ struct MfmaEntry {
 // planner falls back to 4 channels when the 8-channel tile exceeds 64 KiB of
 // LDS (tall filters), to keep several workgroups per CU.
 static const MfmaEntry kMfma[] = {
+    // Row packing first: 31x31 bf16 on 32x56x56x128 ran 72.5 us with two
+    // rows per MFMA against 82 with four and 88 with one; 7x7 fp16 on
+    // 64x56x56x96 37.1 us with four rows (B kept) against 39.7 with one and
+    // 41.4 with four rows and B read from LDS.  Eight-channel slices (140 KB
+    // of LDS, one workgroup per CU: 79.9 us) and 32-column strips (95 us)
+    // were slower on the 31x31 layer; they stay for the tuning choices and
+    // for outputs that a 64-column strip would pad more.
+    MFPD(4, 4, 3, 0, 31, 2), MFPD(8, 2, 3, 8, 7, 4),
+    MFPD(4, 4, 6, 0, 31, 4), MFPD(8, 2, 2, 8, 7, 2),
+    MFPD(8, 4, 3, 0, 31, 2), MFPD(4, 2, 3, 0, 31, 2), MFPD(8, 2, 3, 0, 7, 4),
     // compile-time filter heights of the common square filters
     MF2D(8, 4, 1, 8, 7),
     MF2D(4, 4, 2, 0, 31),
@@ -762,6 +924,8 @@ static const MfmaEntry kMfma[] = {
 #undef MF2
 #undef MF
 #undef MFA
+#undef MFPD
+#undef MFP
 
 // The fused prologue: two fp16 parts or three bf16 parts of U, for filters
 // of at most two fragments; FHK = 8 keeps the B operands of filters of up
@@ -802,9 +966,11 @@ bool plan_mfma(Plan &p) {
     if (p.s.S != 1 || p.s.D != 1) return false;
     // tuning choices: mfma_cs=4|8|16 the channel slice, mfma_al=0|1 A
     // windows by DPP row shift / from LDS for every lane, mfma_nb=2|4 strips
-    // of 32 / 64 output columns
+    // of 32 / 64 output columns, mfma_pk=1|2|4 filter rows per MFMA,
+    // mfma_fhk=0|1 B operands read from LDS / kept in registers
     const int want_cs = tune_int("mfma_cs", 0), want_al = tune_int("mfma_al", -1),
-              want_nb = tune_int("mfma_nb", 0);
+              want_nb = tune_int("mfma_nb", 0), want_pk = tune_int("mfma_pk", 0),
+              want_fhk = tune_int("mfma_fhk", -1);
     const int nfrag = (p.s.FW + 15) / 16;
     const int nb_pref = want_nb ? want_nb : strip_blocks(p.s, nfrag);
     const MfmaEntry *e = nullptr;
@@ -813,19 +979,25 @@ bool plan_mfma(Plan &p) {
         for (const auto &k : kMfma) {
             if ((pass == 0) != (k.nb == nb_pref)) continue;
             if (want_nb && k.nb != want_nb) continue;
-            if (k.dtype != p.dtype || k.nfrag != nfrag || p.s.C % k.cs != 0) continue;
+            if (want_pk && k.pk != want_pk) continue;
+            if (want_fhk >= 0 && (k.fhk > 0) != (want_fhk > 0)) continue;
+            // windows per output block: fragments of 16 taps, or with row
+            // packing the KW-column windows that span 16 + FW - 1 columns
+            const int need = k.pk == 1 ? nfrag : (15 + p.s.FW + 32 / k.pk - 1) / (32 / k.pk);
+            if (k.pk > 1 && p.s.FH > 32) continue;
+            if (k.dtype != p.dtype || k.nfrag != need || p.s.C % k.cs != 0) continue;
             if (k.fhk && p.s.FH > k.fhk) continue;
             if (k.fht && p.s.FH != k.fht) continue;
             if (want_cs && k.cs != want_cs) continue;
             if (want_al >= 0 && k.al != want_al) continue;
-            const int need = k.lds(p.s);
+            const int bytes = k.lds(p.s);
             // 16-channel slices run one 8-wavefront workgroup per CU; narrower
             // ones aim for at least two per CU unless nothing else fits
             const bool last = k.cs == 4 || want_cs;
             const int cap = k.cs == 16 || last ? 160 * 1024 : 64 * 1024;
-            if (need <= cap) {
+            if (bytes <= cap) {
                 e = &k;
-                lds = need;
+                lds = bytes;
                 break;
             }
         }
@@ -849,11 +1021,17 @@ bool plan_mfma(Plan &p) {
     p.grid = (uint32_t)blocks;
     p.lds_bytes = lds;
     p.launch = e->fn;
-    snprintf(p.desc, sizeof(p.desc),
-             "mfma: 16x16x32 banded GEMM, strips of %d cols x %d ch walked 16 rows at a "
-             "time, %d fragment(s) of 16 taps, A by %s, LDS %d B, %u x %d",
-             16 * e->nb, e->cs, nfrag, e->al ? "LDS reads" : "DPP row shift", lds, p.grid,
-             p.block);
+    if (e->pk > 1)
+        snprintf(p.desc, sizeof(p.desc),
+                 "mfma: 16x16x32 banded GEMM, %d filter rows per MFMA (%d windows of %d "
+                 "cols), strips of %d cols x %d ch walked 16 rows at a time, LDS %d B, %u x %d",
+                 e->pk, e->nfrag, 32 / e->pk, 16 * e->nb, e->cs, lds, p.grid, p.block);
+    else
+        snprintf(p.desc, sizeof(p.desc),
+                 "mfma: 16x16x32 banded GEMM, strips of %d cols x %d ch walked 16 rows at a "
+                 "time, %d fragment(s) of 16 taps, A by %s, LDS %d B, %u x %d",
+                 16 * e->nb, e->cs, nfrag, e->al ? "LDS reads" : "DPP row shift", lds, p.grid,
+                 p.block);
     return true;
 }
 

@@ -1,18 +1,22 @@
 """GPU numerics beyond the tolerance bound: what the matrix cores' rounding,
 fp16 / bf16 subnormal inputs and non-finite inputs do, through the C ABI.
 
-* The matrix-core error bound (one fp32 chain per output tile) assumes that
+* The matrix-core error bound (one fp32 chain per output tile) rests on how
   one v_mfma_f32_16x16x32_{f16,bf16} adds its 32 products to the accumulator
-  with a single rounding.  The filter gradient is the one pass whose output
-  stays fp32, so it shows the instruction's rounding directly.
+  (the measured model in test_mfma_product_grouping).  The filter gradient is
+  the one pass whose output stays fp32, so it shows the instruction's
+  rounding directly.
 * Subnormal fp16 inputs next to normal ones must not cost more than the bound
   (the paired-tap column stream and the matrix cores both take fp16 pairs).
 * Non-finite inputs: the definition sends an Inf or NaN input to exactly the
   outputs whose taps read it.  The vector families do the same.  The matrix
-  cores multiply every input column of a tile's window by the banded filter,
-  zeros included, so an output may also turn NaN when its 16-column block's
-  input window holds a non-finite value in a row its filter rows read.
+  cores multiply every input column of a tile's K windows by the banded
+  filter, zeros included, so an output may also turn NaN when one of its
+  16-column block's windows holds a non-finite value in a row its filter
+  rows read (rows past the filter in a packed group have zero inputs).
 """
+import re
+
 import numpy as np
 import pytest
 import torch
@@ -223,21 +227,24 @@ NONFINITE = [
 FAMILIES = ["direct", "rowwin", "ldstile", "mfma"]
 
 
-def _mfma_reach(shape, bad, P):
+def _mfma_reach(shape, bad, P, desc):
     """Outputs the matrix-core family may turn NaN for the non-finite inputs
     `bad` (list of (ih, iw)): the rows whose filter rows read ih, and the
-    16-column output blocks whose input window (16 * (block + fragments) + 16
-    columns from the block's first output) holds iw."""
+    16-column output blocks whose K windows hold iw.  One filter row per
+    MFMA: windows of 32 columns at 16-column steps, 16 * (fragments + 1)
+    columns from the block's first input column; PK rows per MFMA: J
+    windows of 32 / PK columns (the plan description names both)."""
     N, H, W, C, FH, FW, S, D, _ = shape
     OH, OW = oracle.out_dim(H, FH, S, D, P), oracle.out_dim(W, FW, S, D, P)
-    nfrag = (FW + 15) // 16
+    m = re.search(r"(\d+) windows of (\d+) cols", desc)
+    span = int(m.group(1)) * int(m.group(2)) if m else 16 * ((FW + 15) // 16) + 16
     mask = np.zeros((OH, OW), bool)
     for ih, iw in bad:
         rows = [oh for oh in range(OH) if 0 <= ih - (oh - P) < FH]
         for oh in rows:
             for ow in range(OW):
                 b0 = 16 * (ow // 16) - P
-                if b0 <= iw < b0 + 16 * nfrag + 16:
+                if b0 <= iw < b0 + span:
                     mask[oh, ow] = True
     return mask
 
@@ -282,8 +289,9 @@ def test_nonfinite_inputs(case):
         keep = fin.copy()
         if fam == "mfma":
             reach = np.zeros_like(fin)
+            desc = describe(shape, fmt, fam)
             for ih, iw, c, _ in bad:
-                reach[0, :, :, c] |= _mfma_reach(shape, [(ih, iw)], P)
+                reach[0, :, :, c] |= _mfma_reach(shape, [(ih, iw)], P, desc)
             # inside the reach an output is NaN or else checked like the rest
             assert not np.isnan(yv[fin & ~reach]).any(), fam
             keep &= ~(reach & np.isnan(yv))

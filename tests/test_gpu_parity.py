@@ -433,6 +433,48 @@ def test_mfma_strip_widths(nb, monkeypatch):
             assert_matches_oracle(y, x, w, b, shape, fmt, f"mfma nb{nb} {shape}")
 
 
+ROW_PACKED = {  # tuning choice -> (dtype, FH, FW) the compiled entries cover
+    "mfma_pk=2": [("bf16", 31, 31), ("f16", 31, 25), ("f16", 7, 7), ("bf16", 7, 9)],
+    "mfma_pk=4": [("f16", 31, 31), ("bf16", 31, 27), ("f16", 7, 7), ("bf16", 7, 5)],
+    "mfma_pk=2,mfma_cs=8": [("bf16", 31, 31), ("f16", 31, 19)],
+    "mfma_pk=2,mfma_nb=2": [("bf16", 31, 31), ("f16", 31, 33)],
+    "mfma_pk=4,mfma_fhk=0": [("f16", 7, 7), ("bf16", 7, 9)],
+}
+
+
+@pytest.mark.parametrize("tune", sorted(ROW_PACKED))
+def test_mfma_row_packing(tune, monkeypatch):
+    """Filter rows packed 2 or 4 to an MFMA (forced through the mfma_pk
+    tuning choice, with the channel slice, strip width and kept-B choices
+    of each compiled entry) against the oracle: 7- and 31-row filters (the
+    last group has PK - FH mod PK rows of zero taps), filter widths that need
+    the same number of windows, ragged strips and row blocks, images shorter
+    than the filter, several channel slices."""
+    monkeypatch.setenv("DWCONV_TUNE", tune)
+    pk = int(tune.split(",")[0].split("=")[1])
+    rng = np.random.default_rng(70 + len(tune))
+    for fmt, FH, FW in ROW_PACKED[tune]:
+        for (N, H, W, C) in [(1, 23, 37, 16), (2, 9, 70, 8), (1, 40, 17, 24), (1, 56, 56, 8)]:
+            shape = (N, H, W, C, FH, FW, 1, 1, FH // 2)
+            assert supported(shape, fmt, "mfma"), shape
+            wl = synth.Workload("mfma", fmt, *shape, ("normal", 0.0, 1.0),
+                                ("normal", 0.0, 1.0 / (FH * FW)), ("uniform", -0.1, 0.1),
+                                int(rng.integers(0, 2**31)))
+            x, w, b = make_inputs(wl)
+            h = dw.dwconv_create_variant(*shape, fmt, "mfma")
+            desc = dw.dwconv_plan_describe(h)
+            dw.dwconv_destroy(h)
+            assert f"{pk} filter rows per MFMA" in desc, desc
+            if "mfma_cs=8" in tune:
+                assert "x 8 ch" in desc, desc
+            if "mfma_nb=2" in tune:
+                assert "strips of 32 cols" in desc, desc
+            say(f"[gpu] mfma {tune}, {fmt} shape {shape}")
+            y, used = run(x, w, b, shape, fmt, "mfma", guard=512)
+            assert used == "mfma", used
+            assert_matches_oracle(y, x, w, b, shape, fmt, f"mfma {tune} {shape}")
+
+
 # wide filters on the matrix cores: the compiled 31-row entry, ragged row
 # blocks and strips, outputs narrower than one strip, non-square filters of
 # 17 to 33 taps, one output row
