@@ -153,7 +153,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     constexpr int NCH = CS / NW;            // channels per wavefront
     constexpr int NWIN = T::NWIN;           // distinct A windows per filter row / group
     static_assert(FHK == 0 || NFRAG == 1 || PK > 1, "kept B operands: one fragment");
-    static_assert(FHT == 0 || FHK == 0 || FHT <= FHK, "kept B operands cover the filter");
+    static_assert(FHT == 0 || FHK == 0 || FHT <= FHK || PK > 1, "kept B operands cover the filter");
     static_assert(NS == 1 || (AL && FHT == 0 && NFRAG <= 2 && NS <= 3 && PK == 1),
                   "the fused prologue: LDS-read A windows, runtime filter height");
     static_assert(PK == 1 || ((PK == 2 || PK == 4) && AL && NS == 1 && (FHK == 0 || FHT > 0)),
@@ -184,7 +184,11 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const int ow0 = ct * 16 * NB;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform, and visibly so: the bias loads indexed by it become
+    // scalar loads, which no MFMA then waits on together with the ring refill
+    // loads (a vector load of the bias made the first row block's MFMAs wait
+    // for the refill of the next block)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint16_t *xn = x + (long long)n * s.H * s.W * s.C + c0;
     const int nrb = (s.OH + 15) / 16;
     const int WC = s.W * s.C;  // elements of one image row (< 2^31)
@@ -370,8 +374,10 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
 #pragma unroll
         for (int q = 0; q < 4; ++q) b[q] = __builtin_amdgcn_alignbit(d[q + 1], d[q], bsh);
     };
-    // row packing with kept B operands: every group's J windows
-    constexpr int NGK = PK > 1 && FHK > 0 ? (FHT + PK - 1) / PK : 1;
+    // row packing with kept B operands: the J windows of the groups that
+    // start below filter row FHK (all of them when FHK >= FHT), the others
+    // read from LDS for each row block
+    constexpr int NGK = PK > 1 && FHK > 0 ? ((FHK < FHT ? FHK : FHT) + PK - 1) / PK : 1;
     u32x4 Bp[PK > 1 && FHK > 0 ? NCH : 1][NGK][PK > 1 && FHK > 0 ? NFRAG : 1];
     if constexpr (PK > 1 && FHK > 0) {
 #pragma unroll
@@ -555,7 +561,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
             slotp %= XR;
             struct OpsU {
                 u32x4 A[NWIN];
-                uint32_t R[FHK > 0 ? 1 : NFRAG][5];
+                uint32_t R[FHK > 0 && FHK >= FHT ? 1 : NFRAG][5];
             };
             auto load_unit = [&](OpsU &o, int ci, int fh0) {
                 int sl = slotp + fh0;
@@ -569,13 +575,15 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     const u32x4 a = *reinterpret_cast<const u32x4 *>(xr + KW * h);
                     o.A[h] = ok ? a : (u32x4){0u, 0u, 0u, 0u};
                 }
-                if constexpr (FHK == 0) {
+                if constexpr (!(FHK > 0 && FHK >= FHT)) {
+                    if (FHK == 0 || fh0 >= PK * NGK) {
 #pragma unroll
-                    for (int j = 0; j < NFRAG; ++j) {
-                        const uint32_t *zd =
-                            reinterpret_cast<const uint32_t *>(zc[ci] + fh0 * ZS + KW * j);
+                        for (int j = 0; j < NFRAG; ++j) {
+                            const uint32_t *zd =
+                                reinterpret_cast<const uint32_t *>(zc[ci] + fh0 * ZS + KW * j);
 #pragma unroll
-                        for (int q = 0; q < 5; ++q) o.R[j][q] = zd[q];
+                            for (int q = 0; q < 5; ++q) o.R[j][q] = zd[q];
+                        }
                     }
                 }
             };
@@ -583,12 +591,12 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                 u32x4 bb[NFRAG];
 #pragma unroll
                 for (int j = 0; j < NFRAG; ++j) {
-                    if constexpr (FHK > 0) {
+                    if (FHK > 0 && gi < NGK) {
                         bb[j] = Bp[ci][0][j];
 #pragma unroll
                         for (int k = 1; k < NGK; ++k)
                             if (gi == k) bb[j] = Bp[ci][k][j];
-                    } else {
+                    } else if constexpr (!(FHK > 0 && FHK >= FHT)) {
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
                             bb[j][q] = __builtin_amdgcn_alignbit(o.R[j][q + 1], o.R[j][q], bsh);
@@ -890,13 +898,17 @@ struct MfmaEntry {
 // LDS (tall filters), to keep several workgroups per CU.
 static const MfmaEntry kMfma[] = {
     // Row packing first: 31x31 bf16 on 32x56x56x128 ran 72.5 us with two
-    // rows per MFMA against 82 with four and 88 with one; 7x7 fp16 on
-    // 64x56x56x96 37.1 us with four rows (B kept) against 39.7 with one and
-    // 41.4 with four rows and B read from LDS.  Eight-channel slices (140 KB
-    // of LDS, one workgroup per CU: 79.9 us) and 32-column strips (95 us)
-    // were slower on the 31x31 layer; they stay for the tuning choices and
-    // for outputs that a 64-column strip would pad more.
-    MFPD(4, 4, 3, 0, 31, 2), MFPD(8, 2, 3, 8, 7, 4),
+    // rows per MFMA against 82 with four and 88 with one, and 68.7 us with
+    // the B operands of the first 9 of its 16 row groups kept in registers
+    // (252 registers; LDS, not registers, holds it at two workgroups per CU;
+    // 6 groups: 71.4 us); 7x7 fp16 on 64x56x56x96 37.1 us with four rows (B
+    // kept) against 39.7 with one and 41.4 with four rows and B read from
+    // LDS.  Eight-channel slices (140 KB of LDS, one workgroup per CU: 79.9
+    // us) and 32-column strips (95 us) were slower on the 31x31 layer; they
+    // stay for the tuning choices and for outputs that a 64-column strip
+    // would pad more.
+    MFPD(4, 4, 3, 18, 31, 2), MFPD(8, 2, 3, 8, 7, 4),
+    MFPD(4, 4, 3, 0, 31, 2),
     MFPD(4, 4, 6, 0, 31, 4), MFPD(8, 2, 2, 8, 7, 2),
     MFPD(8, 4, 3, 0, 31, 2), MFPD(4, 2, 3, 0, 31, 2), MFPD(8, 2, 3, 0, 7, 4),
     // compile-time filter heights of the common square filters
@@ -967,7 +979,8 @@ bool plan_mfma(Plan &p) {
     // tuning choices: mfma_cs=4|8|16 the channel slice, mfma_al=0|1 A
     // windows by DPP row shift / from LDS for every lane, mfma_nb=2|4 strips
     // of 32 / 64 output columns, mfma_pk=1|2|4 filter rows per MFMA,
-    // mfma_fhk=0|1 B operands read from LDS / kept in registers
+    // mfma_fhk=0|1|F B operands read from LDS / kept in registers / kept
+    // for the filter rows below F
     const int want_cs = tune_int("mfma_cs", 0), want_al = tune_int("mfma_al", -1),
               want_nb = tune_int("mfma_nb", 0), want_pk = tune_int("mfma_pk", 0),
               want_fhk = tune_int("mfma_fhk", -1);
@@ -980,13 +993,15 @@ bool plan_mfma(Plan &p) {
             if ((pass == 0) != (k.nb == nb_pref)) continue;
             if (want_nb && k.nb != want_nb) continue;
             if (want_pk && k.pk != want_pk) continue;
-            if (want_fhk >= 0 && (k.fhk > 0) != (want_fhk > 0)) continue;
+            if (want_fhk >= 0 &&
+                (want_fhk <= 1 ? (k.fhk > 0) != (want_fhk > 0) : k.fhk != want_fhk))
+                continue;
             // windows per output block: fragments of 16 taps, or with row
             // packing the KW-column windows that span 16 + FW - 1 columns
             const int need = k.pk == 1 ? nfrag : (15 + p.s.FW + 32 / k.pk - 1) / (32 / k.pk);
             if (k.pk > 1 && p.s.FH > 32) continue;
             if (k.dtype != p.dtype || k.nfrag != need || p.s.C % k.cs != 0) continue;
-            if (k.fhk && p.s.FH > k.fhk) continue;
+            if (k.fhk && k.pk == 1 && p.s.FH > k.fhk) continue;
             if (k.fht && p.s.FH != k.fht) continue;
             if (want_cs && k.cs != want_cs) continue;
             if (want_al >= 0 && k.al != want_al) continue;

@@ -439,6 +439,7 @@ ROW_PACKED = {  # tuning choice -> (dtype, FH, FW) the compiled entries cover
     "mfma_pk=2,mfma_cs=8": [("bf16", 31, 31), ("f16", 31, 19)],
     "mfma_pk=2,mfma_nb=2": [("bf16", 31, 31), ("f16", 31, 33)],
     "mfma_pk=4,mfma_fhk=0": [("f16", 7, 7), ("bf16", 7, 9)],
+    "mfma_pk=2,mfma_fhk=0": [("bf16", 31, 31), ("f16", 31, 21)],
 }
 
 
