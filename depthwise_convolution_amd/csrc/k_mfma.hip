@@ -911,6 +911,14 @@ static const MfmaEntry kMfma[] = {
     MFPD(4, 4, 3, 0, 31, 2),
     MFPD(4, 4, 6, 0, 31, 4), MFPD(8, 2, 2, 8, 7, 2),
     MFPD(8, 4, 3, 0, 31, 2), MFPD(4, 2, 3, 0, 31, 2), MFPD(8, 2, 3, 0, 7, 4),
+    // row packing, any filter height up to 32: four rows for filters of at
+    // most 9 taps, two rows for 10 to 17 and for 18 to 33 taps (on the f16
+    // sweep maps 1.02-1.45x the speed of one row per MFMA at F = 7, 9, 17,
+    // 21, 25, 31; 0.97-0.98 at F = 13 and 0.89 at F = 9 on 128x32x32x1024)
+    MFPD(8, 4, 3, 0, 0, 4), MFPD(8, 4, 2, 0, 0, 2), MFPD(8, 4, 3, 0, 0, 2),
+    MFPD(4, 4, 3, 0, 0, 4), MFPD(4, 4, 2, 0, 0, 2), MFPD(4, 4, 3, 0, 0, 2),
+    MFPD(8, 2, 3, 0, 0, 4), MFPD(8, 2, 2, 0, 0, 2), MFPD(8, 2, 3, 0, 0, 2),
+    MFPD(4, 2, 3, 0, 0, 4), MFPD(4, 2, 2, 0, 0, 2), MFPD(4, 2, 3, 0, 0, 2),
     // compile-time filter heights of the common square filters
     MF2D(8, 4, 1, 8, 7),
     MF2D(4, 4, 2, 0, 31),

@@ -434,8 +434,12 @@ def test_mfma_strip_widths(nb, monkeypatch):
 
 
 ROW_PACKED = {  # tuning choice -> (dtype, FH, FW) the compiled entries cover
-    "mfma_pk=2": [("bf16", 31, 31), ("f16", 31, 25), ("f16", 7, 7), ("bf16", 7, 9)],
-    "mfma_pk=4": [("f16", 31, 31), ("bf16", 31, 27), ("f16", 7, 7), ("bf16", 7, 5)],
+    "mfma_pk=2": [("bf16", 31, 31), ("f16", 31, 25), ("f16", 7, 7), ("bf16", 7, 9),
+                  ("bf16", 13, 13), ("f16", 21, 25), ("bf16", 32, 17), ("f16", 1, 31)],
+    "mfma_pk=4": [("f16", 31, 31), ("bf16", 31, 27), ("f16", 7, 7), ("bf16", 7, 5),
+                  ("f16", 5, 5), ("bf16", 9, 9), ("f16", 3, 7), ("bf16", 2, 3)],
+    "mfma_pk=2,mfma_cs=4,mfma_nb=2": [("f16", 9, 17), ("bf16", 15, 21)],
+    "mfma_pk=4,mfma_cs=4": [("bf16", 6, 9), ("f16", 11, 8)],
     "mfma_pk=2,mfma_cs=8": [("bf16", 31, 31), ("f16", 31, 19)],
     "mfma_pk=2,mfma_nb=2": [("bf16", 31, 31), ("f16", 31, 33)],
     "mfma_pk=4,mfma_fhk=0": [("f16", 7, 7), ("bf16", 7, 9)],
@@ -456,7 +460,7 @@ def test_mfma_row_packing(tune, monkeypatch):
     rng = np.random.default_rng(70 + len(tune))
     for fmt, FH, FW in ROW_PACKED[tune]:
         for (N, H, W, C) in [(1, 23, 37, 16), (2, 9, 70, 8), (1, 40, 17, 24), (1, 56, 56, 8)]:
-            shape = (N, H, W, C, FH, FW, 1, 1, FH // 2)
+            shape = (N, H, W, C, FH, FW, 1, 1, max(FH, FW) // 2)
             assert supported(shape, fmt, "mfma"), shape
             wl = synth.Workload("mfma", fmt, *shape, ("normal", 0.0, 1.0),
                                 ("normal", 0.0, 1.0 / (FH * FW)), ("uniform", -0.1, 0.1),
@@ -466,8 +470,9 @@ def test_mfma_row_packing(tune, monkeypatch):
             desc = dw.dwconv_plan_describe(h)
             dw.dwconv_destroy(h)
             assert f"{pk} filter rows per MFMA" in desc, desc
-            if "mfma_cs=8" in tune:
-                assert "x 8 ch" in desc, desc
+            for cs in (4, 8):
+                if f"mfma_cs={cs}" in tune:
+                    assert f"x {cs} ch" in desc, desc
             if "mfma_nb=2" in tune:
                 assert "strips of 32 cols" in desc, desc
             say(f"[gpu] mfma {tune}, {fmt} shape {shape}")
