@@ -146,15 +146,42 @@ FAMILY_SOURCES = {"direct": ("k_direct.hip",), "rowwin": ("k_rowwin.hip",),
                   "bwf": ("k_bwf.hip",), "bwf_mfma": ("k_bwf_mfma.hip", "k_bwf.hip")}
 
 
+def code_only(text):
+    """C/C++ source without its comments, whitespace runs collapsed: what a
+    change to the compiled code changes (string and character literals are
+    kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_sources_hash(variant):
-    """Hash of one kernel family's source file and the headers every family
-    includes; counter figures stored under profiles/ are reported only while
-    it matches the hash they were taken with."""
+    """Hash of the code (comments and layout left out) of one kernel family's
+    source file and the headers every family includes; counter figures stored
+    under profiles/ are reported only while it matches the hash they were
+    taken with."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "depthwise_convolution_amd", "csrc")
     for f in ("dw_common.h", "plan.h") + FAMILY_SOURCES[variant]:
         h.update(f.encode())
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        h.update(code_only(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -37,6 +37,12 @@
 // a fixed per-lane offset, with the band's zeros built in; the lane reads
 // them as five aligned dwords and a 16-bit funnel shift.
 //
+// Row packing (the default for filters of at most 32 rows and 33 taps): a
+// banded fragment fills only FW of each column's 32 K entries, so the K of
+// one MFMA instead holds 2 or 4 filter rows of 16 or 8 input columns each;
+// the kernel comment below gives the operand layout.  Fewer MFMAs and one A
+// read per group of rows instead of one per row.
+//
 // The partial sums stay fp32 in the MFMA accumulators for the whole filter,
 // seeded once with the bias.  How one MFMA adds its products was measured on
 // gfx950 (the same for fp16 and bf16): the 32 products form four groups of 8
@@ -45,8 +51,9 @@
 // group sums and the accumulator are added exactly and rounded once, to
 // nearest even.  One MFMA therefore errs by less than 7 * 2^-24 * sum|p| of
 // its own products plus one rounding of its result, and a chain of at most
-// 64 MFMAs (FH <= 32, two fragments) by less than
-// (7 + 64) * 2^-24 * sum|x*w| < 1e-5 * sum|x*w|.  The epilogue rounds once to
+// 64 MFMAs (FH <= 32, two fragments; with row packing at most 48) by less
+// than (7 + 64) * 2^-24 * sum|x*w| < 1e-5 * sum|x*w|.  Each group of 8
+// consecutive k lies in one filter row, packed or not.  The epilogue rounds once to
 // fp16/bf16 and goes through LDS so that the stores are whole channel
 // vectors of NHWC pixels, masked at the ragged right and bottom edges.
 #include "plan.h"

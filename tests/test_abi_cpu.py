@@ -411,3 +411,14 @@ def test_fused_prologue_family(shape, fmt, family):
     assert desc.startswith(family), desc
     if family.startswith("mfma"):
         assert ("2 fp16 parts" if fmt == "f16" else "3 bf16 parts") in desc, desc
+
+
+def test_counter_hash_ignores_comments_only():
+    """The stored counter figures are keyed by a hash of the kernel sources'
+    code: comments and layout do not change it, code and string literals do."""
+    import bench
+    src = 'int a = 1; // x\n/* y */ const char *s = "p // q /* r */";'
+    assert bench.code_only(src) == 'int a = 1; const char *s = "p // q /* r */";'
+    assert bench.code_only("int  a =\n 1; /* z */") == bench.code_only("int a = 1;")
+    assert bench.code_only("int a = 1;") != bench.code_only("int a = 2;")
+    assert bench.code_only('f("a");') != bench.code_only('f("b");')
