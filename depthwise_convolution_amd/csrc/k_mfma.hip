@@ -61,6 +61,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 namespace dw {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -425,7 +427,10 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
         y + n * yimg + c0, (short)0, (int)(uint32_t)(2 * (yimg - c0)), 0x00020000);
 
-    for (int rb = 0; rb < nrb; ++rb) {
+    // One row block: rb, and NBC = nbc column blocks per MFMA row set (NB, or
+    // NB / 2 for a half block).  The last block is a separate call, so that
+    // the loop over the others carries none of its code or registers.
+    auto block = [&](int rb, auto nbc) {
         if (rb) __syncthreads();  // ring rows of this block written; output tile free
         // prefetch the 16 rows the next block adds (the rows this block
         // needs are in the ring already)
@@ -436,6 +441,12 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
 
         int slot0 = 16 * rb + t16;  // ring slot of this lane's row at fh = 0
         slot0 %= XR;
+        // Row packing, a block with at most 8 rows left (the last one of a
+        // 56-row map): its 16 MFMA rows are 8 output rows of the first NB/2
+        // column blocks and the same 8 rows of the last NB/2 (one filter band
+        // serves both), so the block takes half the MFMAs.  A row i of such
+        // a block is output row i mod 8, columns shifted by (i / 8) * 8 * NB.
+        constexpr bool half = decltype(nbc)::value < NB;
 
         // One fp32 MFMA chain per output tile, seeded with the bias: a chain
         // of at most 2 * 32 MFMAs stays within 1e-5 * sum|x*w| (one rounding
@@ -563,90 +574,101 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
             // of the next unit are issued before the MFMAs of the current
             // one (two units of operands in registers).  At most 8 groups of
             // 6 windows (FH <= 32, FW <= 33): a chain of at most 48 MFMAs
-            // per tile.
-            int slotp = 16 * rb + t16 + pr;  // ring slot of this lane's row at fh0 = 0
-            slotp %= XR;
-            struct OpsU {
-                u32x4 A[NWIN];
-                uint32_t R[FHK > 0 && FHK >= FHT ? 1 : NFRAG][5];
-            };
-            auto load_unit = [&](OpsU &o, int ci, int fh0) {
-                int sl = slotp + fh0;
-                sl -= sl >= XR ? XR : 0;
-                // rows past FH: zero A entries (the taps there are zero too)
-                const bool full = FHT > 0 && fh0 + PK <= FHT;
-                const bool ok = full || fh0 + pr < FH;
-                const uint16_t *xr = xc[ci] + sl * PITCH;
+            // per tile.  NBC column blocks per MFMA row set: NB, or NB/2 in
+            // a half block (each variant compiled on its own, so neither
+            // carries the other's branches or registers).
+            auto packed_rows = [&](auto nbc) {
+                constexpr int NBC = decltype(nbc)::value;
+                constexpr int NWC = (PK / 2) * (NBC - 1) + NFRAG;  // windows per group
+                int slotp = 16 * rb + (NBC < NB ? (t16 & 7) : t16) + pr;  // lane's ring row
+                slotp %= XR;                                               // at fh0 = 0
+                const int hoff = NBC < NB ? (t16 >> 3) * 8 * NB : 0;      // its column shift
+                struct OpsU {
+                    u32x4 A[NWC];
+                    uint32_t R[FHK > 0 && FHK >= FHT ? 1 : NFRAG][5];
+                };
+                auto load_unit = [&](OpsU &o, int ci, int fh0) {
+                    int sl = slotp + fh0;
+                    sl -= sl >= XR ? XR : 0;
+                    // rows past FH: zero A entries (the taps there are zero too)
+                    const bool full = FHT > 0 && fh0 + PK <= FHT;
+                    const bool ok = full || fh0 + pr < FH;
+                    const uint16_t *xr = xc[ci] + sl * PITCH + hoff;
 #pragma unroll
-                for (int h = 0; h < NWIN; ++h) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(xr + KW * h);
-                    o.A[h] = ok ? a : (u32x4){0u, 0u, 0u, 0u};
-                }
-                if constexpr (!(FHK > 0 && FHK >= FHT)) {
-                    if (FHK == 0 || fh0 >= PK * NGK) {
+                    for (int h = 0; h < NWC; ++h) {
+                        const u32x4 a = *reinterpret_cast<const u32x4 *>(xr + KW * h);
+                        o.A[h] = ok ? a : (u32x4){0u, 0u, 0u, 0u};
+                    }
+                    if constexpr (!(FHK > 0 && FHK >= FHT)) {
+                        if (FHK == 0 || fh0 >= PK * NGK) {
 #pragma unroll
-                        for (int j = 0; j < NFRAG; ++j) {
-                            const uint32_t *zd =
-                                reinterpret_cast<const uint32_t *>(zc[ci] + fh0 * ZS + KW * j);
+                            for (int j = 0; j < NFRAG; ++j) {
+                                const uint32_t *zd = reinterpret_cast<const uint32_t *>(
+                                    zc[ci] + fh0 * ZS + KW * j);
 #pragma unroll
-                            for (int q = 0; q < 5; ++q) o.R[j][q] = zd[q];
+                                for (int q = 0; q < 5; ++q) o.R[j][q] = zd[q];
+                            }
+                        }
+                    }
+                };
+                auto mfmas_unit = [&](const OpsU &o, int ci, int gi) {
+                    u32x4 bb[NFRAG];
+#pragma unroll
+                    for (int j = 0; j < NFRAG; ++j) {
+                        if (FHK > 0 && gi < NGK) {
+                            bb[j] = Bp[ci][0][j];
+#pragma unroll
+                            for (int k = 1; k < NGK; ++k)
+                                if (gi == k) bb[j] = Bp[ci][k][j];
+                        } else if constexpr (!(FHK > 0 && FHK >= FHT)) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                bb[j][q] =
+                                    __builtin_amdgcn_alignbit(o.R[j][q + 1], o.R[j][q], bsh);
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < NFRAG; ++j)
+#pragma unroll
+                        for (int b = 0; b < NBC; ++b)
+                            acc[ci][b] =
+                                MfmaOp<DT>::run(o.A[(PK / 2) * b + j], bb[j], acc[ci][b]);
+                };
+                OpsU o[2];
+                load_unit(o[0], 0, 0);
+                if constexpr (FHT > 0) {
+                    constexpr int NU = (FHT + PK - 1) / PK * NCH;
+#pragma unroll
+                    for (int u = 0; u < NU; ++u) {
+                        if (u + 1 < NU)
+                            load_unit(o[(u + 1) & 1], (u + 1) % NCH, PK * ((u + 1) / NCH));
+                        mfmas_unit(o[u & 1], u % NCH, u / NCH);
+                        // keep the scheduler from hoisting later units' operands
+                        // (and their registers) above this unit's MFMAs
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                } else {
+                    // groups two at a time, so that a unit's operand buffer is
+                    // fixed at compile time (2 * NCH units per step)
+                    const int NG = FHP / PK;
+                    for (int gi0 = 0; gi0 < NG; gi0 += 2) {
+#pragma unroll
+                        for (int dg = 0; dg < 2; ++dg) {
+                            const int gi = gi0 + dg;
+                            if (gi >= NG) break;
+#pragma unroll
+                            for (int ci = 0; ci < NCH; ++ci) {
+                                const int u = dg * NCH + ci;
+                                const int nci = ci + 1 < NCH ? ci + 1 : 0;
+                                const int ngi = ci + 1 < NCH ? gi : gi + 1;
+                                if (ngi < NG) load_unit(o[(u + 1) & 1], nci, PK * ngi);
+                                mfmas_unit(o[u & 1], ci, gi);
+                            }
                         }
                     }
                 }
             };
-            auto mfmas_unit = [&](const OpsU &o, int ci, int gi) {
-                u32x4 bb[NFRAG];
-#pragma unroll
-                for (int j = 0; j < NFRAG; ++j) {
-                    if (FHK > 0 && gi < NGK) {
-                        bb[j] = Bp[ci][0][j];
-#pragma unroll
-                        for (int k = 1; k < NGK; ++k)
-                            if (gi == k) bb[j] = Bp[ci][k][j];
-                    } else if constexpr (!(FHK > 0 && FHK >= FHT)) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            bb[j][q] = __builtin_amdgcn_alignbit(o.R[j][q + 1], o.R[j][q], bsh);
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < NFRAG; ++j)
-#pragma unroll
-                    for (int b = 0; b < NB; ++b)
-                        acc[ci][b] = MfmaOp<DT>::run(o.A[(PK / 2) * b + j], bb[j], acc[ci][b]);
-            };
-            OpsU o[2];
-            load_unit(o[0], 0, 0);
-            if constexpr (FHT > 0) {
-                constexpr int NU = (FHT + PK - 1) / PK * NCH;
-#pragma unroll
-                for (int u = 0; u < NU; ++u) {
-                    if (u + 1 < NU) load_unit(o[(u + 1) & 1], (u + 1) % NCH, PK * ((u + 1) / NCH));
-                    mfmas_unit(o[u & 1], u % NCH, u / NCH);
-                    // keep the scheduler from hoisting later units' operands
-                    // (and their registers) above this unit's MFMAs
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            } else {
-                // groups two at a time, so that a unit's operand buffer is
-                // fixed at compile time (2 * NCH units per step)
-                const int NG = FHP / PK;
-                for (int gi0 = 0; gi0 < NG; gi0 += 2) {
-#pragma unroll
-                    for (int dg = 0; dg < 2; ++dg) {
-                        const int gi = gi0 + dg;
-                        if (gi >= NG) break;
-#pragma unroll
-                        for (int ci = 0; ci < NCH; ++ci) {
-                            const int u = dg * NCH + ci;
-                            const int nci = ci + 1 < NCH ? ci + 1 : 0;
-                            const int ngi = ci + 1 < NCH ? gi : gi + 1;
-                            if (ngi < NG) load_unit(o[(u + 1) & 1], nci, PK * ngi);
-                            mfmas_unit(o[u & 1], ci, gi);
-                        }
-                    }
-                }
-            }
+            packed_rows(nbc);
         } else if constexpr (FHT > 0 && FHK > 0) {
             // B operands kept in registers: one row of lookahead
             Ops o[2];
@@ -773,7 +795,12 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int row = 4 * g + q, col = 16 * b + t16;
+                    int row = 4 * g + q, col = 16 * b + t16;
+                    if (half) {  // D row i: output row i mod 8, block b + (i / 8) NB/2
+                        if (2 * b >= NB) continue;
+                        col += (g >> 1) * 8 * NB;
+                        row &= 7;
+                    }
                     ot[row * ORS + col * OPS + c] =
                         __builtin_bit_cast(uint16_t, DT::narrow(acc[ci][b][q]));
                 }
@@ -817,6 +844,12 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     }
                 }
         }
+    };
+    const bool tailhalf = PK > 1 && s.OH - 16 * (nrb - 1) <= 8;
+    const int nfull = tailhalf ? nrb - 1 : nrb;
+    for (int rb = 0; rb < nfull; ++rb) block(rb, std::integral_constant<int, NB>{});
+    if constexpr (PK > 1) {
+        if (tailhalf) block(nrb - 1, std::integral_constant<int, NB / 2>{});
     }
 }
 

@@ -454,12 +454,15 @@ def test_mfma_row_packing(tune, monkeypatch):
     of each compiled entry) against the oracle: 7- and 31-row filters (the
     last group has PK - FH mod PK rows of zero taps), filter widths that need
     the same number of windows, ragged strips and row blocks, images shorter
-    than the filter, several channel slices."""
+    than the filter, several channel slices; last row blocks of 7, 8 and 9
+    rows and an output of 6 rows (blocks of at most 8 rows take the half
+    form: 8 rows of two column blocks per MFMA row set)."""
     monkeypatch.setenv("DWCONV_TUNE", tune)
     pk = int(tune.split(",")[0].split("=")[1])
     rng = np.random.default_rng(70 + len(tune))
     for fmt, FH, FW in ROW_PACKED[tune]:
-        for (N, H, W, C) in [(1, 23, 37, 16), (2, 9, 70, 8), (1, 40, 17, 24), (1, 56, 56, 8)]:
+        for (N, H, W, C) in [(1, 23, 37, 16), (2, 9, 70, 8), (1, 40, 17, 24), (1, 56, 56, 8),
+                             (1, 6, 45, 8)]:
             shape = (N, H, W, C, FH, FW, 1, 1, max(FH, FW) // 2)
             assert supported(shape, fmt, "mfma"), shape
             wl = synth.Workload("mfma", fmt, *shape, ("normal", 0.0, 1.0),
