@@ -37,7 +37,8 @@
 // a fixed per-lane offset, with the band's zeros built in; the lane reads
 // them as five aligned dwords and a 16-bit funnel shift.
 //
-// Row packing (the default for filters of at most 32 rows and 33 taps): a
+// Row packing (the default for filters of at most 32 rows and 33 taps, and
+// of 34 to 65 taps and at most 64 rows): a
 // banded fragment fills only FW of each column's 32 K entries, so the K of
 // one MFMA instead holds 2 or 4 filter rows of 16 or 8 input columns each;
 // the kernel comment below gives the operand layout.  Fewer MFMAs and one A
@@ -51,7 +52,8 @@
 // group sums and the accumulator are added exactly and rounded once, to
 // nearest even.  One MFMA therefore errs by less than 7 * 2^-24 * sum|p| of
 // its own products plus one rounding of its result, and a chain of at most
-// 64 MFMAs (FH <= 32, two fragments; with row packing at most 48) by less
+// 64 MFMAs (FH <= 32, two fragments; with row packing at most 48, or 64
+// where taller and wider filters fold the chain into an fp32 total) by less
 // than (7 + 64) * 2^-24 * sum|x*w| < 1e-5 * sum|x*w|.  Each group of 8
 // consecutive k lies in one filter row, packed or not.  The epilogue rounds once to
 // fp16/bf16 and goes through LDS so that the stores are whole channel
@@ -107,7 +109,10 @@ struct MfmaTile {
     // PK > 1: one padded filter row -- 16 zeros, the FW taps, zeros -- long
     // enough for the 5 dwords a lane reads from element
     // 16 + KW*j + (8g mod KW) - t16 of its row, a multiple of 8 elements
-    static constexpr int ZS = (18 + KW * NFRAG + 7) / 8 * 8;
+    // (of 4 with four or more windows: 1.2 KB less LDS, which keeps two
+    // workgroups per CU up to 49-row filters)
+    static constexpr int ZS = NFRAG >= 4 ? (18 + KW * NFRAG + 3) / 4 * 4
+                                         : (18 + KW * NFRAG + 7) / 8 * 8;
     static constexpr int NW = CS >= 16 ? 8 : 4;       // wavefronts per workgroup
     static constexpr int NT = 64 * NW;                 // threads per workgroup
     static constexpr int NPAIR = 8 * XW;               // column pairs in 16 rows
@@ -299,6 +304,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     // FH .. FHP-1 are zero ----
     {
         const int zlen = ZT;
+        static_assert(PK == 1 || CS * ZS % 8 == 0, "zero fill in 16-byte stores");
         for (int e = 8 * tid; e < zlen; e += 8 * NT)   // zlen is a multiple of 8
             *reinterpret_cast<u32x4 *>(zt + e) = (u32x4){0u, 0u, 0u, 0u};
         __syncthreads();
@@ -467,11 +473,15 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         // More than two fragments (filters wider than 32 taps): the chain of
         // 16 filter rows (at most 64 MFMAs) is added into a separate fp32
         // total, which the bias seeds, and restarts from zero.
-        constexpr bool FOLD = PK == 1 && (NFRAG > 2 || NS > 1);
+        // Row packing with four or more windows (filters of 34 to 65 taps, up
+        // to 64 rows): the chain of FG row groups (at most 64 MFMAs) is folded
+        // the same way.
+        constexpr bool FOLD = PK == 1 ? (NFRAG > 2 || NS > 1) : (NFRAG >= 4 && FHT == 0);
         // filter rows per folded chain: 16 (three or four fragments), or as
         // many as keep a chain within 64 MFMAs with the prologue's parts
         constexpr int FPR = NS > 1 ? 64 / (NFRAG * NS) : 16;
         constexpr int FP = FPR > 2 ? (FPR & ~1) : 2;
+        constexpr int FG = 64 / NFRAG;  // row groups per folded chain (PK > 1)
         f32x4 tot[FOLD ? NCH : 1][FOLD ? NB : 1];
         auto fold = [&]() {
             if constexpr (FOLD) {
@@ -671,6 +681,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                                 if (ngi < NG) load_unit(o[(u + 1) & 1], nci, PK * ngi);
                                 mfmas_unit(o[u & 1], ci, gi);
                             }
+                            if (FOLD && (gi + 1) % FG == 0) fold();
                         }
                     }
                 }
@@ -968,7 +979,11 @@ static const MfmaEntry kMfma[] = {
     // row packing, any filter height up to 32: four rows for filters of at
     // most 9 taps, two rows for 10 to 17 and for 18 to 33 taps (on the f16
     // sweep maps 1.02-1.45x the speed of one row per MFMA at F = 7, 9, 17,
-    // 21, 25, 31; 0.97-0.98 at F = 13 and 0.89 at F = 9 on 128x32x32x1024)
+    // 21, 25, 31; 0.97-0.98 at F = 13 and 0.89 at F = 9 on 128x32x32x1024);
+    // two rows for 34 to 65 taps and up to 64 rows, folded chains: four
+    // windows fit two workgroups per CU up to 49 rows (80 KB), five run one
+    // per CU (107-155 KB); 1.1-2.1x one row per MFMA at F = 41 and 51
+    MFPD(4, 4, 4, 0, 0, 2), MFPD(4, 4, 5, 0, 0, 2), MFPD(4, 2, 4, 0, 0, 2), MFPD(4, 2, 5, 0, 0, 2),
     MFPD(8, 4, 3, 0, 0, 4), MFPD(8, 4, 2, 0, 0, 2), MFPD(8, 4, 3, 0, 0, 2),
     MFPD(4, 4, 3, 0, 0, 4), MFPD(4, 4, 2, 0, 0, 2), MFPD(4, 4, 3, 0, 0, 2),
     MFPD(8, 2, 3, 0, 0, 4), MFPD(8, 2, 2, 0, 0, 2), MFPD(8, 2, 3, 0, 0, 2),
@@ -1050,8 +1065,15 @@ bool plan_mfma(Plan &p) {
     const int nb_pref = want_nb ? want_nb : strip_blocks(p.s, nfrag);
     const MfmaEntry *e = nullptr;
     int lds = 0;
+    // filters of 34 to 65 taps (four or five packed windows) run at two
+    // workgroups per CU where the tile fits in half the CU's LDS, with the
+    // other strip width if the preferred one does not fit (1.2-1.9x the
+    // speed of one workgroup per CU); otherwise the strip width comes first
+    const bool tall = !want_nb && p.s.FW >= 34 && p.s.FW <= 65;
+    for (int tier = tall ? 0 : 1; tier < 2 && !e; ++tier)
     for (int pass = 0; pass < 2 && !e; ++pass) {
         for (const auto &k : kMfma) {
+            if (tier == 0 && (k.pk == 1 || k.nfrag < 4)) continue;
             if ((pass == 0) != (k.nb == nb_pref)) continue;
             if (want_nb && k.nb != want_nb) continue;
             if (want_pk && k.pk != want_pk) continue;
@@ -1061,7 +1083,9 @@ bool plan_mfma(Plan &p) {
             // windows per output block: fragments of 16 taps, or with row
             // packing the KW-column windows that span 16 + FW - 1 columns
             const int need = k.pk == 1 ? nfrag : (15 + p.s.FW + 32 / k.pk - 1) / (32 / k.pk);
-            if (k.pk > 1 && p.s.FH > 32) continue;
+            // taller filters only where the chain is folded (four or more
+            // windows), and at most 64 rows
+            if (k.pk > 1 && p.s.FH > (k.nfrag >= 4 ? 64 : 32)) continue;
             if (k.dtype != p.dtype || k.nfrag != need || p.s.C % k.cs != 0) continue;
             if (k.fhk && k.pk == 1 && p.s.FH > k.fhk) continue;
             if (k.fht && p.s.FH != k.fht) continue;
@@ -1071,7 +1095,7 @@ bool plan_mfma(Plan &p) {
             // 16-channel slices run one 8-wavefront workgroup per CU; narrower
             // ones aim for at least two per CU unless nothing else fits
             const bool last = k.cs == 4 || want_cs;
-            const int cap = k.cs == 16 || last ? 160 * 1024 : 64 * 1024;
+            const int cap = tier == 0 ? 80 * 1024 : k.cs == 16 || last ? 160 * 1024 : 64 * 1024;
             if (bytes <= cap) {
                 e = &k;
                 lds = bytes;

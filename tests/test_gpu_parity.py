@@ -444,6 +444,11 @@ ROW_PACKED = {  # tuning choice -> (dtype, FH, FW) the compiled entries cover
     "mfma_pk=2,mfma_nb=2": [("bf16", 31, 31), ("f16", 31, 33)],
     "mfma_pk=4,mfma_fhk=0": [("f16", 7, 7), ("bf16", 7, 9)],
     "mfma_pk=2,mfma_fhk=0": [("bf16", 31, 31), ("f16", 31, 21)],
+    # filters of 34 to 65 taps and up to 64 rows: four and five windows with
+    # the chain folded every 16 and 12 row pairs
+    "mfma_pk=2,mfma_cs=4": [("f16", 41, 41), ("bf16", 51, 51), ("f16", 64, 65),
+                            ("bf16", 33, 34), ("f16", 40, 50), ("bf16", 17, 49)],
+    "mfma_pk=2,mfma_cs=4,mfma_nb=2,mfma_fhk=0": [("bf16", 41, 41), ("f16", 51, 51)],
 }
 
 
@@ -453,8 +458,9 @@ def test_mfma_row_packing(tune, monkeypatch):
     tuning choice, with the channel slice, strip width and kept-B choices
     of each compiled entry) against the oracle: 7- and 31-row filters (the
     last group has PK - FH mod PK rows of zero taps), filter widths that need
-    the same number of windows, ragged strips and row blocks, images shorter
-    than the filter, several channel slices; last row blocks of 7, 8 and 9
+    the same number of windows, filters of 34 to 65 taps and up to 64 rows
+    (folded chains), ragged strips and row blocks, images shorter than the
+    filter, several channel slices; last row blocks of 7, 8 and 9
     rows and an output of 6 rows (blocks of at most 8 rows take the half
     form: 8 rows of two column blocks per MFMA row set)."""
     monkeypatch.setenv("DWCONV_TUNE", tune)
