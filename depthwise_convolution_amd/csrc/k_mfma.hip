@@ -168,9 +168,10 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     constexpr int NWIN = T::NWIN;           // distinct A windows per filter row / group
     static_assert(FHK == 0 || NFRAG == 1 || PK > 1, "kept B operands: one fragment");
     static_assert(FHT == 0 || FHK == 0 || FHT <= FHK || PK > 1, "kept B operands cover the filter");
-    static_assert(NS == 1 || (AL && FHT == 0 && NFRAG <= 2 && NS <= 3 && PK == 1),
-                  "the fused prologue: LDS-read A windows, runtime filter height");
-    static_assert(PK == 1 || ((PK == 2 || PK == 4) && AL && NS == 1 && (FHK == 0 || FHT > 0)),
+    static_assert(NS == 1 || (AL && NS <= 3 && (PK > 1 || (FHT == 0 && NFRAG <= 2))),
+                  "the fused prologue: LDS-read A windows; one row per MFMA at a runtime "
+                  "filter height");
+    static_assert(PK == 1 || ((PK == 2 || PK == 4) && AL && (FHK == 0 || FHT > 0)),
                   "row packing: 2 or 4 rows, LDS-read A windows, kept B with a fixed height");
     // FHT > 0: the filter height is a compile-time constant and the
     // filter-row loop is fully unrolled, so the accumulators keep fixed
@@ -473,15 +474,18 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         // More than two fragments (filters wider than 32 taps): the chain of
         // 16 filter rows (at most 64 MFMAs) is added into a separate fp32
         // total, which the bias seeds, and restarts from zero.
-        // Row packing with four or more windows (filters of 34 to 65 taps, up
-        // to 64 rows): the chain of FG row groups (at most 64 MFMAs) is folded
-        // the same way.
-        constexpr bool FOLD = PK == 1 ? (NFRAG > 2 || NS > 1) : (NFRAG >= 4 && FHT == 0);
+        // Row packing where the chain could pass 64 MFMAs (four or more
+        // windows for filters of 34 to 65 taps and up to 64 rows, or the
+        // fused prologue's parts): the chain of FG row groups (at most 64
+        // MFMAs) is folded the same way.
+        constexpr int FHMAX = FHT > 0 ? FHT : NFRAG >= 4 ? 64 : 32;
+        constexpr bool FOLD = PK == 1 ? (NFRAG > 2 || NS > 1)
+                                      : (FHMAX + PK - 1) / PK * NFRAG * NS > 64;
         // filter rows per folded chain: 16 (three or four fragments), or as
         // many as keep a chain within 64 MFMAs with the prologue's parts
         constexpr int FPR = NS > 1 ? 64 / (NFRAG * NS) : 16;
         constexpr int FP = FPR > 2 ? (FPR & ~1) : 2;
-        constexpr int FG = 64 / NFRAG;  // row groups per folded chain (PK > 1)
+        constexpr int FG = 64 / (NFRAG * NS);  // row groups per folded chain (PK > 1)
         f32x4 tot[FOLD ? NCH : 1][FOLD ? NB : 1];
         auto fold = [&]() {
             if constexpr (FOLD) {
@@ -591,7 +595,9 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
             // of the next unit are issued before the MFMAs of the current
             // one (two units of operands in registers).  At most 8 groups of
             // 6 windows (FH <= 32, FW <= 33): a chain of at most 48 MFMAs
-            // per tile.  NBC column blocks per MFMA row set: NB, or NB/2 in
+            // per tile, else folded every FG groups.  With the fused
+            // prologue each A window is read and multiplied once per part of
+            // U.  NBC column blocks per MFMA row set: NB, or NB/2 in
             // a half block (each variant compiled on its own, so neither
             // carries the other's branches or registers).
             auto packed_rows = [&](auto nbc) {
@@ -601,7 +607,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                 slotp %= XR;                                               // at fh0 = 0
                 const int hoff = NBC < NB ? (t16 >> 3) * 8 * NB : 0;      // its column shift
                 struct OpsU {
-                    u32x4 A[NWC];
+                    u32x4 A[NS][NWC];
                     uint32_t R[FHK > 0 && FHK >= FHT ? 1 : NFRAG][5];
                 };
                 auto load_unit = [&](OpsU &o, int ci, int fh0) {
@@ -612,10 +618,13 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     const bool ok = full || fh0 + pr < FH;
                     const uint16_t *xr = xc[ci] + sl * PITCH + hoff;
 #pragma unroll
-                    for (int h = 0; h < NWC; ++h) {
-                        const u32x4 a = *reinterpret_cast<const u32x4 *>(xr + KW * h);
-                        o.A[h] = ok ? a : (u32x4){0u, 0u, 0u, 0u};
-                    }
+                    for (int p = 0; p < NS; ++p)
+#pragma unroll
+                        for (int h = 0; h < NWC; ++h) {
+                            const u32x4 a =
+                                *reinterpret_cast<const u32x4 *>(xr + p * RING + KW * h);
+                            o.A[p][h] = ok ? a : (u32x4){0u, 0u, 0u, 0u};
+                        }
                     if constexpr (!(FHK > 0 && FHK >= FHT)) {
                         if (FHK == 0 || fh0 >= PK * NGK) {
 #pragma unroll
@@ -648,8 +657,10 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     for (int j = 0; j < NFRAG; ++j)
 #pragma unroll
                         for (int b = 0; b < NBC; ++b)
-                            acc[ci][b] =
-                                MfmaOp<DT>::run(o.A[(PK / 2) * b + j], bb[j], acc[ci][b]);
+#pragma unroll
+                            for (int p = 0; p < NS; ++p)
+                                acc[ci][b] = MfmaOp<DT>::run(o.A[p][(PK / 2) * b + j], bb[j],
+                                                             acc[ci][b]);
                 };
                 OpsU o[2];
                 load_unit(o[0], 0, 0);
@@ -660,6 +671,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                         if (u + 1 < NU)
                             load_unit(o[(u + 1) & 1], (u + 1) % NCH, PK * ((u + 1) / NCH));
                         mfmas_unit(o[u & 1], u % NCH, u / NCH);
+                        if (FOLD && (u + 1) % NCH == 0 && (u + 1) / NCH % FG == 0) fold();
                         // keep the scheduler from hoisting later units' operands
                         // (and their registers) above this unit's MFMAs
                         __builtin_amdgcn_sched_barrier(0);
@@ -895,28 +907,30 @@ static hipError_t launch_mfma(const Plan &p, const void *x, const void *w, const
 }
 
 // LDS of a tile with NS rings (the fused prologue's parts of U)
-template <int CS, int NB, int NFRAG, int NS>
+template <int CS, int NB, int NFRAG, int NS, int PK>
 static int mfma_lds_bytes_ns(const Shape &s) {
-    using T = MfmaTile<CS, NB, NFRAG>;
+    using T = MfmaTile<CS, NB, NFRAG, PK>;
     const int XR = 16 + s.FH - 1;
-    return 2 * (NS * CS * XR * T::PITCH + CS * s.FH * NFRAG * T::ZLEN + 16 * T::ORS);
+    const int fhp = (s.FH + PK - 1) / PK * PK;
+    const int zt = PK == 1 ? CS * s.FH * NFRAG * T::ZLEN : CS * fhp * T::ZS;
+    return 2 * (NS * CS * XR * T::PITCH + zt + 16 * T::ORS);
 }
 
-// The fused prologue on the same tiling as the plan's forward kernel (same
-// grid and launch shape); the tile's LDS grows by the extra rings.
-template <class DT, int CS, int NB, int NFRAG, int FHK, int NS>
+// The fused prologue on the plan's grid and launch shape (channel slice and
+// strip width); the tile's LDS grows by the extra rings.
+template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, int PK, int NS>
 static hipError_t launch_mfma_bn(const Plan &p, const void *x, const void *w, const void *bias,
                                  const float *bn_scale, const float *bn_shift, int act, void *y,
                                  hipStream_t st) {
-    const int lds = mfma_lds_bytes_ns<CS, NB, NFRAG, NS>(p.s);
+    const int lds = mfma_lds_bytes_ns<CS, NB, NFRAG, NS, PK>(p.s);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, 0, true, NS>),
+            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, FHT, true, NS, PK>),
             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, 0, true, NS>), dim3(p.grid),
-                       dim3(MfmaTile<CS, NB, NFRAG>::NT), lds, st, (const uint16_t *)x,
+    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT, true, NS, PK>), dim3(p.grid),
+                       dim3(MfmaTile<CS, NB, NFRAG, PK>::NT), lds, st, (const uint16_t *)x,
                        (const uint16_t *)w, (const float *)bias, (uint16_t *)y, p.s, p.aux0,
                        p.aux1, bn_scale, bn_shift, act);
     return hipGetLastError();
@@ -1017,28 +1031,46 @@ static const MfmaEntry kMfma[] = {
 #undef MFP
 
 // The fused prologue: two fp16 parts or three bf16 parts of U, for filters
-// of at most two fragments; FHK = 8 keeps the B operands of filters of up
-// to 8 rows in registers.  The tilings whose extra A operands would spill
-// registers (8 channels on 64-column strips; 8 bf16 channels with two
-// fragments) are left out.
+// of at most two fragments (FW <= 32); FHK = 8 keeps the B operands of
+// filters of up to 8 rows in registers.  The tilings whose extra A operands
+// would spill registers (8 channels on 64-column strips; 8 bf16 channels
+// with two fragments) are left out.  Row packing comes first, as forward:
+// 7x7 fp16 57 us against 68 with one row per MFMA, 31x31 bf16 204 against
+// 286 (the plain forward passes: 37 and 64 us).
 struct MfmaBnEntry {
-    int dtype, cs, nb, nfrag, fhk;
+    int dtype, cs, nb, nfrag, fhk, fht, pk;
     LaunchBnFn fn;
     int (*lds)(const Shape &);
 };
 #define MBH(CS_, NB_, NF_, FHK_)                                                    \
-    {DT_F16, CS_, NB_, NF_, FHK_, launch_mfma_bn<F16, CS_, NB_, NF_, FHK_, 2>,      \
-     mfma_lds_bytes_ns<CS_, NB_, NF_, 2>}
+    {DT_F16, CS_, NB_, NF_, FHK_, 0, 1, launch_mfma_bn<F16, CS_, NB_, NF_, FHK_, 0, 1, 2>, \
+     mfma_lds_bytes_ns<CS_, NB_, NF_, 2, 1>}
 #define MBB(CS_, NB_, NF_, FHK_)                                                    \
-    {DT_BF16, CS_, NB_, NF_, FHK_, launch_mfma_bn<BF16, CS_, NB_, NF_, FHK_, 3>,    \
-     mfma_lds_bytes_ns<CS_, NB_, NF_, 3>}
+    {DT_BF16, CS_, NB_, NF_, FHK_, 0, 1, launch_mfma_bn<BF16, CS_, NB_, NF_, FHK_, 0, 1, 3>, \
+     mfma_lds_bytes_ns<CS_, NB_, NF_, 3, 1>}
+// with row packing: PK filter rows per MFMA, J windows of 32 / PK columns
+#define MBPH(CS_, NB_, J_, FHK_, FHT_, PK_)                                          \
+    {DT_F16, CS_, NB_, J_, FHK_, FHT_, PK_,                                          \
+     launch_mfma_bn<F16, CS_, NB_, J_, FHK_, FHT_, PK_, 2>, mfma_lds_bytes_ns<CS_, NB_, J_, 2, PK_>}
+#define MBPB(CS_, NB_, J_, FHK_, FHT_, PK_)                                          \
+    {DT_BF16, CS_, NB_, J_, FHK_, FHT_, PK_,                                         \
+     launch_mfma_bn<BF16, CS_, NB_, J_, FHK_, FHT_, PK_, 3>, mfma_lds_bytes_ns<CS_, NB_, J_, 3, PK_>}
 static const MfmaBnEntry kMfmaBn[] = {
+    MBPH(8, 2, 3, 8, 7, 4), MBPB(8, 2, 3, 8, 7, 4), MBPH(4, 4, 3, 0, 31, 2),
+    MBPB(4, 4, 3, 0, 31, 2),
+    // runtime heights (the bf16 tilings of 64-column strips with three
+    // windows are left out: their operands would spill registers)
+    MBPH(8, 2, 3, 0, 0, 4), MBPB(8, 2, 3, 0, 0, 4), MBPH(4, 4, 3, 0, 0, 4),
+    MBPH(4, 4, 2, 0, 0, 2), MBPB(4, 4, 2, 0, 0, 2), MBPH(4, 4, 3, 0, 0, 2),
+    MBPH(4, 2, 2, 0, 0, 2), MBPB(4, 2, 2, 0, 0, 2), MBPH(4, 2, 3, 0, 0, 2), MBPB(4, 2, 3, 0, 0, 2),
     MBH(8, 2, 1, 8), MBB(8, 2, 1, 8), MBH(8, 2, 1, 0), MBB(8, 2, 1, 0), MBH(8, 2, 2, 0),
     MBH(4, 4, 1, 0), MBB(4, 4, 1, 0), MBH(4, 4, 2, 0), MBB(4, 4, 2, 0),
     MBH(4, 2, 1, 0), MBB(4, 2, 1, 0), MBH(4, 2, 2, 0), MBB(4, 2, 2, 0),
 };
 #undef MBH
 #undef MBB
+#undef MBPH
+#undef MBPB
 
 // The strip width (in 16-column blocks) that pads fewer output columns; on a
 // tie 32-column strips for one fragment and at least 7 filter rows
@@ -1143,19 +1175,27 @@ bool plan_mfma(Plan &p) {
 bool plan_mfma_bn(Plan &b, const Plan &f) {
     if (f.variant != V_MFMA) return false;
     const int nfrag = (f.s.FW + 15) / 16;
-    if (nfrag > 2) return false;
+    // mfma_pk=1|2|4, mfma_cs=4|8 and mfma_fhk=0|1 (tuning) as forward
+    const int want_pk = tune_int("mfma_pk", 0), want_cs = tune_int("mfma_cs", 0),
+              want_fhk = tune_int("mfma_fhk", -1);
     const int nb_pref = strip_blocks(f.s, nfrag);
     const MfmaBnEntry *e = nullptr;
     int lds = 0;
     for (int pass = 0; pass < 2 && !e; ++pass) {
         for (const auto &k : kMfmaBn) {
             if ((pass == 0) != (k.nb == nb_pref)) continue;
-            if (k.dtype != f.dtype || k.nfrag != nfrag || f.s.C % k.cs != 0) continue;
-            if (k.fhk && f.s.FH > k.fhk) continue;
-            const int need = k.lds(f.s);
-            if (need > 160 * 1024) continue;
+            if (want_pk && k.pk != want_pk) continue;
+            if (want_cs && k.cs != want_cs) continue;
+            if (want_fhk >= 0 && (k.fhk > 0) != (want_fhk > 0)) continue;
+            const int need = k.pk == 1 ? nfrag : (15 + f.s.FW + 32 / k.pk - 1) / (32 / k.pk);
+            if (k.dtype != f.dtype || k.nfrag != need || f.s.C % k.cs != 0) continue;
+            if (k.pk > 1 && f.s.FH > 32) continue;
+            if (k.fhk && k.pk == 1 && f.s.FH > k.fhk) continue;
+            if (k.fht && f.s.FH != k.fht) continue;
+            const int bytes = k.lds(f.s);
+            if (bytes > 160 * 1024) continue;
             e = &k;
-            lds = need;
+            lds = bytes;
             break;
         }
     }
@@ -1175,11 +1215,17 @@ bool plan_mfma_bn(Plan &b, const Plan &f) {
     b.lds_bytes = lds;
     b.launch = nullptr;
     b.bn_launch = e->fn;
-    snprintf(b.desc, sizeof(b.desc),
-             "mfma with the prologue fused: strips of %d cols x %d ch, %d fragment(s), U in "
-             "%s, LDS %d B, %u x %d",
-             16 * e->nb, e->cs, nfrag, f.dtype == DT_F16 ? "2 fp16 parts" : "3 bf16 parts", lds,
-             b.grid, b.block);
+    const char *parts = f.dtype == DT_F16 ? "2 fp16 parts" : "3 bf16 parts";
+    if (e->pk > 1)
+        snprintf(b.desc, sizeof(b.desc),
+                 "mfma with the prologue fused: %d filter rows per MFMA (%d windows of %d "
+                 "cols), strips of %d cols x %d ch, U in %s, LDS %d B, %u x %d",
+                 e->pk, e->nfrag, 32 / e->pk, 16 * e->nb, e->cs, parts, lds, b.grid, b.block);
+    else
+        snprintf(b.desc, sizeof(b.desc),
+                 "mfma with the prologue fused: strips of %d cols x %d ch, %d fragment(s), U in "
+                 "%s, LDS %d B, %u x %d",
+                 16 * e->nb, e->cs, nfrag, parts, lds, b.grid, b.block);
     return true;
 }
 

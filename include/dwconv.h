@@ -151,10 +151,9 @@ dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
  * direct kernel here.
  * Cost: on the vector families the prologue is nearly free (fp32 3x3: about
  * 4 % over dwconv_fwd).  On the matrix cores each part of U is one more set
- * of operands and instructions, and the fused kernel takes one filter row
- * per MFMA: measured about 1.8x dwconv_fwd's time for fp16 7x7 (two parts)
- * and 4x for bf16 31x31 (three parts); a widening vector kernel was slower
- * still for those shapes.  With the identity activation the sum could be
+ * of A operands and MFMAs: measured about 1.5x dwconv_fwd's time for fp16
+ * 7x7 (two parts) and 3.2x for bf16 31x31 (three parts, one workgroup per
+ * CU); a widening vector kernel was slower still for those shapes.  With the identity activation the sum could be
  * split as bn_scale * conv(x) + bn_shift * (the in-image filter taps), but
  * where x * bn_scale cancels bn_shift that split loses the accuracy the
  * tolerance states against sum |x*s + b| * |w|, so it is not used.  A caller that accepts U

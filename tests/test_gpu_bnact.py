@@ -153,13 +153,16 @@ def test_identity_prologue_matches_plain_forward(fmt):
         assert np.array_equal(y0.view(np.uint8), y1.view(np.uint8)), shape
 
 
+@pytest.mark.parametrize("tune", ["", "mfma_pk=1"])
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-def test_mfma_fused_prologue(fmt):
+def test_mfma_fused_prologue(fmt, tune, monkeypatch):
     """The prologue fused into the matrix-core kernel (U held as two fp16 or
     three bf16 parts): filters kept in registers (5x5, 7x7), runtime heights
     whose chains are folded (31x31, a 25-row filter), ragged strips, several
-    channel slices and every activation, against the oracle."""
-    rng = np.random.default_rng({"f16": 311, "bf16": 312}[fmt])
+    channel slices and every activation, against the oracle; with the
+    planner's choice of filter rows per MFMA and with one row per MFMA."""
+    monkeypatch.setenv("DWCONV_TUNE", tune)
+    rng = np.random.default_rng({"f16": 311, "bf16": 312}[fmt] + len(tune))
     for shape in [(2, 23, 37, 16, 7, 7, 1, 1, 3), (1, 30, 45, 8, 5, 5, 1, 1, 2),
                   (1, 40, 33, 8, 13, 13, 1, 1, 6), (1, 26, 19, 8, 31, 31, 1, 1, 15),
                   (1, 35, 20, 8, 25, 9, 1, 1, 4), (1, 17, 70, 24, 7, 7, 1, 1, 3)]:
@@ -173,7 +176,38 @@ def test_mfma_fused_prologue(fmt):
             say(f"[gpu] bn+act on the matrix cores {fmt} {shape} {act}")
             y, desc = run_bnact(x, w, bias, s, b, act, shape, fmt)
             assert desc.startswith("mfma with the prologue fused"), desc
+            if tune:
+                assert "filter rows per MFMA" not in desc, desc
             check_bnact(y, x, w, bias, s, b, act, shape, fmt, f"bnact mfma {fmt} {shape} {act}")
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_mfma_fused_prologue_row_packed(fmt, monkeypatch):
+    """The fused prologue with filter rows packed into the MFMA's K: four
+    7-row filter rows (kept B operands, 8-channel slices, 32-column strips)
+    and two 31-row filter rows (64-column strips, the chain of three bf16
+    parts folded), ragged strips, a map whose last 8 rows form a half row
+    block (after the full blocks for 7 rows, first for 31), an output of 6
+    rows and every activation, against the oracle."""
+    rng = np.random.default_rng({"f16": 321, "bf16": 322}[fmt])
+    cases = [("mfma_pk=4", 7, [(2, 23, 37, 16), (1, 56, 56, 8), (1, 6, 45, 8)]),
+             ("mfma_pk=2", 31, [(1, 26, 19, 4), (1, 56, 56, 4), (2, 40, 70, 8)])]
+    for tune, F, shapes in cases:
+        monkeypatch.setenv("DWCONV_TUNE", tune)
+        for (N, H, W, C) in shapes:
+            shape = (N, H, W, C, F, F, 1, 1, F // 2)
+            wl = synth.Workload("bn", fmt, *shape, ("normal", 0.0, 1.0),
+                                ("normal", 0.0, 1.0 / (F * F)), ("uniform", -0.1, 0.1),
+                                int(rng.integers(0, 2**31)))
+            x, w, bias = make_inputs(wl)
+            s, b = bn_params(C, int(rng.integers(0, 2**31)))
+            for act in ("none", "relu", "relu6"):
+                say(f"[gpu] bn+act packed rows {tune} {fmt} {shape} {act}")
+                y, desc = run_bnact(x, w, bias, s, b, act, shape, fmt)
+                assert desc.startswith("mfma with the prologue fused"), desc
+                assert f"{tune[-1]} filter rows per MFMA" in desc, desc
+                check_bnact(y, x, w, bias, s, b, act, shape, fmt,
+                            f"bnact mfma {tune} {fmt} {shape} {act}")
 
 
 def test_fp16_5x5_column_stream_prologue():
