@@ -182,6 +182,41 @@ def test_mfma_fused_prologue(fmt, tune, monkeypatch):
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_mfma_fused_prologue_random_shapes(fmt):
+    """The fused prologue on the matrix cores over random stride-1 shapes
+    (filters of 1 to 32 rows and 5 to 33 taps, channel counts that are
+    multiples of 4 or 8, ragged maps, padding from none to past half the
+    filter, a random activation), every output against the oracle."""
+    rng = np.random.default_rng({"f16": 331, "bf16": 332}[fmt])
+    done = 0
+    while done < 40:
+        FH = int(rng.integers(1, 33))
+        FW = int(rng.integers(5, 34))
+        H = int(rng.integers(1, 41))
+        W = int(rng.integers(1, 49))
+        C = 4 * int(rng.integers(1, 7))
+        P = int(rng.integers(0, max(FH, FW) // 2 + 3))
+        shape = (1, H, W, C, FH, FW, 1, 1, P)
+        if H + 2 * P - FH < 0 or W + 2 * P - FW < 0:
+            continue
+        h = dw.dwconv_create(*shape, fmt)
+        desc = dw.dwconv_fwd_bn_act_describe(h)
+        dw.dwconv_destroy(h)
+        if not desc.startswith("mfma with the prologue fused"):
+            continue
+        wl = synth.Workload("bn_rand", fmt, *shape, ("normal", 0.0, 1.0),
+                            ("normal", 0.0, 1.0 / (FH * FW)), ("uniform", -0.1, 0.1),
+                            int(rng.integers(0, 2**31)))
+        x, w, bias = make_inputs(wl)
+        s, b = bn_params(C, int(rng.integers(0, 2**31)))
+        act = ("none", "relu", "relu6")[int(rng.integers(0, 3))]
+        say(f"[gpu] bn+act random {fmt} #{done} {shape} {act}: {desc[:70]}")
+        y, desc = run_bnact(x, w, bias, s, b, act, shape, fmt)
+        check_bnact(y, x, w, bias, s, b, act, shape, fmt, f"bnact random {fmt} {shape} {act}")
+        done += 1
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
 def test_mfma_fused_prologue_row_packed(fmt, monkeypatch):
     """The fused prologue with filter rows packed into the MFMA's K: four
     7-row filter rows (kept B operands, 8-channel slices, 32-column strips)

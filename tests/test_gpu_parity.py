@@ -490,6 +490,41 @@ def test_mfma_row_packing(tune, monkeypatch):
             assert_matches_oracle(y, x, w, b, shape, fmt, f"mfma {tune} {shape}")
 
 
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_mfma_random_shapes(fmt):
+    """Random stride-1 shapes on the matrix cores, every output against the
+    oracle: filter heights 1 to 64 and widths 5 to 65 (one, two or four
+    filter rows per MFMA as the planner picks them, folded chains for the
+    tallest and widest), channel counts that are multiples of 4 or 8, ragged
+    maps narrower or shorter than a strip or a row block, padding from none
+    to more than half the filter, and a NaN guard band around y."""
+    rng = np.random.default_rng({"f16": 91, "bf16": 92}[fmt])
+    done = 0
+    while done < 64:
+        FH = int(rng.integers(1, 65))
+        FW = int(rng.integers(5, 66))
+        H = int(rng.integers(1, 49))
+        W = int(rng.integers(1, 57))
+        C = 4 * int(rng.integers(1, 7))
+        P = int(rng.integers(0, max(FH, FW) // 2 + 3))
+        shape = (1, H, W, C, FH, FW, 1, 1, P)
+        if H + 2 * P - FH < 0 or W + 2 * P - FW < 0 or not supported(shape, fmt, "mfma"):
+            continue
+        h = dw.dwconv_create_variant(*shape, fmt, "mfma")
+        desc = dw.dwconv_plan_describe(h)
+        dw.dwconv_destroy(h)
+        wl = synth.Workload("mfma_rand", fmt, *shape, ("normal", 0.0, 1.0),
+                            ("normal", 0.0, 1.0 / (FH * FW)),
+                            ("uniform", -0.1, 0.1) if rng.integers(0, 4) else None,
+                            int(rng.integers(0, 2**31)))
+        x, w, b = make_inputs(wl)
+        say(f"[gpu] mfma random {fmt} #{done} shape {shape}: {desc[:70]}")
+        y, used = run(x, w, b, shape, fmt, "mfma", guard=256)
+        assert used == "mfma", used
+        assert_matches_oracle(y, x, w, b, shape, fmt, f"mfma random {fmt} {shape} ({desc[:60]})")
+        done += 1
+
+
 # wide filters on the matrix cores: the compiled 31-row entry, ragged row
 # blocks and strips, outputs narrower than one strip, non-square filters of
 # 17 to 33 taps, one output row
