@@ -94,7 +94,7 @@ struct MfmaOp<BF16> {
 // PK > 1 (row packing): the K of one MFMA holds PK filter rows of
 // KW = 32 / PK input columns each, and NFRAG is the number J of KW-column
 // windows one 16-column output block reads per group of PK rows.
-template <int CS, int NB, int NFRAG, int PK = 1>
+template <int CS, int NB, int NFRAG, int PK = 1, int KS = 1>
 struct MfmaTile {
     static constexpr int KW = 32 / PK;
     // distinct A windows per filter row (PK = 1) or row group (PK > 1)
@@ -113,7 +113,9 @@ struct MfmaTile {
     // workgroups per CU up to 49-row filters)
     static constexpr int ZS = NFRAG >= 4 ? (18 + KW * NFRAG + 3) / 4 * 4
                                          : (18 + KW * NFRAG + 7) / 8 * 8;
-    static constexpr int NW = CS >= 16 ? 8 : 4;       // wavefronts per workgroup
+    // wavefronts per workgroup; KS = 2: two wavefronts per channel, each
+    // taking half of the filter's row groups
+    static constexpr int NW = (CS >= 16 ? 8 : 4) * KS;
     static constexpr int NT = 64 * NW;                 // threads per workgroup
     static constexpr int NPAIR = 8 * XW;               // column pairs in 16 rows
     static constexpr int NEWP = (NPAIR + NT - 1) / NT; // column pairs per thread
@@ -155,16 +157,19 @@ struct MfmaTile {
 // and their A entries are set to zero, so an Inf or NaN in the ring does
 // not reach outputs through them.
 template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL = false, int NS = 1,
-          int PK = 1>
-__global__ void __launch_bounds__(CS >= 16 ? 512 : 256, 2)  // at most 256 registers
+          int PK = 1, int KS = 1>
+__global__ void __launch_bounds__((CS >= 16 ? 512 : 256) * KS, 2 / KS)  // at most 256 registers
 k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
        const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int ncs, int nct,
        const float *__restrict__ bns, const float *__restrict__ bnb, int act) {
-    using T = MfmaTile<CS, NB, NFRAG, PK>;
+    using T = MfmaTile<CS, NB, NFRAG, PK, KS>;
     constexpr int XW = T::XW, PITCH = T::PITCH, ZLEN = T::ZLEN, ZS = T::ZS, KW = T::KW;
     constexpr int NW = T::NW, NT = T::NT;
-    static_assert(NT == (CS >= 16 ? 512 : 256), "launch bounds match the tile");
-    constexpr int NCH = CS / NW;            // channels per wavefront
+    static_assert(NT == (CS >= 16 ? 512 : 256) * KS, "launch bounds match the tile");
+    static_assert(KS == 1 || (KS == 2 && PK > 1 && FHT == 0 && NS == 1 && FHK == 0),
+                  "row groups split over two wavefronts: packed rows, runtime height");
+    constexpr int NWC = NW / KS;            // wavefronts per row-group half
+    constexpr int NCH = CS / NWC;           // channels per wavefront
     constexpr int NWIN = T::NWIN;           // distinct A windows per filter row / group
     static_assert(FHK == 0 || NFRAG == 1 || PK > 1, "kept B operands: one fragment");
     static_assert(FHT == 0 || FHK == 0 || FHT <= FHK || PK > 1, "kept B operands cover the filter");
@@ -203,7 +208,9 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     // scalar loads, which no MFMA then waits on together with the ring refill
     // loads (a vector load of the bias made the first row block's MFMAs wait
     // for the refill of the next block)
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = wave_id % NWC;         // the wavefront's channels: wave + NWC * ci
+    const int khalf = wave_id / NWC;        // its half of the row groups (KS = 2)
     const uint16_t *xn = x + (long long)n * s.H * s.W * s.C + c0;
     const int WC = s.W * s.C;  // elements of one image row (< 2^31)
 
@@ -374,7 +381,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     float bv[NCH];
 #pragma unroll
     for (int ci = 0; ci < NCH; ++ci) {
-        const int c = wave + NW * ci;
+        const int c = wave + NWC * ci;
         xc[ci] = xt + c * XR * PITCH + po;
         zc[ci] = zt + (PK == 1 ? c * FH * NFRAG * ZLEN : (c * FHP + pr) * ZS) + (boff & ~1);
         bv[ci] = bias ? bias[c0 + c] : 0.0f;
@@ -470,7 +477,12 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
 #pragma unroll
         for (int ci = 0; ci < NCH; ++ci)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) acc[ci][b] = (f32x4){bv[ci], bv[ci], bv[ci], bv[ci]};
+            for (int b = 0; b < NB; ++b) {
+                // with the row groups split over two wavefronts, the second
+                // half's sums start at zero (the bias is added once)
+                const float seed = KS > 1 && khalf ? 0.0f : bv[ci];
+                acc[ci][b] = (f32x4){seed, seed, seed, seed};
+            }
         // More than two fragments (filters wider than 32 taps): the chain of
         // 16 filter rows (at most 64 MFMAs) is added into a separate fp32
         // total, which the bias seeds, and restarts from zero.
@@ -662,8 +674,13 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                                 acc[ci][b] = MfmaOp<DT>::run(o.A[p][(PK / 2) * b + j], bb[j],
                                                              acc[ci][b]);
                 };
+                // this wavefront's row groups [gb, ge): all of them, or one
+                // half of them with KS = 2
+                const int NG = FHP / PK;
+                const int gb = KS > 1 && khalf ? (NG + 1) / 2 : 0;
+                const int ge = KS > 1 && !khalf ? (NG + 1) / 2 : NG;
                 OpsU o[2];
-                load_unit(o[0], 0, 0);
+                if (gb < ge) load_unit(o[0], 0, PK * gb);
                 if constexpr (FHT > 0) {
                     constexpr int NU = (FHT + PK - 1) / PK * NCH;
 #pragma unroll
@@ -679,21 +696,20 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                 } else {
                     // groups two at a time, so that a unit's operand buffer is
                     // fixed at compile time (2 * NCH units per step)
-                    const int NG = FHP / PK;
-                    for (int gi0 = 0; gi0 < NG; gi0 += 2) {
+                    for (int gi0 = gb; gi0 < ge; gi0 += 2) {
 #pragma unroll
                         for (int dg = 0; dg < 2; ++dg) {
                             const int gi = gi0 + dg;
-                            if (gi >= NG) break;
+                            if (gi >= ge) break;
 #pragma unroll
                             for (int ci = 0; ci < NCH; ++ci) {
                                 const int u = dg * NCH + ci;
                                 const int nci = ci + 1 < NCH ? ci + 1 : 0;
                                 const int ngi = ci + 1 < NCH ? gi : gi + 1;
-                                if (ngi < NG) load_unit(o[(u + 1) & 1], nci, PK * ngi);
+                                if (ngi < ge) load_unit(o[(u + 1) & 1], nci, PK * ngi);
                                 mfmas_unit(o[u & 1], ci, gi);
                             }
-                            if (FOLD && (gi + 1) % FG == 0) fold();
+                            if (FOLD && (gi - gb + 1) % FG == 0) fold();
                         }
                     }
                 }
@@ -816,11 +832,33 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                 for (int b = 0; b < NB; ++b) acc[ci][b] = tot[ci][b];
         }
 
-        // ---- epilogue: round once, regroup through LDS into NHWC vectors ----
+        // two wavefronts per channel: the second half's sums are added to
+        // the first half's through LDS (past the output tile), in a fixed
+        // order
         constexpr int OPS = T::OPS, ORS = T::ORS;
+        if constexpr (KS > 1) {
+            f32x4 *red = reinterpret_cast<f32x4 *>(ot + 16 * ORS);
+            if (khalf) {
+#pragma unroll
+                for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        red[((wave * NCH + ci) * NB + b) * 64 + lane] = acc[ci][b];
+            }
+            __syncthreads();
+            if (!khalf) {
+#pragma unroll
+                for (int ci = 0; ci < NCH; ++ci)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        acc[ci][b] += red[((wave * NCH + ci) * NB + b) * 64 + lane];
+            }
+        }
+        // ---- epilogue: round once, regroup through LDS into NHWC vectors ----
 #pragma unroll
         for (int ci = 0; ci < NCH; ++ci) {
-            const int c = wave + NW * ci;
+            const int c = wave + NWC * ci;
+            if (KS > 1 && khalf) break;  // the first half's wavefronts hold the sums
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -890,17 +928,17 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     }
 }
 
-template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL, int PK>
+template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL, int PK, int KS = 1>
 static hipError_t launch_mfma(const Plan &p, const void *x, const void *w, const void *bias,
                               void *y, hipStream_t st) {
     if (p.lds_bytes > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL, 1, PK>),
+            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL, 1, PK, KS>),
             hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL, 1, PK>), dim3(p.grid),
-                       dim3(MfmaTile<CS, NB, NFRAG, PK>::NT), p.lds_bytes, st,
+    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL, 1, PK, KS>), dim3(p.grid),
+                       dim3(MfmaTile<CS, NB, NFRAG, PK, KS>::NT), p.lds_bytes, st,
                        (const uint16_t *)x, (const uint16_t *)w, (const float *)bias,
                        (uint16_t *)y, p.s, p.aux0, p.aux1, nullptr, nullptr, 0);
     return hipGetLastError();
@@ -936,21 +974,24 @@ static hipError_t launch_mfma_bn(const Plan &p, const void *x, const void *w, co
     return hipGetLastError();
 }
 
-template <int CS, int NB, int NFRAG, int PK>
+template <int CS, int NB, int NFRAG, int PK, int KS = 1>
 static int mfma_lds_bytes(const Shape &s) {
-    using T = MfmaTile<CS, NB, NFRAG, PK>;
+    using T = MfmaTile<CS, NB, NFRAG, PK, KS>;
     const int XR = 16 + s.FH - 1;
     const int xt = CS * XR * T::PITCH;
     const int fhp = (s.FH + PK - 1) / PK * PK;
     const int zt = PK == 1 ? CS * s.FH * NFRAG * T::ZLEN : CS * fhp * T::ZS;
     const int ot = 16 * T::ORS;
-    return 2 * (xt + zt + ot);
+    // KS = 2: the second half's fp32 sums, 64 lanes x NB tiles per channel
+    const int red = KS > 1 ? CS * NB * 64 * 16 : 0;
+    return 2 * (xt + zt + ot) + red;
 }
 
 struct MfmaEntry {
     int dtype, cs, nb, nfrag, fhk, fht, al, pk;
     LaunchFn fn;
     int (*lds)(const Shape &);
+    int ks = 1;
 };
 
 #define MFA(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_, AL_)                                 \
@@ -962,6 +1003,11 @@ struct MfmaEntry {
      launch_mfma<DTT, CS_, NB_, J_, FHK_, FHT_, true, PK_>, mfma_lds_bytes<CS_, NB_, J_, PK_>}
 #define MFPD(CS_, NB_, J_, FHK_, FHT_, PK_) \
     MFP(DT_F16, F16, CS_, NB_, J_, FHK_, FHT_, PK_), MFP(DT_BF16, BF16, CS_, NB_, J_, FHK_, FHT_, PK_)
+// two rows per MFMA, each channel's row groups split over two wavefronts
+#define MFS(DTE, DTT, CS_, NB_, J_)                                                    \
+    {DTE,      CS_, NB_, J_, 0, 0, true, 2, launch_mfma<DTT, CS_, NB_, J_, 0, 0, true, 2, 2>, \
+     mfma_lds_bytes<CS_, NB_, J_, 2, 2>, 2}
+#define MFSD(CS_, NB_, J_) MFS(DT_F16, F16, CS_, NB_, J_), MFS(DT_BF16, BF16, CS_, NB_, J_)
 #define MF(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_) MFA(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_, false)
 
 // Each configuration twice: A windows read from LDS by every lane first
@@ -994,10 +1040,13 @@ static const MfmaEntry kMfma[] = {
     // most 9 taps, two rows for 10 to 17 and for 18 to 33 taps (on the f16
     // sweep maps 1.02-1.45x the speed of one row per MFMA at F = 7, 9, 17,
     // 21, 25, 31; 0.97-0.98 at F = 13 and 0.89 at F = 9 on 128x32x32x1024);
-    // two rows for 34 to 65 taps and up to 64 rows, folded chains: four
-    // windows fit two workgroups per CU up to 49 rows (80 KB), five run one
-    // per CU (107-155 KB); 1.1-2.1x one row per MFMA at F = 41 and 51
-    MFPD(4, 4, 4, 0, 0, 2), MFPD(4, 4, 5, 0, 0, 2), MFPD(4, 2, 4, 0, 0, 2), MFPD(4, 2, 5, 0, 0, 2),
+    // two rows for 34 to 65 taps and up to 64 rows, folded chains: two
+    // 4-wavefront workgroups per CU where the tile fits 80 KB, else one
+    // 8-wavefront workgroup with each channel's row groups split over two
+    // wavefronts, else one 4-wavefront workgroup; 1.1-2.7x one row per MFMA
+    // at F = 41 and 51
+    MFPD(4, 4, 4, 0, 0, 2), MFSD(4, 4, 5), MFSD(4, 2, 5), MFSD(4, 4, 4), MFPD(4, 4, 5, 0, 0, 2),
+    MFPD(4, 2, 4, 0, 0, 2), MFPD(4, 2, 5, 0, 0, 2),
     MFPD(8, 4, 3, 0, 0, 4), MFPD(8, 4, 2, 0, 0, 2), MFPD(8, 4, 3, 0, 0, 2),
     MFPD(4, 4, 3, 0, 0, 4), MFPD(4, 4, 2, 0, 0, 2), MFPD(4, 4, 3, 0, 0, 2),
     MFPD(8, 2, 3, 0, 0, 4), MFPD(8, 2, 2, 0, 0, 2), MFPD(8, 2, 3, 0, 0, 2),
@@ -1089,26 +1138,23 @@ bool plan_mfma(Plan &p) {
     // windows by DPP row shift / from LDS for every lane, mfma_nb=2|4 strips
     // of 32 / 64 output columns, mfma_pk=1|2|4 filter rows per MFMA,
     // mfma_fhk=0|1|F B operands read from LDS / kept in registers / kept
-    // for the filter rows below F
+    // for the filter rows below F, mfma_ks=1|2 one or two wavefronts per
+    // channel
     const int want_cs = tune_int("mfma_cs", 0), want_al = tune_int("mfma_al", -1),
               want_nb = tune_int("mfma_nb", 0), want_pk = tune_int("mfma_pk", 0),
-              want_fhk = tune_int("mfma_fhk", -1);
+              want_fhk = tune_int("mfma_fhk", -1), want_ks = tune_int("mfma_ks", 0);
     const int nfrag = (p.s.FW + 15) / 16;
     const int nb_pref = want_nb ? want_nb : strip_blocks(p.s, nfrag);
     const MfmaEntry *e = nullptr;
     int lds = 0;
-    // filters of 34 to 65 taps (four or five packed windows) run at two
-    // workgroups per CU where the tile fits in half the CU's LDS, with the
-    // other strip width if the preferred one does not fit (1.2-1.9x the
-    // speed of one workgroup per CU); otherwise the strip width comes first
-    const bool tall = !want_nb && p.s.FW >= 34 && p.s.FW <= 65;
-    for (int tier = tall ? 0 : 1; tier < 2 && !e; ++tier)
-    for (int pass = 0; pass < 2 && !e; ++pass) {
+    // The first entry (in table order) that `want` accepts, covers the shape
+    // and fits `cap` bytes of LDS (0: the channel slice's own cap).
+    auto pick = [&](auto want, int cap) {
         for (const auto &k : kMfma) {
-            if (tier == 0 && (k.pk == 1 || k.nfrag < 4)) continue;
-            if ((pass == 0) != (k.nb == nb_pref)) continue;
+            if (!want(k)) continue;
             if (want_nb && k.nb != want_nb) continue;
             if (want_pk && k.pk != want_pk) continue;
+            if (want_ks && k.ks != want_ks) continue;
             if (want_fhk >= 0 &&
                 (want_fhk <= 1 ? (k.fhk > 0) != (want_fhk > 0) : k.fhk != want_fhk))
                 continue;
@@ -1127,14 +1173,34 @@ bool plan_mfma(Plan &p) {
             // 16-channel slices run one 8-wavefront workgroup per CU; narrower
             // ones aim for at least two per CU unless nothing else fits
             const bool last = k.cs == 4 || want_cs;
-            const int cap = tier == 0 ? 80 * 1024 : k.cs == 16 || last ? 160 * 1024 : 64 * 1024;
-            if (bytes <= cap) {
+            const int lim = cap ? cap : k.cs == 16 || last ? 160 * 1024 : 64 * 1024;
+            if (bytes <= lim) {
                 e = &k;
                 lds = bytes;
-                break;
+                return true;
             }
         }
+        return false;
+    };
+    // Filters of 34 to 65 taps (four or five packed windows), at the
+    // preferred strip width: two workgroups per CU where the tile fits half
+    // the CU's LDS (35x35 on 64-column strips); else one 8-wavefront
+    // workgroup whose wavefronts split each channel's row groups (41 to 57
+    // taps: 1.25-1.3x one 4-wavefront workgroup per CU, and 1.25x two
+    // workgroups on 32-column strips); else one 4-wavefront workgroup (61
+    // taps on 64-column strips, where the split tile no longer fits).
+    const bool tall = !want_nb && p.s.FW >= 34 && p.s.FW <= 65;
+    if (tall) {
+        auto packed = [&](const MfmaEntry &k, int ks) {
+            return k.pk > 1 && k.nfrag >= 4 && k.ks == ks && k.nb == nb_pref;
+        };
+        pick([&](const MfmaEntry &k) { return packed(k, 1); }, 80 * 1024) ||
+            pick([&](const MfmaEntry &k) { return packed(k, 2); }, 160 * 1024) ||
+            pick([&](const MfmaEntry &k) { return packed(k, 1); }, 160 * 1024);
     }
+    // otherwise the preferred strip width first
+    if (!e) pick([&](const MfmaEntry &k) { return k.nb == nb_pref; }, 0);
+    if (!e) pick([&](const MfmaEntry &k) { return k.nb != nb_pref; }, 0);
     if (!e) return false;  // tall filters: the tile does not fit LDS
     const int ncs = p.s.C / e->cs;
     const int nct = (p.s.OW + 16 * e->nb - 1) / (16 * e->nb);
@@ -1150,15 +1216,17 @@ bool plan_mfma(Plan &p) {
     p.tile_c = e->cs;
     p.aux0 = ncs;
     p.aux1 = nct;
-    p.block = e->cs >= 16 ? 512 : 256;
+    p.block = (e->cs >= 16 ? 512 : 256) * e->ks;
     p.grid = (uint32_t)blocks;
     p.lds_bytes = lds;
     p.launch = e->fn;
     if (e->pk > 1)
         snprintf(p.desc, sizeof(p.desc),
                  "mfma: 16x16x32 banded GEMM, %d filter rows per MFMA (%d windows of %d "
-                 "cols), strips of %d cols x %d ch walked 16 rows at a time, LDS %d B, %u x %d",
-                 e->pk, e->nfrag, 32 / e->pk, 16 * e->nb, e->cs, lds, p.grid, p.block);
+                 "cols), strips of %d cols x %d ch walked 16 rows at a time%s, LDS %d B, %u x %d",
+                 e->pk, e->nfrag, 32 / e->pk, 16 * e->nb, e->cs,
+                 e->ks > 1 ? ", row groups split over two wavefronts per channel" : "", lds,
+                 p.grid, p.block);
     else
         snprintf(p.desc, sizeof(p.desc),
                  "mfma: 16x16x32 banded GEMM, strips of %d cols x %d ch walked 16 rows at a "

@@ -42,7 +42,7 @@ struct Plan {
     LaunchFn fallback;    // launcher for misaligned pointers (direct family)
     LaunchBnFn bn_launch;   // the same tiling with the fused prologue (NULL: none)
     LaunchBnFn bn_fallback; // the direct family with the fused prologue
-    char desc[192];
+    char desc[256];
 };
 
 // Backward-filter plan: pass 1 writes Z chunk sums per filter element into a
@@ -70,7 +70,7 @@ struct BwfPlan {
     BwfLaunchFn mfma_launch;
     int mcs, mncs, mnrc, mrpc, mZ, mlds;
     uint32_t mgrid;
-    char desc[192];
+    char desc[256];
 };
 bool plan_bwd_filter(BwfPlan &b, const Plan &forward);
 // Fills the matrix-core fields of `b` (b.s and b.dtype set); false when the

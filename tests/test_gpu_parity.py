@@ -449,6 +449,11 @@ ROW_PACKED = {  # tuning choice -> (dtype, FH, FW) the compiled entries cover
     "mfma_pk=2,mfma_cs=4": [("f16", 41, 41), ("bf16", 51, 51), ("f16", 64, 65),
                             ("bf16", 33, 34), ("f16", 40, 50), ("bf16", 17, 49)],
     "mfma_pk=2,mfma_cs=4,mfma_nb=2,mfma_fhk=0": [("bf16", 41, 41), ("f16", 51, 51)],
+    # each channel's row groups split over two wavefronts (the second half
+    # empty for filters of one or two rows)
+    "mfma_pk=2,mfma_ks=2": [("f16", 51, 51), ("bf16", 64, 65), ("f16", 17, 53),
+                            ("bf16", 40, 41), ("bf16", 1, 50), ("f16", 3, 60)],
+    "mfma_pk=2,mfma_ks=2,mfma_nb=2": [("f16", 57, 57), ("bf16", 33, 50)],
 }
 
 
@@ -484,6 +489,8 @@ def test_mfma_row_packing(tune, monkeypatch):
                     assert f"x {cs} ch" in desc, desc
             if "mfma_nb=2" in tune:
                 assert "strips of 32 cols" in desc, desc
+            if "mfma_ks=2" in tune:
+                assert "row groups split over two wavefronts" in desc, desc
             say(f"[gpu] mfma {tune}, {fmt} shape {shape}")
             y, used = run(x, w, b, shape, fmt, "mfma", guard=512)
             assert used == "mfma", used
