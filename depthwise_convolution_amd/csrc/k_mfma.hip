@@ -1043,7 +1043,7 @@ static const MfmaEntry kMfma[] = {
     // two rows for 34 to 65 taps and up to 64 rows, folded chains: two
     // 4-wavefront workgroups per CU where the tile fits 80 KB, else one
     // 8-wavefront workgroup with each channel's row groups split over two
-    // wavefronts, else one 4-wavefront workgroup; 1.1-2.7x one row per MFMA
+    // wavefronts, else one 4-wavefront workgroup; 1.6-2.7x one row per MFMA
     // at F = 41 and 51
     MFPD(4, 4, 4, 0, 0, 2), MFSD(4, 4, 5), MFSD(4, 2, 5), MFSD(4, 4, 4), MFPD(4, 4, 5, 0, 0, 2),
     MFPD(4, 2, 4, 0, 0, 2), MFPD(4, 2, 5, 0, 0, 2),
