@@ -24,9 +24,10 @@
 // one channel are formed: every MFMA works on a single channel, as the pages'
 // one-GEMM-per-channel does.
 //
-// Workgroup (4 wavefronts, 8 for 16-channel slices): one image, a strip of
-// 16*NB output columns and CS channels, walked down 16 output rows at a
-// time.  The input a row block needs -- the halo span (16 + FH - 1) rows x 16(NB + NFRAG) columns of
+// Workgroup (4 wavefronts; 8 for 16-channel slices, and for filters of 41 to
+// 61 taps, whose 8 wavefronts split each channel's filter rows in two halves
+// summed before the epilogue): one image, a strip of 16*NB output columns and
+// CS channels, walked down 16 output rows at a time.  The input a row block needs -- the halo span (16 + FH - 1) rows x 16(NB + NFRAG) columns of
 // "Tiles, halos and partial sums", with padding generated as zeros -- sits in
 // an LDS ring, channel-major, so that one 16-byte LDS read gives a lane its 8
 // consecutive columns of one channel (the A operand); each new block loads
@@ -126,9 +127,9 @@ struct MfmaTile {
     static constexpr int ORS = 16 * NB * OPS + 4;
 };
 
-// Workgroup (4 wavefronts, 8 for 16-channel slices): one image, a strip of
-// 16*NB output columns and CS channels, walking down the image 16 output rows
-// at a time.  The
+// Workgroup (4 wavefronts, 8 for 16-channel slices or with KS = 2): one
+// image, a strip of 16*NB output columns and CS channels, walking down the
+// image 16 output rows at a time.  The
 // XR = 16 + FH - 1 padded input rows a row block needs sit in an LDS ring;
 // moving to the next block replaces the 16 oldest rows, whose loads are
 // issued before the current block's MFMAs so that their latency is hidden.
@@ -156,6 +157,12 @@ struct MfmaTile {
 // group of a filter whose height is not a multiple of PK) have zero taps,
 // and their A entries are set to zero, so an Inf or NaN in the ring does
 // not reach outputs through them.
+// KS = 2 (packed rows, runtime height): two wavefronts per channel, the
+// first running the first half of the row groups into sums seeded with the
+// bias, the second the rest into sums seeded with zero; before the epilogue
+// the second half's sums go through LDS and are added to the first's (one
+// more fp32 rounding).  For tiles so large that one 4-wavefront workgroup
+// fills a CU, this gives each SIMD two wavefronts.
 template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL = false, int NS = 1,
           int PK = 1, int KS = 1>
 __global__ void __launch_bounds__((CS >= 16 ? 512 : 256) * KS, 2 / KS)  // at most 256 registers
