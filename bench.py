@@ -456,6 +456,12 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
 
     h = dw.dwconv_create_variant(wl.N, wl.H, wl.W, wl.C, wl.FH, wl.FW, wl.stride,
                                  wl.dilation, wl.pad, wl.dtype, variant_req)
+    # the steps pass raw device pointers and the raw stream handle (the
+    # tensors above stay alive), so a step costs the host one C call: the
+    # small workloads are then bound by the launch itself, not by Python
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    xp, yp, wp, bp = [ptr(t) for t in xs], [ptr(t) for t in ys], ptr(wd), ptr(bd)
+    sp = stream.cuda_stream
     bn_s = bn_b = None
     if bwf:
         desc = dw.dwconv_bwd_filter_describe(h)
@@ -464,8 +470,10 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
         variant = "bwf_mfma" if desc.startswith("bwf mfma") else "bwf"
         wsb = torch.empty(dw.dwconv_bwd_filter_workspace(h), dtype=torch.uint8, device=dev)
 
+        dyp, wsp = [ptr(t) for t in dys], ptr(wsb)
+
         def step(i):
-            dw.dwconv_bwd_filter(h, xs[i % sets], dys[i % sets], ys[i % sets], wsb, stream)
+            dw.dwconv_bwd_filter(h, xp[i % sets], dyp[i % sets], yp[i % sets], wsp, sp)
     elif bwd:
         if not dw.dwconv_bwd_data_supported(h):
             raise SystemExit(f"bench.py: {wl.name} has no backward-data pass in this build")
@@ -475,7 +483,7 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
         variant = "rowwin" if variant == "colstream" else variant
 
         def step(i):
-            dw.dwconv_bwd_data(h, xs[i % sets], wd, ys[i % sets], stream)
+            dw.dwconv_bwd_data(h, xp[i % sets], wp, yp[i % sets], sp)
     elif bna:
         desc = dw.dwconv_fwd_bn_act_describe(h)
         if not desc:
@@ -487,15 +495,16 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
         bn_s = torch.from_numpy(rs.uniform(0.5, 1.5, wl.C).astype(np.float32)).to(dev)
         bn_b = torch.from_numpy(rs.normal(0.0, 0.5, wl.C).astype(np.float32)).to(dev)
 
+        bsp, bbp = ptr(bn_s), ptr(bn_b)
+
         def step(i):
-            dw.dwconv_fwd_bn_act(h, xs[i % sets], wd, bd, bn_s, bn_b, "relu", ys[i % sets],
-                                 stream)
+            dw.dwconv_fwd_bn_act(h, xp[i % sets], wp, bp, bsp, bbp, "relu", yp[i % sets], sp)
     else:
         variant = dw.dwconv_plan_variant(h)
         desc = dw.dwconv_plan_describe(h)
 
         def step(i):
-            dw.dwconv_fwd(h, xs[i % sets], wd, bd, ys[i % sets], stream)
+            dw.dwconv_fwd(h, xp[i % sets], wp, bp, yp[i % sets], sp)
     print(f"[bench] plan: {desc}; {sets} buffer sets of {set_bytes / 1e6:.1f} MB",
           file=sys.stderr, flush=True)
 
