@@ -56,7 +56,7 @@ def bind(path):
     lib.dwref_bwd_data_f64.restype = I
     lib.dwref_bwd_filter_f64.argtypes = [P, P, P, P] + [I] * 11
     lib.dwref_bwd_filter_f64.restype = I
-    lib.dwref_fwd_bnact_f64.argtypes = [P, P, P, P, P, I, P, P] + [I] * 11
+    lib.dwref_fwd_bnact_f64.argtypes = [P, P, P, P, P, I, I, P, P] + [I] * 11
     lib.dwref_fwd_bnact_f64.restype = I
     return lib
 
@@ -247,16 +247,23 @@ def bwd_filter(x, dy, shape, dtype, threads=1, lib=None):
 
 
 ACTS = {"none": 0, "relu": 1, "relu6": 2}
+# the format U is stored in before the convolution: exact (fp32 data), or
+# binary16 / bfloat16 after one fp32 fused multiply-add
+FORMATS = {"f32": 0, "f16": 1, "bf16": 2}
 
 
 def fwd_bn_act(x, w, bias, bn_scale, bn_shift, act, stride, dilation, pad, dtype, threads=1,
                lib=None):
-    """Forward pass of act(x * bn_scale + bn_shift) -- a per-channel affine
-    (folded batch normalization) and an activation fused in front of the
-    convolution ("Flash-DWC", section 5.2) -- with zero padding of the
-    activated input.  ``act`` is "none", "relu" or "relu6"; bn_scale and
-    bn_shift hold C fp32 values.  Float dtypes only.  Returns ``(y, scale)``
-    in fp64, scale the sum of |x*s + b| * |w| over each output's taps."""
+    """Forward pass of U = act(x * bn_scale + bn_shift) -- a per-channel
+    affine (folded batch normalization) and an activation fused in front of
+    the convolution ("Flash-DWC", section 5.2) -- with zero padding of U.
+    ``act`` is "none", "relu" or "relu6"; bn_scale and bn_shift hold C fp32
+    values.  Float dtypes only.  fp32: U exact.  fp16 / bf16: U is what the
+    separate BN + Act pass would store in that format (section 4.1: tensors
+    kept in FP16, FP16 multiplications, FP32 accumulation): one fp32 fused
+    multiply-add, the activation, then round to nearest even.  Returns
+    ``(y, scale)`` in fp64, scale the sum of |x*s + b| * |w| over each
+    output's taps."""
     if dtype not in ("f32", "f16", "bf16"):
         raise ValueError("the fused prologue is defined here for float dtypes")
     if act not in ACTS:
@@ -278,7 +285,7 @@ def fwd_bn_act(x, w, bias, bn_scale, bn_shift, act, stride, dilation, pad, dtype
 
     def run(n0, n1):
         return lib.dwref_fwd_bnact_f64(_ptr(xx), _ptr(ww), _ptr(bb), _ptr(ss), _ptr(tt),
-                                       ACTS[act], _ptr(y), _ptr(scale),
+                                       ACTS[act], FORMATS[dtype], _ptr(y), _ptr(scale),
                                        N, H, W, C, FH, FW, stride, dilation, pad, n0, n1)
     threads = max(1, min(int(threads), N))
     if threads == 1:

@@ -305,6 +305,35 @@ int dwref_bwd_filter_f64(const double *x, const double *dy, double *dw, double *
     return 0;
 }
 
+/* Round-to-nearest-even of a finite or infinite double v to a binary format
+ * with `mant` stored significand bits and smallest normal exponent `emin`,
+ * returned as a double (exact).  The quantum is the value of the last
+ * significand bit at v's exponent, never finer than the subnormal spacing
+ * 2^(emin - mant); results past `maxf` become infinities (IEEE 754
+ * overflow under round-to-nearest); NaN stays NaN.  binary16: mant 10,
+ * emin -14, maxf 65504.  bfloat16: mant 7, emin -126, maxf (2 - 2^-7) 2^127. */
+static double round_binary(double v, int mant, int emin, double maxf)
+{
+    if (v != v || isinf(v)) return v;
+    double a = fabs(v);
+    int k;
+    frexp(a, &k);                 /* a = m 2^k with 0.5 <= m < 1 (or a = 0) */
+    int e = k - 1;                /* exponent of the leading bit */
+    if (e < emin) e = emin;
+    double q = ldexp(1.0, e - mant);
+    double r = nearbyint(a / q) * q;  /* a / q is exact; ties go to even */
+    if (r > maxf) r = INFINITY;
+    return v < 0 ? -r : r;
+}
+
+/* The fused prologue's input value in the storage format: fmt 1 binary16,
+ * 2 bfloat16. */
+static double round_storage(double u, int fmt)
+{
+    if (fmt == 1) return round_binary(u, 10, -14, 65504.0);
+    return round_binary(u, 7, -126, ldexp(255.0, 120));
+}
+
 /* Forward pass with the per-channel affine (batch normalization folded to a
  * scale and a shift) and an activation fused in front of the convolution
  * ("Flash-DWC: Making Depthwise Convolution Compute-Efficient on GPUs",
@@ -319,18 +348,26 @@ int dwref_bwd_filter_f64(const double *x, const double *dy, double *dw, double *
  *
  *   Y[n,oh,ow,c] = bias[c] + sum over in-image taps of U * W[fh,fw,c]
  *
- * all in fp64.  scale = sum over the same taps of |X*s + b| * |W| (the
- * magnitude before the activation).  Same layouts and batch split as
- * dwref_fwd_f64.  Returns 0, or -1 on a bad shape or activation. */
+ * accumulated in fp64.  fmt 0 (fp32 data): U exact in fp64.  fmt 1 / 2
+ * (fp16 / bf16 data): U is the tensor the separate BN + Act pass would store
+ * in the data's format -- section 4.1 of the same page: mixed precision keeps
+ * tensors in FP16 and multiplies FP16 operands, accumulating in FP32 -- so
+ * X * s + b is one fp32 fused multiply-add (fmaf, rounded once), the
+ * activation applies to that fp32 value, and U is it rounded to nearest even
+ * in binary16 / bfloat16.  scale = sum over the same taps of |X*s + b| * |W|
+ * (the magnitude before the activation; the fp32 value for fmt 1 / 2).  Same
+ * layouts and batch split as dwref_fwd_f64.  Returns 0, or -1 on a bad shape,
+ * activation or format. */
 int dwref_fwd_bnact_f64(const double *x, const double *w, const double *bias,
-                        const double *bn_scale, const double *bn_shift, int act,
+                        const double *bn_scale, const double *bn_shift, int act, int fmt,
                         double *y, double *scale,
                         int N, int H, int W, int C, int FH, int FW, int S, int D, int P,
                         int n0, int n1)
 {
     int OH, OW;
     if (!shape_ok(N, H, W, C, FH, FW, S, D, P, &OH, &OW)) return -1;
-    if (n0 < 0 || n1 > N || n0 > n1 || act < 0 || act > 2) return -1;
+    if (n0 < 0 || n1 > N || n0 > n1 || act < 0 || act > 2 || fmt < 0 || fmt > 2)
+        return -1;
     for (long long n = n0; n < n1; ++n)
         for (int oh = 0; oh < OH; ++oh)
             for (int ow = 0; ow < OW; ++ow)
@@ -343,11 +380,14 @@ int dwref_fwd_bnact_f64(const double *x, const double *w, const double *bias,
                         for (int fw = 0; fw < FW; ++fw) {
                             int iw = ow * S - P + fw * D;
                             if (iw < 0 || iw >= W) continue;
-                            double pre = x[((n * H + ih) * (long long)W + iw) * C + c] *
-                                         bn_scale[c] + bn_shift[c];
+                            double xv = x[((n * H + ih) * (long long)W + iw) * C + c];
+                            double pre = fmt ? (double)fmaf((float)xv, (float)bn_scale[c],
+                                                            (float)bn_shift[c])
+                                             : xv * bn_scale[c] + bn_shift[c];
                             double u = pre;
                             if (act >= 1 && u < 0.0) u = 0.0;
                             if (act == 2 && u > 6.0) u = 6.0;
+                            if (fmt) u = round_storage(u, fmt);
                             double wv = w[((long long)fh * FW + fw) * C + c];
                             acc += u * wv;
                             sabs += fabs(pre) * fabs(wv);

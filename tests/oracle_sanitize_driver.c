@@ -28,9 +28,9 @@ int dwref_bwd_filter_f64(const double *x, const double *dy, double *dw, double *
                          int H, int W, int C, int FH, int FW, int S, int D, int P, int c0,
                          int c1);
 int dwref_fwd_bnact_f64(const double *x, const double *w, const double *bias,
-                        const double *bn_scale, const double *bn_shift, int act, double *y,
-                        double *scale, int N, int H, int W, int C, int FH, int FW, int S,
-                        int D, int P, int n0, int n1);
+                        const double *bn_scale, const double *bn_shift, int act, int fmt,
+                        double *y, double *scale, int N, int H, int W, int C, int FH, int FW,
+                        int S, int D, int P, int n0, int n1);
 
 static uint64_t rng = 88172645463325252ull;
 static int rnd(int lo, int hi) { /* [lo, hi] */
@@ -86,8 +86,8 @@ int main(int argc, char **argv) {
         bad |= dwref_points_i8(xi, wi, bi, idx, 8, yip, N, H, W, C, FH, FW, S, D, P);
         bad |= dwref_bwd_data_f64(y, w, dx, dxs, N, H, W, C, FH, FW, S, D, P, 0, N);
         bad |= dwref_bwd_filter_f64(x, y, dwv, dws, N, H, W, C, FH, FW, S, D, P, 0, C);
-        bad |= dwref_fwd_bnact_f64(x, w, b, bs, bb, t % 3, y, sc, N, H, W, C, FH, FW, S, D, P,
-                                   0, N);
+        bad |= dwref_fwd_bnact_f64(x, w, b, bs, bb, t % 3, (t / 3) % 3, y, sc, N, H, W, C, FH,
+                                   FW, S, D, P, 0, N);
         if (bad) return 3;
         /* the points agree with the full passes */
         dwref_fwd_f64(x, w, b, y, sc, N, H, W, C, FH, FW, S, D, P, 0, N);
