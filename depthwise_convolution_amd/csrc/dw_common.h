@@ -91,14 +91,22 @@ __device__ __forceinline__ int32_t mac<int32_t>(int32_t acc, int32_t a, int32_t 
 // The fused prologue of the forward pass ("Flash-DWC: Making Depthwise
 // Convolution Compute-Efficient on GPUs", section 5.2: BN and the activation
 // applied to the input inside the convolution kernel): the input value x,
-// widened to fp32, becomes act(x * s + b) with one fused multiply-add and no
-// rounding to the storage format; act 0 = identity, 1 = ReLU, 2 = ReLU6.
-// Padding positions are zeros of the result, so callers apply it to in-image
-// values only.
+// widened to fp32, becomes act(x * s + b) with one fused multiply-add; act
+// 0 = identity, 1 = ReLU, 2 = ReLU6.  Padding positions are zeros of the
+// result, so callers apply it to in-image values only.
 __device__ __forceinline__ float bn_act(float x, float s, float b, int act) {
     float u = __builtin_fmaf(x, s, b);
     u = act >= 1 ? __builtin_fmaxf(u, 0.0f) : u;
     return act == 2 ? __builtin_fminf(u, 6.0f) : u;
+}
+
+// ... stored in the data's format before the convolution multiplies it:
+// fp16 / bf16 round to nearest even (section 4.1 of the same page: mixed
+// precision keeps tensors in FP16 and multiplies FP16 operands), as a
+// separate BN + Act pass would store it; fp32 is unchanged.
+template <class DT>
+__device__ __forceinline__ float bn_act_stored(float x, float s, float b, int act) {
+    return DT::widen(DT::narrow(bn_act(x, s, b, act)));
 }
 
 // Greatest common divisor (compile-time or host use).
@@ -112,6 +120,28 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb) {
     uint32_t q = nb / NX, rem = nb % NX;
     uint32_t xcd = b % NX, k = b / NX;
     return xcd < rem ? xcd * (q + 1) + k : rem * (q + 1) + (xcd - rem) * q + k;
+}
+
+// xcd_remap, and then, inside each XCD's range, the workgroups that one pass
+// of the XCD's dispatcher over its 32 CUs places on the same CU (positions
+// k, k + 32, ..., k + 32 (slots - 1) of a pass of 32 slots when the CUs are
+// filled breadth first) take consecutive logical tiles.  Positions past the
+// last whole pass keep their order.  A bijection on [0, nb) for any slots.
+__device__ __forceinline__ uint32_t xcd_remap_slots(uint32_t b, uint32_t nb, int slots) {
+    constexpr uint32_t NX = 8, NCU = 32;
+    const uint32_t q = nb / NX, rem = nb % NX;
+    const uint32_t xcd = b % NX;
+    uint32_t k = b / NX;
+    const uint32_t cnt = q + (xcd < rem ? 1u : 0u);
+    const uint32_t lo = xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
+    if (slots > 1) {
+        const uint32_t P = NCU * (uint32_t)slots;
+        if (k < cnt / P * P) {
+            const uint32_t i = k % P;
+            k = k - i + (i % NCU) * (uint32_t)slots + i / NCU;
+        }
+    }
+    return lo + k;
 }
 
 }  // namespace dw

@@ -52,7 +52,7 @@ k_direct(const typename DT::X *__restrict__ x, const typename DT::X *__restrict_
                 int iw = ow * s.S - s.P + fw * s.D;
                 if ((unsigned)iw >= (unsigned)s.W) continue;  // generated zeros
                 Acc xv = DT::widen(xr[(long long)iw * s.C]);
-                if constexpr (BN) xv = bn_act(xv, bs, bb, act);
+                if constexpr (BN) xv = bn_act_stored<DT>(xv, bs, bb, act);
                 row = mac<Acc>(row, xv, DT::widen(wc[(long long)tap_index(s, fh, fw) * s.C]));
             }
             acc += row;

@@ -136,14 +136,11 @@ struct MfmaTile {
 // FHK > 0: filters of at most FHK rows and one fragment keep every B operand
 // of the wavefront's channels in registers for the whole strip.
 // AL: every lane reads its A windows of each filter row from LDS (no DPP)
-// NS > 1: the fused prologue.  Each input value x becomes
-// U = act(x * bn_scale[c] + bn_shift[c]) in fp32 as the ring is written
-// (padding stays zero), and U is held as NS parts of the input format,
-// U = U_0 + U_1 (+ U_2), each the rounded remainder of the ones before: two
-// fp16 parts keep 22 of U's bits, three bf16 parts 24.  Each A window is
-// multiplied by the same B once per part, so the sum is that of U * w to
-// fp32 precision.  The chain is folded into an fp32 total every FP filter
-// rows (at most 64 MFMAs per chain).
+// BN: the fused prologue.  Each in-image input value x becomes
+// U = act(x * bn_scale[c] + bn_shift[c]) (one fp32 fused multiply-add, then
+// the activation) rounded to the input format as the ring is written -- the
+// value a separate BN + Act pass would store -- and the padding stays zero;
+// everything after the ring is the plain pass.
 // PK > 1 (row packing): the filter rows are taken PK at a time.  The K
 // window of one MFMA is PK filter rows of KW = 32 / PK consecutive input
 // columns each: lane (g, t16) holds row fh0 + 8g/KW + t16 of the ring,
@@ -163,26 +160,23 @@ struct MfmaTile {
 // the second half's sums go through LDS and are added to the first's (one
 // more fp32 rounding).  For tiles so large that one 4-wavefront workgroup
 // fills a CU, this gives each SIMD two wavefronts.
-template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL = false, int NS = 1,
+template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, bool AL = false, bool BN = false,
           int PK = 1, int KS = 1>
 __global__ void __launch_bounds__((CS >= 16 ? 512 : 256) * KS, 2 / KS)  // at most 256 registers
 k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
        const float *__restrict__ bias, uint16_t *__restrict__ y, Shape s, int ncs, int nct,
-       const float *__restrict__ bns, const float *__restrict__ bnb, int act) {
+       const float *__restrict__ bns, const float *__restrict__ bnb, int act, int slots) {
     using T = MfmaTile<CS, NB, NFRAG, PK, KS>;
     constexpr int XW = T::XW, PITCH = T::PITCH, ZLEN = T::ZLEN, ZS = T::ZS, KW = T::KW;
     constexpr int NW = T::NW, NT = T::NT;
     static_assert(NT == (CS >= 16 ? 512 : 256) * KS, "launch bounds match the tile");
-    static_assert(KS == 1 || (KS == 2 && PK > 1 && FHT == 0 && NS == 1 && FHK == 0),
+    static_assert(KS == 1 || (KS == 2 && PK > 1 && FHT == 0 && FHK == 0),
                   "row groups split over two wavefronts: packed rows, runtime height");
     constexpr int NWC = NW / KS;            // wavefronts per row-group half
     constexpr int NCH = CS / NWC;           // channels per wavefront
     constexpr int NWIN = T::NWIN;           // distinct A windows per filter row / group
     static_assert(FHK == 0 || NFRAG == 1 || PK > 1, "kept B operands: one fragment");
     static_assert(FHT == 0 || FHK == 0 || FHT <= FHK || PK > 1, "kept B operands cover the filter");
-    static_assert(NS == 1 || (AL && NS <= 3 && (PK > 1 || (FHT == 0 && NFRAG <= 2))),
-                  "the fused prologue: LDS-read A windows; one row per MFMA at a runtime "
-                  "filter height");
     static_assert(PK == 1 || ((PK == 2 || PK == 4) && AL && (FHK == 0 || FHT > 0)),
                   "row packing: 2 or 4 rows, LDS-read A windows, kept B with a fixed height");
     // FHT > 0: the filter height is a compile-time constant and the
@@ -194,15 +188,15 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const int FHP = (FH + PK - 1) / PK * PK;        // filter rows staged (PK > 1)
     const int XR = 16 + FH - 1;                     // ring rows
     const int RING = CS * XR * PITCH;               // elements of one ring
-    uint16_t *xt = lds;                             // [NS][CS][XR][PITCH]
-    uint16_t *zt = xt + NS * RING;  // [CS][FH][NFRAG][ZLEN], PK > 1: [CS][FHP][ZS]
+    uint16_t *xt = lds;                             // [CS][XR][PITCH]
+    uint16_t *zt = xt + RING;  // [CS][FH][NFRAG][ZLEN], PK > 1: [CS][FHP][ZS]
     const int ZT = PK == 1 ? CS * FH * NFRAG * ZLEN : CS * FHP * ZS;
     uint16_t *ot = zt + ZT;                         // [16][16*NB][CS]
 
     // workgroup -> (image, column strip, channel slice); channel slices vary
     // fastest so that the slices of one strip run together and share the L2
     // lines of its pixels
-    const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t bid = xcd_remap_slots(blockIdx.x, gridDim.x, slots);
     const int cs = bid % ncs;
     const uint32_t r = bid / ncs;
     const int ct = r % nct;
@@ -256,8 +250,8 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     // channel-major scatter into the ring, one dword (two columns) per
     // channel: padded row R lives in slot R mod XR
     // the fused prologue's per-channel scale and shift of the slice's channels
-    float bnsc[NS > 1 ? CS : 1], bnsh[NS > 1 ? CS : 1];
-    if constexpr (NS > 1) {
+    float bnsc[BN ? CS : 1], bnsh[BN ? CS : 1];
+    if constexpr (BN) {
 #pragma unroll
         for (int c = 0; c < CS; ++c) {
             bnsc[c] = bns[c0 + c];
@@ -272,7 +266,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
             int slot = r0m + crow[u];
             slot -= slot >= XR ? XR : 0;
             uint16_t *dst = xt + slot * PITCH + ccol[u];
-            if constexpr (NS == 1) {
+            if constexpr (!BN) {
 #pragma unroll
                 for (int k = 0; k < CS / 2; ++k) {
                     const uint32_t a = v[u][0][k], b = v[u][1][k];
@@ -282,32 +276,26 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                         (a >> 16) | (b & 0xffff0000u);
                 }
             } else {
-                // in-image values become U; the generated padding stays zero
+                // in-image values become U in the input format; the
+                // generated padding stays zero
                 const int ih = R0 + crow[u] - s.P;
                 const bool rok = (unsigned)ih < (unsigned)s.H;
                 const bool in0 = rok && cok0[u], in1 = rok && cok1[u];
 #pragma unroll
                 for (int c = 0; c < CS; ++c) {
                     const int sh16 = 16 * (c & 1);
-                    uint32_t parts[2][NS];
+                    uint32_t h[2];
 #pragma unroll
                     for (int col = 0; col < 2; ++col) {
                         const uint16_t xb = (uint16_t)(v[u][col][c / 2] >> sh16);
-                        float rem = (col ? in1 : in0)
-                                        ? bn_act(DT::widen(__builtin_bit_cast(typename DT::X, xb)),
-                                                 bnsc[c], bnsh[c], act)
-                                        : 0.0f;
-#pragma unroll
-                        for (int j = 0; j < NS; ++j) {
-                            const auto h = DT::narrow(rem);
-                            parts[col][j] = __builtin_bit_cast(uint16_t, h);
-                            rem -= DT::widen(h);
-                        }
+                        const float uv =
+                            bn_act(DT::widen(__builtin_bit_cast(typename DT::X, xb)), bnsc[c],
+                                   bnsh[c], act);
+                        h[col] = (col ? in1 : in0)
+                                     ? (uint32_t)__builtin_bit_cast(uint16_t, DT::narrow(uv))
+                                     : 0u;
                     }
-#pragma unroll
-                    for (int j = 0; j < NS; ++j)
-                        *reinterpret_cast<uint32_t *>(dst + j * RING + c * XR * PITCH) =
-                            parts[0][j] | (parts[1][j] << 16);
+                    *reinterpret_cast<uint32_t *>(dst + c * XR * PITCH) = h[0] | (h[1] << 16);
                 }
             }
         }
@@ -494,17 +482,12 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         // 16 filter rows (at most 64 MFMAs) is added into a separate fp32
         // total, which the bias seeds, and restarts from zero.
         // Row packing where the chain could pass 64 MFMAs (four or more
-        // windows for filters of 34 to 65 taps and up to 64 rows, or the
-        // fused prologue's parts): the chain of FG row groups (at most 64
-        // MFMAs) is folded the same way.
+        // windows for filters of 34 to 65 taps and up to 64 rows): the chain
+        // of FG row groups (at most 64 MFMAs) is folded the same way.
         constexpr int FHMAX = FHT > 0 ? FHT : NFRAG >= 4 ? 64 : 32;
-        constexpr bool FOLD = PK == 1 ? (NFRAG > 2 || NS > 1)
-                                      : (FHMAX + PK - 1) / PK * NFRAG * NS > 64;
-        // filter rows per folded chain: 16 (three or four fragments), or as
-        // many as keep a chain within 64 MFMAs with the prologue's parts
-        constexpr int FPR = NS > 1 ? 64 / (NFRAG * NS) : 16;
-        constexpr int FP = FPR > 2 ? (FPR & ~1) : 2;
-        constexpr int FG = 64 / (NFRAG * NS);  // row groups per folded chain (PK > 1)
+        constexpr bool FOLD = PK == 1 ? NFRAG > 2 : (FHMAX + PK - 1) / PK * NFRAG > 64;
+        constexpr int FP = 16;             // filter rows per folded chain (PK = 1)
+        constexpr int FG = 64 / NFRAG;     // row groups per folded chain (PK > 1)
         f32x4 tot[FOLD ? NCH : 1][FOLD ? NB : 1];
         auto fold = [&]() {
             if constexpr (FOLD) {
@@ -533,7 +516,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
         // from LDS.  B operands (unless kept) and the next windows are
         // produced before the MFMAs of row fh issue.
         struct Ops {
-            u32x4 A[NS][NCH][NWIN];
+            u32x4 A[NCH][NWIN];
             u32x4 B[NCH][FHK > 0 ? 1 : NFRAG];
         };
         auto full_a = [&](Ops &o) {
@@ -541,11 +524,8 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
             for (int ci = 0; ci < NCH; ++ci) {
                 const uint16_t *xr = xc[ci] + slot0 * PITCH;
 #pragma unroll
-                for (int j = 0; j < NS; ++j)
-#pragma unroll
-                    for (int win = 0; win < NWIN; ++win)
-                        o.A[j][ci][win] =
-                            *reinterpret_cast<const u32x4 *>(xr + j * RING + 16 * win);
+                for (int win = 0; win < NWIN; ++win)
+                    o.A[ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
             }
         };
         auto next_a = [&](Ops &o, const Ops &prev, int fh) {
@@ -557,24 +537,21 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                 if constexpr (AL) {
                     const uint16_t *xr = xc[ci] + slot * PITCH;
 #pragma unroll
-                    for (int j = 0; j < NS; ++j)
-#pragma unroll
-                        for (int win = 0; win < NWIN; ++win)
-                            o.A[j][ci][win] =
-                                *reinterpret_cast<const u32x4 *>(xr + j * RING + 16 * win);
+                    for (int win = 0; win < NWIN; ++win)
+                        o.A[ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
                     continue;
                 }
 #pragma unroll
                 for (int win = 0; win < NWIN; ++win)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        o.A[0][ci][win][q] = __builtin_amdgcn_update_dpp(
-                            0, (int)prev.A[0][ci][win][q], 0x101, 0xf, 0xf, true);
+                        o.A[ci][win][q] = __builtin_amdgcn_update_dpp(
+                            0, (int)prev.A[ci][win][q], 0x101, 0xf, 0xf, true);
                 if (t16 == 15) {
                     const uint16_t *xr = xc[ci] + slot * PITCH;
 #pragma unroll
                     for (int win = 0; win < NWIN; ++win)
-                        o.A[0][ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
+                        o.A[ci][win] = *reinterpret_cast<const u32x4 *>(xr + 16 * win);
                 }
             }
         };
@@ -602,9 +579,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                         } else {
                             bb = o.B[ci][f];
                         }
-#pragma unroll
-                        for (int j = 0; j < NS; ++j)
-                            acc[ci][b] = MfmaOp<DT>::run(o.A[j][ci][b + f], bb, acc[ci][b]);
+                        acc[ci][b] = MfmaOp<DT>::run(o.A[ci][b + f], bb, acc[ci][b]);
                     }
         };
 
@@ -614,9 +589,8 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
             // of the next unit are issued before the MFMAs of the current
             // one (two units of operands in registers).  At most 8 groups of
             // 6 windows (FH <= 32, FW <= 33): a chain of at most 48 MFMAs
-            // per tile, else folded every FG groups.  With the fused
-            // prologue each A window is read and multiplied once per part of
-            // U.  NBC column blocks per MFMA row set: NB, or NB/2 in
+            // per tile, else folded every FG groups.  NBC column blocks per
+            // MFMA row set: NB, or NB/2 in
             // a half block (each variant compiled on its own, so neither
             // carries the other's branches or registers).
             auto packed_rows = [&](auto nbc) {
@@ -626,7 +600,7 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                 slotp %= XR;                                               // at fh0 = 0
                 const int hoff = NBC < NB ? (t16 >> 3) * 8 * NB : 0;      // its column shift
                 struct OpsU {
-                    u32x4 A[NS][NWC];
+                    u32x4 A[NWC];
                     uint32_t R[FHK > 0 && FHK >= FHT ? 1 : NFRAG][5];
                 };
                 auto load_unit = [&](OpsU &o, int ci, int fh0) {
@@ -637,13 +611,10 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     const bool ok = full || fh0 + pr < FH;
                     const uint16_t *xr = xc[ci] + sl * PITCH + hoff;
 #pragma unroll
-                    for (int p = 0; p < NS; ++p)
-#pragma unroll
-                        for (int h = 0; h < NWC; ++h) {
-                            const u32x4 a =
-                                *reinterpret_cast<const u32x4 *>(xr + p * RING + KW * h);
-                            o.A[p][h] = ok ? a : (u32x4){0u, 0u, 0u, 0u};
-                        }
+                    for (int h = 0; h < NWC; ++h) {
+                        const u32x4 a = *reinterpret_cast<const u32x4 *>(xr + KW * h);
+                        o.A[h] = ok ? a : (u32x4){0u, 0u, 0u, 0u};
+                    }
                     if constexpr (!(FHK > 0 && FHK >= FHT)) {
                         if (FHK == 0 || fh0 >= PK * NGK) {
 #pragma unroll
@@ -676,10 +647,8 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     for (int j = 0; j < NFRAG; ++j)
 #pragma unroll
                         for (int b = 0; b < NBC; ++b)
-#pragma unroll
-                            for (int p = 0; p < NS; ++p)
-                                acc[ci][b] = MfmaOp<DT>::run(o.A[p][(PK / 2) * b + j], bb[j],
-                                                             acc[ci][b]);
+                            acc[ci][b] =
+                                MfmaOp<DT>::run(o.A[(PK / 2) * b + j], bb[j], acc[ci][b]);
                 };
                 // this wavefront's row groups [gb, ge): all of them, or one
                 // half of them with KS = 2
@@ -776,10 +745,10 @@ k_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     for (int win = 0; win < NWIN; ++win)
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
-                            n.A[0][ci][win][q] =
+                            n.A[ci][win][q] =
                                 AL ? Lw[fh & 1][ci][win][q]
                                    : __builtin_amdgcn_update_dpp((int)Lw[fh & 1][ci][win][q],
-                                                                 (int)p.A[0][ci][win][q], 0x101, 0xf,
+                                                                 (int)p.A[ci][win][q], 0x101, 0xf,
                                                                  0xf, false);
                 {
 #pragma unroll
@@ -940,44 +909,14 @@ static hipError_t launch_mfma(const Plan &p, const void *x, const void *w, const
                               void *y, hipStream_t st) {
     if (p.lds_bytes > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL, 1, PK, KS>),
+            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL, false, PK, KS>),
             hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL, 1, PK, KS>), dim3(p.grid),
+    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT, AL, false, PK, KS>), dim3(p.grid),
                        dim3(MfmaTile<CS, NB, NFRAG, PK, KS>::NT), p.lds_bytes, st,
                        (const uint16_t *)x, (const uint16_t *)w, (const float *)bias,
-                       (uint16_t *)y, p.s, p.aux0, p.aux1, nullptr, nullptr, 0);
-    return hipGetLastError();
-}
-
-// LDS of a tile with NS rings (the fused prologue's parts of U)
-template <int CS, int NB, int NFRAG, int NS, int PK>
-static int mfma_lds_bytes_ns(const Shape &s) {
-    using T = MfmaTile<CS, NB, NFRAG, PK>;
-    const int XR = 16 + s.FH - 1;
-    const int fhp = (s.FH + PK - 1) / PK * PK;
-    const int zt = PK == 1 ? CS * s.FH * NFRAG * T::ZLEN : CS * fhp * T::ZS;
-    return 2 * (NS * CS * XR * T::PITCH + zt + 16 * T::ORS);
-}
-
-// The fused prologue on the plan's grid and launch shape (channel slice and
-// strip width); the tile's LDS grows by the extra rings.
-template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, int PK, int NS>
-static hipError_t launch_mfma_bn(const Plan &p, const void *x, const void *w, const void *bias,
-                                 const float *bn_scale, const float *bn_shift, int act, void *y,
-                                 hipStream_t st) {
-    const int lds = mfma_lds_bytes_ns<CS, NB, NFRAG, NS, PK>(p.s);
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, FHT, true, NS, PK>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT, true, NS, PK>), dim3(p.grid),
-                       dim3(MfmaTile<CS, NB, NFRAG, PK>::NT), lds, st, (const uint16_t *)x,
-                       (const uint16_t *)w, (const float *)bias, (uint16_t *)y, p.s, p.aux0,
-                       p.aux1, bn_scale, bn_shift, act);
+                       (uint16_t *)y, p.s, p.aux0, p.aux1, nullptr, nullptr, 0, p.aux2);
     return hipGetLastError();
 }
 
@@ -994,26 +933,48 @@ static int mfma_lds_bytes(const Shape &s) {
     return 2 * (xt + zt + ot) + red;
 }
 
+// The fused prologue: the forward tiling with U formed as the ring is
+// written; the same LDS.
+template <class DT, int CS, int NB, int NFRAG, int FHK, int FHT, int PK>
+static hipError_t launch_mfma_bn(const Plan &p, const void *x, const void *w, const void *bias,
+                                 const float *bn_scale, const float *bn_shift, int act, void *y,
+                                 hipStream_t st) {
+    if (p.lds_bytes > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&k_mfma<DT, CS, NB, NFRAG, FHK, FHT, true, true, PK>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_mfma<DT, CS, NB, NFRAG, FHK, FHT, true, true, PK>), dim3(p.grid),
+                       dim3(MfmaTile<CS, NB, NFRAG, PK>::NT), p.lds_bytes, st,
+                       (const uint16_t *)x, (const uint16_t *)w, (const float *)bias,
+                       (uint16_t *)y, p.s, p.aux0, p.aux1, bn_scale, bn_shift, act, p.aux2);
+    return hipGetLastError();
+}
+
 struct MfmaEntry {
     int dtype, cs, nb, nfrag, fhk, fht, al, pk;
     LaunchFn fn;
     int (*lds)(const Shape &);
+    const void *kfn;  // the kernel, for the occupancy query
     int ks = 1;
 };
+#define KFN(...) reinterpret_cast<const void *>(&k_mfma<__VA_ARGS__>)
 
 #define MFA(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_, AL_)                                 \
     {DTE,      CS_, NB_, NF_, FHK_, FHT_, AL_, 1, launch_mfma<DTT, CS_, NB_, NF_, FHK_, FHT_, AL_, 1>, \
-     mfma_lds_bytes<CS_, NB_, NF_, 1>}
+     mfma_lds_bytes<CS_, NB_, NF_, 1>, KFN(DTT, CS_, NB_, NF_, FHK_, FHT_, AL_, false, 1, 1)}
 // row packing: PK filter rows per MFMA, J windows of 32 / PK columns
 #define MFP(DTE, DTT, CS_, NB_, J_, FHK_, FHT_, PK_)                                   \
     {DTE,      CS_, NB_, J_, FHK_, FHT_, true, PK_,                                     \
-     launch_mfma<DTT, CS_, NB_, J_, FHK_, FHT_, true, PK_>, mfma_lds_bytes<CS_, NB_, J_, PK_>}
+     launch_mfma<DTT, CS_, NB_, J_, FHK_, FHT_, true, PK_>, mfma_lds_bytes<CS_, NB_, J_, PK_>, \
+     KFN(DTT, CS_, NB_, J_, FHK_, FHT_, true, false, PK_, 1)}
 #define MFPD(CS_, NB_, J_, FHK_, FHT_, PK_) \
     MFP(DT_F16, F16, CS_, NB_, J_, FHK_, FHT_, PK_), MFP(DT_BF16, BF16, CS_, NB_, J_, FHK_, FHT_, PK_)
 // two rows per MFMA, each channel's row groups split over two wavefronts
 #define MFS(DTE, DTT, CS_, NB_, J_)                                                    \
     {DTE,      CS_, NB_, J_, 0, 0, true, 2, launch_mfma<DTT, CS_, NB_, J_, 0, 0, true, 2, 2>, \
-     mfma_lds_bytes<CS_, NB_, J_, 2, 2>, 2}
+     mfma_lds_bytes<CS_, NB_, J_, 2, 2>, KFN(DTT, CS_, NB_, J_, 0, 0, true, false, 2, 2), 2}
 #define MFSD(CS_, NB_, J_) MFS(DT_F16, F16, CS_, NB_, J_), MFS(DT_BF16, BF16, CS_, NB_, J_)
 #define MF(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_) MFA(DTE, DTT, CS_, NB_, NF_, FHK_, FHT_, false)
 
@@ -1086,47 +1047,52 @@ static const MfmaEntry kMfma[] = {
 #undef MFPD
 #undef MFP
 
-// The fused prologue: two fp16 parts or three bf16 parts of U, for filters
-// of at most two fragments (FW <= 32); FHK = 8 keeps the B operands of
-// filters of up to 8 rows in registers.  The tilings whose extra A operands
-// would spill registers (8 channels on 64-column strips; 8 bf16 channels
-// with two fragments) are left out.  Row packing comes first, as forward:
-// 7x7 fp16 57 us against 68 with one row per MFMA, 31x31 bf16 204 against
-// 286 (the plain forward passes: 37 and 64 us).
+// The fused prologue: the forward tilings (A windows read from LDS) for
+// filters of at most 33 taps, with U formed as the ring is written.  The
+// planner takes the forward plan's own tiling when it is here, else the
+// first that fits in this order (the forward order).
 struct MfmaBnEntry {
     int dtype, cs, nb, nfrag, fhk, fht, pk;
     LaunchBnFn fn;
     int (*lds)(const Shape &);
+    const void *kfn;
 };
-#define MBH(CS_, NB_, NF_, FHK_)                                                    \
-    {DT_F16, CS_, NB_, NF_, FHK_, 0, 1, launch_mfma_bn<F16, CS_, NB_, NF_, FHK_, 0, 1, 2>, \
-     mfma_lds_bytes_ns<CS_, NB_, NF_, 2, 1>}
-#define MBB(CS_, NB_, NF_, FHK_)                                                    \
-    {DT_BF16, CS_, NB_, NF_, FHK_, 0, 1, launch_mfma_bn<BF16, CS_, NB_, NF_, FHK_, 0, 1, 3>, \
-     mfma_lds_bytes_ns<CS_, NB_, NF_, 3, 1>}
-// with row packing: PK filter rows per MFMA, J windows of 32 / PK columns
-#define MBPH(CS_, NB_, J_, FHK_, FHT_, PK_)                                          \
-    {DT_F16, CS_, NB_, J_, FHK_, FHT_, PK_,                                          \
-     launch_mfma_bn<F16, CS_, NB_, J_, FHK_, FHT_, PK_, 2>, mfma_lds_bytes_ns<CS_, NB_, J_, 2, PK_>}
-#define MBPB(CS_, NB_, J_, FHK_, FHT_, PK_)                                          \
-    {DT_BF16, CS_, NB_, J_, FHK_, FHT_, PK_,                                         \
-     launch_mfma_bn<BF16, CS_, NB_, J_, FHK_, FHT_, PK_, 3>, mfma_lds_bytes_ns<CS_, NB_, J_, 3, PK_>}
+#define MBE(DTE, DTT, CS_, NB_, J_, FHK_, FHT_, PK_)                                  \
+    {DTE, CS_, NB_, J_, FHK_, FHT_, PK_, launch_mfma_bn<DTT, CS_, NB_, J_, FHK_, FHT_, PK_>, \
+     mfma_lds_bytes<CS_, NB_, J_, PK_>, KFN(DTT, CS_, NB_, J_, FHK_, FHT_, true, true, PK_, 1)}
+#define MBD(CS_, NB_, J_, FHK_, FHT_, PK_) \
+    MBE(DT_F16, F16, CS_, NB_, J_, FHK_, FHT_, PK_), MBE(DT_BF16, BF16, CS_, NB_, J_, FHK_, FHT_, PK_)
 static const MfmaBnEntry kMfmaBn[] = {
-    MBPH(8, 2, 3, 8, 7, 4), MBPB(8, 2, 3, 8, 7, 4), MBPH(4, 4, 3, 0, 31, 2),
-    MBPB(4, 4, 3, 0, 31, 2),
-    // runtime heights (the bf16 tilings of 64-column strips with three
-    // windows are left out: their operands would spill registers)
-    MBPH(8, 2, 3, 0, 0, 4), MBPB(8, 2, 3, 0, 0, 4), MBPH(4, 4, 3, 0, 0, 4),
-    MBPH(4, 4, 2, 0, 0, 2), MBPB(4, 4, 2, 0, 0, 2), MBPH(4, 4, 3, 0, 0, 2),
-    MBPH(4, 2, 2, 0, 0, 2), MBPB(4, 2, 2, 0, 0, 2), MBPH(4, 2, 3, 0, 0, 2), MBPB(4, 2, 3, 0, 0, 2),
-    MBH(8, 2, 1, 8), MBB(8, 2, 1, 8), MBH(8, 2, 1, 0), MBB(8, 2, 1, 0), MBH(8, 2, 2, 0),
-    MBH(4, 4, 1, 0), MBB(4, 4, 1, 0), MBH(4, 4, 2, 0), MBB(4, 4, 2, 0),
-    MBH(4, 2, 1, 0), MBB(4, 2, 1, 0), MBH(4, 2, 2, 0), MBB(4, 2, 2, 0),
+    // fixed heights: 31x31 and 7x7
+    MBD(4, 4, 3, 18, 31, 2), MBD(8, 2, 3, 8, 7, 4),
+    // row packing, any height up to 32
+    MBD(8, 4, 3, 0, 0, 4), MBD(8, 4, 2, 0, 0, 2), MBD(8, 4, 3, 0, 0, 2),
+    MBD(4, 4, 3, 0, 0, 4), MBD(4, 4, 2, 0, 0, 2), MBD(4, 4, 3, 0, 0, 2),
+    MBD(8, 2, 3, 0, 0, 4), MBD(8, 2, 2, 0, 0, 2), MBD(8, 2, 3, 0, 0, 2),
+    MBD(4, 2, 3, 0, 0, 4), MBD(4, 2, 2, 0, 0, 2), MBD(4, 2, 3, 0, 0, 2),
+    // one row per MFMA (filters taller than 32 rows, and mfma_pk=1)
+    MBD(8, 4, 1, 8, 0, 1), MBD(8, 4, 1, 0, 0, 1), MBD(8, 4, 2, 0, 0, 1),
+    MBD(4, 4, 1, 0, 0, 1), MBD(4, 4, 2, 0, 0, 1),
+    MBD(8, 2, 1, 8, 0, 1), MBD(8, 2, 1, 0, 0, 1), MBD(8, 2, 2, 0, 0, 1),
+    MBD(4, 2, 1, 0, 0, 1), MBD(4, 2, 2, 0, 0, 1),
 };
-#undef MBH
-#undef MBB
-#undef MBPH
-#undef MBPB
+#undef MBD
+#undef MBE
+#undef KFN
+
+// Workgroups of kernel `kfn` that one CU holds at once, from the runtime's
+// occupancy query; 1 when it cannot answer (no device).  The tuning choice
+// mfma_slots=n sets it.
+static int cu_slots(const void *kfn, int block, int lds) {
+    const int want = tune_int("mfma_slots", 0);
+    if (want >= 1) return want;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kfn, block, lds) != hipSuccess) {
+        (void)hipGetLastError();  // clear the error the query left
+        return 1;
+    }
+    return n >= 1 ? n : 1;
+}
 
 // The strip width (in 16-column blocks) that pads fewer output columns; on a
 // tie 32-column strips for one fragment and at least 7 filter rows
@@ -1224,6 +1190,8 @@ bool plan_mfma(Plan &p) {
     p.aux0 = ncs;
     p.aux1 = nct;
     p.block = (e->cs >= 16 ? 512 : 256) * e->ks;
+    p.aux2 = cu_slots(e->kfn, p.block, lds);
+    p.aux3 = (int)(e - kMfma);  // the tiling, for the fused prologue's plan
     p.grid = (uint32_t)blocks;
     p.lds_bytes = lds;
     p.launch = e->fn;
@@ -1244,9 +1212,10 @@ bool plan_mfma(Plan &p) {
 }
 
 // The forward pass with the fused prologue on the matrix cores, for a plan
-// whose forward pass runs there: the preferred strip width, 8-channel slices
-// before 4, the first tiling whose rings fit LDS.  Its own grid and launch
-// shape; the forward launchers are not used.
+// whose forward pass runs there: the forward plan's own tiling when the
+// fused table has it (the fused kernel is then the forward kernel with U
+// formed as its ring is written), else the preferred strip width, 8-channel
+// slices before 4, the first tiling whose ring fits LDS.
 bool plan_mfma_bn(Plan &b, const Plan &f) {
     if (f.variant != V_MFMA) return false;
     const int nfrag = (f.s.FW + 15) / 16;
@@ -1254,26 +1223,31 @@ bool plan_mfma_bn(Plan &b, const Plan &f) {
     const int want_pk = tune_int("mfma_pk", 0), want_cs = tune_int("mfma_cs", 0),
               want_fhk = tune_int("mfma_fhk", -1);
     const int nb_pref = strip_blocks(f.s, nfrag);
+    const MfmaEntry &fe = kMfma[f.aux3];
     const MfmaBnEntry *e = nullptr;
     int lds = 0;
-    for (int pass = 0; pass < 2 && !e; ++pass) {
-        for (const auto &k : kMfmaBn) {
-            if ((pass == 0) != (k.nb == nb_pref)) continue;
-            if (want_pk && k.pk != want_pk) continue;
-            if (want_cs && k.cs != want_cs) continue;
-            if (want_fhk >= 0 && (k.fhk > 0) != (want_fhk > 0)) continue;
-            const int need = k.pk == 1 ? nfrag : (15 + f.s.FW + 32 / k.pk - 1) / (32 / k.pk);
-            if (k.dtype != f.dtype || k.nfrag != need || f.s.C % k.cs != 0) continue;
-            if (k.pk > 1 && f.s.FH > 32) continue;
-            if (k.fhk && k.pk == 1 && f.s.FH > k.fhk) continue;
-            if (k.fht && f.s.FH != k.fht) continue;
-            const int bytes = k.lds(f.s);
-            if (bytes > 160 * 1024) continue;
-            e = &k;
-            lds = bytes;
+    auto fits = [&](const MfmaBnEntry &k) {
+        if (want_pk && k.pk != want_pk) return false;
+        if (want_cs && k.cs != want_cs) return false;
+        if (want_fhk >= 0 && (k.fhk > 0) != (want_fhk > 0)) return false;
+        const int need = k.pk == 1 ? nfrag : (15 + f.s.FW + 32 / k.pk - 1) / (32 / k.pk);
+        if (k.dtype != f.dtype || k.nfrag != need || f.s.C % k.cs != 0) return false;
+        if (k.pk > 1 && f.s.FH > 32) return false;
+        if (k.fhk && k.pk == 1 && f.s.FH > k.fhk) return false;
+        if (k.fht && f.s.FH != k.fht) return false;
+        const int bytes = k.lds(f.s);
+        if (bytes > 160 * 1024) return false;
+        e = &k;
+        lds = bytes;
+        return true;
+    };
+    for (const auto &k : kMfmaBn)
+        if (fe.ks == 1 && k.cs == fe.cs && k.nb == fe.nb && k.nfrag == fe.nfrag &&
+            k.fhk == fe.fhk && k.fht == fe.fht && k.pk == fe.pk && fits(k))
             break;
-        }
-    }
+    for (int pass = 0; pass < 2 && !e; ++pass)
+        for (const auto &k : kMfmaBn)
+            if ((pass == 0) == (k.nb == nb_pref) && fits(k)) break;
     if (!e) return false;
     const int ncs = f.s.C / e->cs;
     const int nct = (f.s.OW + 16 * e->nb - 1) / (16 * e->nb);
@@ -1286,21 +1260,23 @@ bool plan_mfma_bn(Plan &b, const Plan &f) {
     b.aux0 = ncs;
     b.aux1 = nct;
     b.block = 256;
+    b.aux2 = cu_slots(e->kfn, b.block, lds);
     b.grid = (uint32_t)blocks;
     b.lds_bytes = lds;
     b.launch = nullptr;
     b.bn_launch = e->fn;
-    const char *parts = f.dtype == DT_F16 ? "2 fp16 parts" : "3 bf16 parts";
+    const char *fmt = f.dtype == DT_F16 ? "fp16" : "bf16";
     if (e->pk > 1)
         snprintf(b.desc, sizeof(b.desc),
                  "mfma with the prologue fused: %d filter rows per MFMA (%d windows of %d "
-                 "cols), strips of %d cols x %d ch, U in %s, LDS %d B, %u x %d",
-                 e->pk, e->nfrag, 32 / e->pk, 16 * e->nb, e->cs, parts, lds, b.grid, b.block);
+                 "cols), strips of %d cols x %d ch, U rounded to %s as the ring is written, "
+                 "LDS %d B, %u x %d",
+                 e->pk, e->nfrag, 32 / e->pk, 16 * e->nb, e->cs, fmt, lds, b.grid, b.block);
     else
         snprintf(b.desc, sizeof(b.desc),
-                 "mfma with the prologue fused: strips of %d cols x %d ch, %d fragment(s), U in "
-                 "%s, LDS %d B, %u x %d",
-                 16 * e->nb, e->cs, nfrag, parts, lds, b.grid, b.block);
+                 "mfma with the prologue fused: strips of %d cols x %d ch, %d fragment(s), U "
+                 "rounded to %s as the ring is written, LDS %d B, %u x %d",
+                 16 * e->nb, e->cs, nfrag, fmt, lds, b.grid, b.block);
     return true;
 }
 

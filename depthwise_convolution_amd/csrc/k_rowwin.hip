@@ -68,7 +68,7 @@ __device__ __forceinline__ void store_vec(E *dst, const E (&src)[VEC]) {
 // it to the accumulator type.  Columns outside the image read as zero: their
 // address is clamped to column 0 (always inside the row, so the load is in
 // bounds and branch-free) and the value is replaced by zero.
-// BN: in-image values go through the fused prologue bn_act (bs, bb: the
+// BN: in-image values go through the fused prologue bn_act_stored (bs, bb: the
 // lane's VEC scales and shifts); positions outside the image stay zero.
 template <class DT, int VEC, int NWIN, bool BN = false>
 __device__ __forceinline__ void load_window(typename DT::Acc (&xw)[NWIN][VEC],
@@ -89,7 +89,7 @@ __device__ __forceinline__ void load_window(typename DT::Acc (&xw)[NWIN][VEC],
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
             typename DT::Acc val = DT::widen(e[j][v]);
-            if constexpr (BN) val = bn_act(val, bs[v], bb[v], act);
+            if constexpr (BN) val = bn_act_stored<DT>(val, bs[v], bb[v], act);
             xw[j][v] = ok ? val : typename DT::Acc(0);
         }
     }
@@ -396,7 +396,7 @@ __device__ __forceinline__ void colstream_walk(const typename DT::X *xn,
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
                 Acc val = DT::widen(raw[k % RING][j][v]);
-                if constexpr (BN) val = bn_act(val, bs[v], bb[v], act);
+                if constexpr (BN) val = bn_act_stored<DT>(val, bs[v], bb[v], act);
                 xw[j][v] = ok ? val : Acc(0);
             }
         }

@@ -401,16 +401,20 @@ def test_plans_from_many_host_threads():
 ])
 def test_fused_prologue_family(shape, fmt, family):
     """Which kernel runs the fused-prologue pass: the forward family where
-    it fuses the prologue, the matrix cores with U split into parts for their
-    shapes of at most two fragments, else a vector kernel."""
+    it fuses the prologue -- on the matrix cores the forward plan's own
+    tiling, with U rounded to the data's format as the ring is written --
+    else a vector kernel."""
     h = dw.dwconv_create(*shape, fmt)
     try:
         desc = dw.dwconv_fwd_bn_act_describe(h)
+        fwd = dw.dwconv_plan_describe(h)
     finally:
         dw.dwconv_destroy(h)
     assert desc.startswith(family), desc
     if family.startswith("mfma"):
-        assert ("2 fp16 parts" if fmt == "f16" else "3 bf16 parts") in desc, desc
+        assert ("U rounded to fp16" if fmt == "f16" else "U rounded to bf16") in desc, desc
+        tiling = fwd.split("banded GEMM, ", 1)[1].split(" walked", 1)[0]
+        assert tiling in desc, (tiling, desc)
 
 
 def test_counter_hash_ignores_comments_only():

@@ -2,7 +2,10 @@
 ("Flash-DWC: Making Depthwise Convolution Compute-Efficient on GPUs",
 section 5.2) through the C ABI, against the oracle's fwd_bn_act: the same
 elementwise bound as the forward pass, |y - y_exact| <= 1e-5 * scale + 1e-6
-on the value before the final rounding, scale = sum |x*s + b| * |w|."""
+on the value before the final rounding, scale = sum |x*s + b| * |w|.  For
+fp16 / bf16 data the convolution's input U = act(x*s + b) is in the data's
+format (one fp32 fused multiply-add, then rounded to nearest even), as a
+separate BN + Act pass would store it."""
 import numpy as np
 import pytest
 import torch
@@ -131,6 +134,56 @@ def test_misaligned_pointers_take_the_fallback():
     check_bnact(y, x, w, bias, s, b, "relu", shape, fmt, "bnact misaligned")
 
 
+ACT_F32 = {"none": lambda v: v,
+           "relu": lambda v: np.maximum(v, np.float32(0)),
+           "relu6": lambda v: np.minimum(np.maximum(v, np.float32(0)), np.float32(6))}
+
+
+def stored_u(x, s, act, fmt):
+    """U = act(x * s) (bn_shift 0, so the fused multiply-add is the float32
+    product) in fmt, by numpy's float16 / torch's bfloat16 conversion."""
+    if fmt == "f16":
+        return ACT_F32[act](x.astype(np.float32) * s).astype(np.float16)
+    xf = (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    u = torch.from_numpy(np.ascontiguousarray(ACT_F32[act](xf * s))).to(torch.bfloat16)
+    return u.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_fused_prologue_is_forward_of_stored_u(fmt):
+    """fp16 / bf16: the fused pass is the forward pass of U stored in the
+    data's format.  With bn_shift = 0 the host forms the same U with library
+    conversions, and where the fused kernel runs the forward tiling the
+    outputs are bit-identical: the 7x7 and 31x31 layers' tilings on the
+    matrix cores (two images), a one-row-per-MFMA filter, and the vector
+    column stream and (fp16, strided) row window."""
+    rng = np.random.default_rng({"f16": 341, "bf16": 342}[fmt])
+    for shape in [(2, 56, 56, 96, 7, 7, 1, 1, 3), (2, 56, 56, 128, 31, 31, 1, 1, 15),
+                  (1, 40, 21, 8, 35, 9, 1, 1, 4), (2, 30, 19, 16, 3, 3, 1, 1, 1)] + \
+            ([(2, 33, 35, 16, 5, 5, 2, 2, 4)] if fmt == "f16" else []):
+        N, H, W, C, FH, FW, S, D, P = shape
+        wl = synth.Workload("bn", fmt, *shape, ("normal", 0.0, 1.0),
+                            ("normal", 0.0, 1.0 / (FH * FW)), ("uniform", -0.1, 0.1),
+                            int(rng.integers(0, 2**31)))
+        x, w, bias = make_inputs(wl)
+        s = rng.uniform(0.5, 1.5, C).astype(np.float32)
+        h = dw.dwconv_create(*shape, fmt)
+        fdesc, pdesc = dw.dwconv_fwd_bn_act_describe(h), dw.dwconv_plan_describe(h)
+        dw.dwconv_destroy(h)
+        if pdesc.startswith("mfma"):
+            tiling = pdesc.split("banded GEMM, ", 1)[1].split(" walked", 1)[0].split(", A by")[0]
+            assert fdesc.startswith("mfma with the prologue fused") and tiling in fdesc, \
+                (pdesc, fdesc)
+        else:
+            assert fdesc == pdesc, (pdesc, fdesc)
+        for act in ("relu", "relu6", "none"):
+            say(f"[gpu] fused = forward of stored U {fmt} {shape} {act}")
+            y0, _ = run(stored_u(x, s, act, fmt), w, bias, shape, fmt, "auto", guard=64)
+            y1, _ = run_bnact(x, w, bias, s, np.zeros(C, np.float32), act, shape, fmt,
+                              guard=64)
+            assert np.array_equal(y0.view(np.uint8), y1.view(np.uint8)), (shape, act)
+
+
 @pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
 def test_identity_prologue_matches_plain_forward(fmt):
     """bn_scale = 1, bn_shift = 0, no activation: x*1 + 0 is x exactly, so
@@ -156,11 +209,11 @@ def test_identity_prologue_matches_plain_forward(fmt):
 @pytest.mark.parametrize("tune", ["", "mfma_pk=1"])
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 def test_mfma_fused_prologue(fmt, tune, monkeypatch):
-    """The prologue fused into the matrix-core kernel (U held as two fp16 or
-    three bf16 parts): filters kept in registers (5x5, 7x7), runtime heights
-    whose chains are folded (31x31, a 25-row filter), ragged strips, several
-    channel slices and every activation, against the oracle; with the
-    planner's choice of filter rows per MFMA and with one row per MFMA."""
+    """The prologue fused into the matrix-core kernel (U rounded to the data's
+    format as the ring is written): filters kept in registers (5x5, 7x7),
+    runtime heights (31x31, a 25-row filter), ragged strips, several channel
+    slices and every activation, against the oracle; with the planner's
+    choice of filter rows per MFMA and with one row per MFMA."""
     monkeypatch.setenv("DWCONV_TUNE", tune)
     rng = np.random.default_rng({"f16": 311, "bf16": 312}[fmt] + len(tune))
     for shape in [(2, 23, 37, 16, 7, 7, 1, 1, 3), (1, 30, 45, 8, 5, 5, 1, 1, 2),
@@ -220,8 +273,8 @@ def test_mfma_fused_prologue_random_shapes(fmt):
 def test_mfma_fused_prologue_row_packed(fmt, monkeypatch):
     """The fused prologue with filter rows packed into the MFMA's K: four
     7-row filter rows (kept B operands, 8-channel slices, 32-column strips)
-    and two 31-row filter rows (64-column strips, the chain of three bf16
-    parts folded), ragged strips, a map whose last 8 rows form a half row
+    and two 31-row filter rows (64-column strips), ragged strips, a map
+    whose last 8 rows form a half row
     block (after the full blocks for 7 rows, first for 31), an output of 6
     rows and every activation, against the oracle."""
     rng = np.random.default_rng({"f16": 321, "bf16": 322}[fmt])
