@@ -140,28 +140,22 @@ dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
  *   y[n,oh,ow,c]  = bias[c] + sum_{fh,fw} U[n, oh*S-P+fh*D, ow*S-P+fw*D, c]
  *                                         * w[fh,fw,c]
  *
- * U is computed in fp32 with one fused multiply-add per input value and is
- * never rounded to the storage format; padding positions are zeros of U.
- * bn_scale and bn_shift are C fp32 device values each -- batch normalization
- * folded by the caller (scale = gamma / sqrt(var + eps), shift = beta -
- * mean * scale) -- owned by the caller, any 4-byte alignment.  x, w, bias and
- * y as for dwconv_fwd; the same tolerance as the forward pass applies, stated
- * against sum |x*s + b| * |w|.  The register families and the matrix-core
- * family fuse the prologue; the matrix cores hold U as two fp16 or three
- * bf16 parts (U to fp32 precision), which for fp16 needs |x*s + b| within
- * the fp16 range (65504).  LDS-tile shapes run a row-window, row-chunk or
- * direct kernel here.
- * Cost: on the vector families the prologue is nearly free (fp32 3x3: about
- * 4 % over dwconv_fwd).  On the matrix cores each part of U is one more set
- * of A operands and MFMAs: measured about 1.5x dwconv_fwd's time for fp16
- * 7x7 (two parts) and 3.2x for bf16 31x31 (three parts, one workgroup per
- * CU); a widening vector kernel was slower still for those shapes.  With the identity activation the sum could be
- * split as bn_scale * conv(x) + bn_shift * (the in-image filter taps), but
- * where x * bn_scale cancels bn_shift that split loses the accuracy the
- * tolerance states against sum |x*s + b| * |w|, so it is not used.  A caller that accepts U
- * rounded once to the storage format (as an unfused batch-normalization pass
- * would leave it) gets that lower precision faster from its own elementwise
- * pass into a buffer followed by dwconv_fwd.
+ * U is computed in fp32 with one fused multiply-add and the activation per
+ * input value; for fp16 and bf16 data it is then rounded to nearest even in
+ * the data's format (the tensor a separate BN + Act pass would store, and
+ * what section 4.1 of the same page multiplies: FP16 operands with FP32
+ * accumulation); fp32 data keeps the fp32 value.  Padding positions are
+ * zeros of U.  bn_scale and bn_shift are C fp32 device values each -- batch
+ * normalization folded by the caller (scale = gamma / sqrt(var + eps),
+ * shift = beta - mean * scale) -- owned by the caller, any 4-byte alignment.
+ * x, w, bias and y as for dwconv_fwd; the forward pass's tolerance applies,
+ * stated against sum |x*s + b| * |w|.  Every float family fuses the prologue: the
+ * vector families form U as each input vector is loaded, the matrix cores as
+ * their LDS ring is written, on the forward plan's own tiling.  LDS-tile
+ * shapes run a row-window, row-chunk or direct kernel here.
+ * Cost: measured on MI355X at 1.04x dwconv_fwd's time for the fp32 3x3
+ * MobileNet layer, 1.08x for the fp16 7x7 ConvNeXt layer and 1.12x for the
+ * bf16 31x31 large-kernel layer.
  * Enqueued on `stream` without waiting.  Returns DWCONV_ERR_INVALID_ARG for a
  * NULL handle, x, w, y, bn_scale or bn_shift or an unknown activation,
  * DWCONV_ERR_UNSUPPORTED for int8 and DWCONV_ERR_HIP if the launch fails. */
