@@ -1081,11 +1081,21 @@ static const MfmaBnEntry kMfmaBn[] = {
 #undef KFN
 
 // Workgroups of kernel `kfn` that one CU holds at once, from the runtime's
-// occupancy query; 1 when it cannot answer (no device).  The tuning choice
-// mfma_slots=n sets it.
-static int cu_slots(const void *kfn, int block, int lds) {
+// occupancy query; 1 when it cannot answer (no device).  The kernel hands
+// the workgroups one CU holds consecutive tiles (xcd_remap_slots) only for
+// filters of 16 rows or more: there the co-resident channel slices of one
+// strip share their pixels' cache lines and the layer runs faster (31x31
+// bf16: 58.5 against 59.6 us, with 4.5 % more bytes written).  For shorter
+// filters the gain was within noise (7x7 fp16: 36.3 against 36.5 us) and
+// the cost is not: workgroups dispatched as slots free up then take channel
+// slices of many strips at once, the slices of one pixel reach L2 far apart
+// in time, its partly written lines are evicted before they are whole, and
+// HBM writes rose to 1.50 times y (1.025 with consecutive dispatch).
+// The tuning choice mfma_slots=n sets the count.
+static int cu_slots(const void *kfn, int block, int lds, int fh) {
     const int want = tune_int("mfma_slots", 0);
     if (want >= 1) return want;
+    if (fh < 16) return 1;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kfn, block, lds) != hipSuccess) {
         (void)hipGetLastError();  // clear the error the query left
@@ -1190,7 +1200,7 @@ bool plan_mfma(Plan &p) {
     p.aux0 = ncs;
     p.aux1 = nct;
     p.block = (e->cs >= 16 ? 512 : 256) * e->ks;
-    p.aux2 = cu_slots(e->kfn, p.block, lds);
+    p.aux2 = cu_slots(e->kfn, p.block, lds, p.s.FH);
     p.aux3 = (int)(e - kMfma);  // the tiling, for the fused prologue's plan
     p.grid = (uint32_t)blocks;
     p.lds_bytes = lds;
@@ -1260,7 +1270,7 @@ bool plan_mfma_bn(Plan &b, const Plan &f) {
     b.aux0 = ncs;
     b.aux1 = nct;
     b.block = 256;
-    b.aux2 = cu_slots(e->kfn, b.block, lds);
+    b.aux2 = cu_slots(e->kfn, b.block, lds, b.s.FH);
     b.grid = (uint32_t)blocks;
     b.lds_bytes = lds;
     b.launch = nullptr;

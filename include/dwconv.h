@@ -46,9 +46,10 @@
  * environment variable DWCONV_TUNE may hold comma-separated key=value
  * choices that force a compiled alternative; unset, the planner chooses.
  * Keys: mfma_cs=4|8|16, mfma_al=0|1, mfma_nb=2|4, mfma_pk=1|2|4,
- * mfma_fhk=0|1|F, mfma_ks=1|2 (the matrix-core kernel's channel slice,
- * A-operand source, strip width, filter rows per MFMA, B operands kept in
- * registers, and one or two wavefronts per channel), tile=TMxTH[pPF[n][l|i]] (a column-stream
+ * mfma_fhk=0|1|F, mfma_ks=1|2, mfma_slots=N (the matrix-core kernel's
+ * channel slice, A-operand source, strip width, filter rows per MFMA, B
+ * operands kept in registers, one or two wavefronts per channel, and the
+ * workgroups per CU whose tiles are numbered consecutively), tile=TMxTH[pPF[n][l|i]] (a column-stream
  * tiling), chunk_tm=8, lds_tb=1..64 (the LDS tile's height), bwf_valu=1 and
  * bwf_nocs=1 (filter-gradient pass 1 on the vector kernel).  A choice that
  * no compiled kernel provides makes dwconv_create_variant fail with
