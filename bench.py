@@ -34,8 +34,9 @@ large-kernel bf16 31x31, strided int8 5x5), timed in the same run.
                   of the same byte count, back to back; torch_copy is torch's
                   device-to-device copy timed the same way
   cpu_baseline    the CPU oracle timed on this host's cores on a sample
-Algorithmic bytes count x, w, bias and y once each; halo re-reads and
-padding are not counted.  FLOPs are 2 per tap per output.
+Algorithmic bytes count the input elements some tap reads (all of x at
+stride 1), w, bias and y once each; halo re-reads and padding are not
+counted.  FLOPs are 2 per tap per output.
 """
 import argparse
 import hashlib
@@ -79,11 +80,23 @@ def out_extent(size, f, s, d, p):
     return (size + 2 * p - d * (f - 1) - 1) // s + 1
 
 
+def touched(size, out, f, s, d, p):
+    """Input positions along one axis that at least one tap of one output
+    reads: oh*S - P + fh*D inside [0, size)."""
+    return len({o * s - p + k * d for o in range(out) for k in range(f)} & set(range(size)))
+
+
 def work(wl):
-    """(algorithmic bytes, flops, OH, OW) of one forward pass."""
+    """(algorithmic bytes, flops, OH, OW) of one forward pass.  The bytes are
+    the unique tensor bytes the operation must move ("Tiles, halos and partial
+    sums": unique bytes are the lower bound): the input elements that some
+    tap reads (all of x at stride 1; at stride 2 and dilation 2 only the even
+    rows and columns), w, bias and y, each once."""
     OH = out_extent(wl.H, wl.FH, wl.stride, wl.dilation, wl.pad)
     OW = out_extent(wl.W, wl.FW, wl.stride, wl.dilation, wl.pad)
-    xb = wl.N * wl.H * wl.W * wl.C * XB[wl.dtype]
+    rows = touched(wl.H, OH, wl.FH, wl.stride, wl.dilation, wl.pad)
+    cols = touched(wl.W, OW, wl.FW, wl.stride, wl.dilation, wl.pad)
+    xb = wl.N * rows * cols * wl.C * XB[wl.dtype]
     wb = wl.FH * wl.FW * wl.C * XB[wl.dtype]
     bb = wl.C * 4 if wl.b_dist is not None else 0
     yb = wl.N * OH * OW * wl.C * YB[wl.dtype]

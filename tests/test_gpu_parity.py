@@ -433,6 +433,30 @@ def test_mfma_strip_widths(nb, monkeypatch):
             assert_matches_oracle(y, x, w, b, shape, fmt, f"mfma nb{nb} {shape}")
 
 
+@pytest.mark.parametrize("slots", [1, 2, 3])
+def test_mfma_slot_renumbering(slots, monkeypatch):
+    """The workgroups one CU holds at once take consecutive tiles of their
+    XCD's range (mfma_slots=N forces N; unset, the planner takes the
+    occupancy for filters of 16 rows or more and 1 below).  The renumbering
+    must be a bijection on the grid: every output of grids with whole and
+    partial dispatcher passes (8 XCDs x 32 CUs x N slots) matches the
+    oracle, for a short and a tall filter."""
+    monkeypatch.setenv("DWCONV_TUNE", f"mfma_slots={slots}")
+    rng = np.random.default_rng(70 + slots)
+    # 7x7 fp16: 12 slices x 2 strips x 32 images = 768 workgroups;
+    # 31x31 bf16: 32 slices x 16 images = 512 workgroups
+    for fmt, F, (N, H, W, C) in [("f16", 7, (32, 56, 56, 96)), ("bf16", 31, (16, 40, 60, 128))]:
+        shape = (N, H, W, C, F, F, 1, 1, F // 2)
+        wl = synth.Workload("mfma", fmt, *shape, ("normal", 0.0, 1.0),
+                            ("normal", 0.0, 1.0 / F), ("uniform", -0.1, 0.1),
+                            int(rng.integers(0, 2**31)))
+        x, w, b = make_inputs(wl)
+        say(f"[gpu] mfma slots {slots}, {fmt} shape {shape}")
+        y, used = run(x, w, b, shape, fmt, "mfma", guard=512)
+        assert used == "mfma", used
+        assert_matches_oracle(y, x, w, b, shape, fmt, f"mfma slots{slots} {shape}")
+
+
 ROW_PACKED = {  # tuning choice -> (dtype, FH, FW) the compiled entries cover
     "mfma_pk=2": [("bf16", 31, 31), ("f16", 31, 25), ("f16", 7, 7), ("bf16", 7, 9),
                   ("bf16", 13, 13), ("f16", 21, 25), ("bf16", 32, 17), ("f16", 1, 31)],
