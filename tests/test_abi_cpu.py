@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import depthwise_convolution_amd as dw
@@ -426,3 +427,37 @@ def test_counter_hash_ignores_comments_only():
     assert bench.code_only("int  a =\n 1; /* z */") == bench.code_only("int a = 1;")
     assert bench.code_only("int a = 1;") != bench.code_only("int a = 2;")
     assert bench.code_only('f("a");') != bench.code_only('f("b");')
+
+
+def test_algorithmic_bytes_count_touched_inputs():
+    """The bench's algorithmic bytes count the input elements some tap reads
+    (unique bytes, "Tiles, halos and partial sums"): all of x for the
+    stride-1 "same" layers, the even rows and columns -- 56 of 112 each --
+    for the stride-2, dilation-2 5x5 int8 layer; brute force over a small
+    strided shape agrees with the per-axis count."""
+    import bench
+    from synth import WORKLOADS
+    for name in ("tiny_f32_3x3", "mobilenet_f32_3x3", "convnext_f16_7x7",
+                 "largekernel_bf16_31x31"):
+        wl = WORKLOADS[name]
+        nbytes, _, OH, OW = bench.work(wl)
+        x = wl.N * wl.H * wl.W * wl.C * bench.XB[wl.dtype]
+        y = wl.N * OH * OW * wl.C * bench.YB[wl.dtype]
+        assert nbytes == x + y + wl.FH * wl.FW * wl.C * bench.XB[wl.dtype] + wl.C * 4, name
+    wl = WORKLOADS["strided_i8_5x5"]
+    assert bench.touched(112, 56, 5, 2, 2, 4) == 56
+    nbytes, _, OH, OW = bench.work(wl)
+    assert nbytes == 16 * 56 * 56 * 61 + 16 * 56 * 56 * 61 * 4 + 25 * 61 + 61 * 4
+    # brute force: mark every (ih, iw) some output's tap reads
+    H, W, F, S, D, P = 11, 9, 3, 3, 2, 1
+    OH = (H + 2 * P - D * (F - 1) - 1) // S + 1
+    OW = (W + 2 * P - D * (F - 1) - 1) // S + 1
+    hit = np.zeros((H, W), bool)
+    for oh in range(OH):
+        for ow in range(OW):
+            for fh in range(F):
+                for fw in range(F):
+                    ih, iw = oh * S - P + fh * D, ow * S - P + fw * D
+                    if 0 <= ih < H and 0 <= iw < W:
+                        hit[ih, iw] = True
+    assert hit.sum() == bench.touched(H, OH, F, S, D, P) * bench.touched(W, OW, F, S, D, P)
