@@ -3,11 +3,16 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--variant auto|direct|rowwin|ldstile|mfma]
-                    [--op fwd|bwd_data|bwd_filter]
-                    [--no-cpu] [--no-copy]
+                    [--op fwd|bwd_data|bwd_filter|fwd_bn_act]
+                    [--launch graph|eager] [--no-cpu] [--no-copy]
 
 A step is one forward pass (one launch of the library's kernel) over one batch
-of seeded synthetic input.  The inputs are copied to HBM before timing.  So
+of seeded synthetic input, launched back to back (--launch graph also captures
+the K timed steps into one HIP graph and replays it).  Before each timed pass
+the bench runs about 100 ms of untimed steps: the GPU's clocks rise over the
+first tens of milliseconds of sustained load (a compute-bound layer's launches
+start about 20 % slower than they settle), and the timed steps are meant to
+see the sustained state.  The inputs are copied to HBM before timing.  So
 that no step finds its input in the 256 MB Infinity Cache (MALL) or in L2
 from an earlier step, the bench keeps several copies of x and y, at least
 1 GiB in all, and steps walk through them in turn.
@@ -18,6 +23,8 @@ default the fp32 3x3 MobileNet-shaped layer); with no --workload, --op or
 five workloads (tiny fp32 3x3, MobileNet fp32 3x3, ConvNeXt fp16 7x7,
 large-kernel bf16 31x31, strided int8 5x5), timed in the same run.
   value           algorithmic GB/s of K back-to-back steps (bytes / time per step)
+  launch, graph   how the timed steps were launched; the graph replay's and
+                  the eager launches' average per step
   roofline        the kernel's average duration (HIP events around the K
                   back-to-back steps, one launch each) against the roof that
                   binds it -- MI355X's 8 TB/s HBM, or for compute-bound
@@ -250,6 +257,7 @@ def copy_ceiling(torch, dev, stream, nbytes, sets, K, warmup, kind="nt"):
         one(i)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    clock_warmup(torch, stream, one)
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(K):
@@ -403,8 +411,29 @@ def run_sweep(args):
     return summary
 
 
+CLOCK_WARMUP_MS = 100.0
+
+
+def clock_warmup(torch, stream, step, ms=CLOCK_WARMUP_MS):
+    """Untimed steps, back to back, for about `ms` of GPU time (estimated from
+    ten timed steps), so that the clocks have settled when the timed steps
+    start.  Returns the number of steps run."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(10):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per = max(e0.elapsed_time(e1) / 10, 1e-3)
+    n = int(min(20000, max(0.0, ms - 10 * per) / per))
+    for i in range(n):
+        step(i)
+    return 10 + n
+
+
 def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=True,
-            warm_cache=False):
+            warm_cache=False, launch="eager"):
     """Times one workload's pass (op) and returns its record: value, kernel
     average and spread, roofline, copy ceilings and the CPU oracle baseline
     (cpu_budget seconds of host work; 0 skips it)."""
@@ -485,8 +514,8 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
 
         dyp, wsp = [ptr(t) for t in dys], ptr(wsb)
 
-        def step(i):
-            dw.dwconv_bwd_filter(h, xp[i % sets], dyp[i % sets], yp[i % sets], wsp, sp)
+        def step(i, st=sp):
+            dw.dwconv_bwd_filter(h, xp[i % sets], dyp[i % sets], yp[i % sets], wsp, st)
     elif bwd:
         if not dw.dwconv_bwd_data_supported(h):
             raise SystemExit(f"bench.py: {wl.name} has no backward-data pass in this build")
@@ -495,8 +524,8 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
                        if desc.startswith(v))
         variant = "rowwin" if variant == "colstream" else variant
 
-        def step(i):
-            dw.dwconv_bwd_data(h, xp[i % sets], wp, yp[i % sets], sp)
+        def step(i, st=sp):
+            dw.dwconv_bwd_data(h, xp[i % sets], wp, yp[i % sets], st)
     elif bna:
         desc = dw.dwconv_fwd_bn_act_describe(h)
         if not desc:
@@ -510,14 +539,14 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
 
         bsp, bbp = ptr(bn_s), ptr(bn_b)
 
-        def step(i):
-            dw.dwconv_fwd_bn_act(h, xp[i % sets], wp, bp, bsp, bbp, "relu", yp[i % sets], sp)
+        def step(i, st=sp):
+            dw.dwconv_fwd_bn_act(h, xp[i % sets], wp, bp, bsp, bbp, "relu", yp[i % sets], st)
     else:
         variant = dw.dwconv_plan_variant(h)
         desc = dw.dwconv_plan_describe(h)
 
-        def step(i):
-            dw.dwconv_fwd(h, xp[i % sets], wp, bp, yp[i % sets], sp)
+        def step(i, st=sp):
+            dw.dwconv_fwd(h, xp[i % sets], wp, bp, yp[i % sets], st)
     print(f"[bench] plan: {desc}; {sets} buffer sets of {set_bytes / 1e6:.1f} MB",
           file=sys.stderr, flush=True)
 
@@ -525,9 +554,11 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
         step(i)
     # pass 1: K steps back to back, bracketed by synchronisation (one GPU:
     # no barrier needed) -> whole-job throughput, and (one launch per step)
-    # the kernel's average duration, from HIP events on the launch stream
+    # the kernel's average duration, from HIP events on the launch stream;
+    # the clocks are brought to their sustained state first
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    n_clock = clock_warmup(torch, stream, step)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     start.record(stream)
@@ -542,6 +573,7 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
     # event packets' own time, so these run a little above pass 1's average)
     ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    clock_warmup(torch, stream, step)
     torch.cuda.synchronize()
     for i in range(K):
         ev0[i].record(stream)
@@ -549,12 +581,45 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
         ev1[i].record(stream)
     torch.cuda.synchronize()
     kern_ms = np.array([a.elapsed_time(z) for a, z in zip(ev0, ev1)])
+    # pass 1g (launch == "graph"): the same K steps captured once into a HIP
+    # graph (on a side stream of default priority) and replayed, timed with
+    # HIP events around the replay: the host submits one graph instead of K
+    # launches
+    graph = None
+    if launch == "graph":
+        try:
+            g = torch.cuda.CUDAGraph()
+            cs = torch.cuda.Stream(dev)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cs):
+                for i in range(K):
+                    step(i, cs.cuda_stream)
+            torch.cuda.synchronize()
+            g.replay()
+            clock_warmup(torch, stream, step)
+            torch.cuda.synchronize()
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
+            g.replay()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            graph = {"avg_us": round(g0.elapsed_time(g1) / K * 1e3, 3),
+                     "eager_avg_us": round(total_ms / K * 1e3, 3),
+                     "note": "the K steps captured into one HIP graph and replayed; "
+                             "eager_avg_us: the same steps launched one by one"}
+            del g
+        except RuntimeError as e:
+            graph = {"error": str(e)[:200]}
+            print(f"[bench] graph capture failed ({e}); timing the eager launches",
+                  file=sys.stderr, flush=True)
     # pass 3 (warm_cache), labelled: the same buffer set every step, so up
     # to 256 MB of it can stay in the MALL (not the headline figure)
     warm = None
     if warm_cache:
         w0 = torch.cuda.Event(enable_timing=True)
         w1 = torch.cuda.Event(enable_timing=True)
+        clock_warmup(torch, stream, lambda i: step(0))
         torch.cuda.synchronize()
         w0.record(stream)
         for i in range(K):
@@ -566,7 +631,10 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
     tmodel = tile_model(wl, dw.dwconv_plan_tile(h), OH, OW) if op == "fwd" else None
     dw.dwconv_destroy(h)
 
-    ms_per_step = total_ms / K
+    # the timed region: the graph replay when it was captured, else the
+    # eager launches
+    launched = "graph" if graph and "avg_us" in graph else "eager"
+    ms_per_step = graph["avg_us"] / 1e3 if launched == "graph" else total_ms / K
     kavg_ms = ms_per_step
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     traffic = stored_traffic(wl.name + (f":{op}" if op != "fwd" else ""), variant)
@@ -617,6 +685,9 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
                        "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3)},
                    "buffer_sets": sets},
         "warm_cache": warm,
+        "launch": launched,
+        "clock_warmup_steps": n_clock,
+        "graph": graph,
         "tile_model": tmodel,
         "copy_ceiling": copy,
         "torch_copy": tcopy,
@@ -646,6 +717,10 @@ def main():
                     help="also time K steps on one buffer set (labelled warm cache)")
     ap.add_argument("--no-copy", action="store_true",
                     help="skip the copy ceiling measurements")
+    ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
+                    help="eager (default): the K timed steps are launched one by one; "
+                         "graph: also captured into one HIP graph and replayed (reported "
+                         "beside, and the headline when the capture succeeds)")
     ap.add_argument("--sweep", action="store_true",
                     help="the filter-size sweep instead of the bench line: TFLOP/s against "
                          "F on three NHWC maps of 128 images (one JSON line per point)")
@@ -673,14 +748,15 @@ def main():
     name = args.workload or DEFAULT_WORKLOAD
     cpu_s = 0.0 if args.no_cpu else args.cpu_seconds
     head = measure(torch, dw, WORKLOADS[name], args.op, args.variant, args.steps,
-                   args.warmup, cpu_s, not args.no_copy, args.warm_cache)
+                   args.warmup, cpu_s, not args.no_copy, args.warm_cache, args.launch)
     others = {}
     if all_five:
         for other in WORKLOADS.values():
             if other.name == name:
                 continue
             others[other.name] = measure(torch, dw, other, "fwd", "auto", args.steps,
-                                         args.warmup, cpu_s / 3, not args.no_copy)
+                                         args.warmup, cpu_s / 3, not args.no_copy,
+                                         launch=args.launch)
     rec = {
         "metric": {"fwd": METRIC, "bwd_data": METRIC_BWD, "bwd_filter": METRIC_BWF,
                    "fwd_bn_act": METRIC_BNACT}[args.op],

@@ -1,0 +1,94 @@
+"""HIP graph capture of the library's passes (the bench times its steps as one
+captured graph).  Each pass is captured once through torch's graph capture and
+replayed several times, with eager work and synchronisations between the
+replays and the outputs cleared by a fill kernel before each; every replay
+must reproduce the eager result bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import depthwise_convolution_amd as dw
+import synth
+from synth import make_inputs
+
+from gpu_helpers import to_dev, y_torch_dtype, say, DEV
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # (fmt, N, H, W, C, FH, FW, S, D, P): one shape per kernel family of the workloads
+    ("f32", 4, 28, 28, 128, 3, 3, 1, 1, 1),
+    ("f16", 4, 28, 28, 96, 7, 7, 1, 1, 3),
+    ("bf16", 2, 40, 40, 128, 31, 31, 1, 1, 15),
+    ("i8", 2, 56, 56, 61, 5, 5, 2, 2, 4),
+]
+REPLAYS = 3
+
+
+def bits(t):
+    """The raw bits of a tensor, for a bitwise comparison."""
+    if t.dtype in (torch.float16, torch.bfloat16):
+        return t.view(torch.int16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32)
+    return t
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-{c[5]}x{c[6]}")
+def test_graph_replays_match_eager(case):
+    fmt, *shape = case
+    N, H, W, C, FH, FW, S, D, P = shape
+    wl = synth.Workload("graph", fmt, *shape, ("normal", 0.0, 1.0) if fmt != "i8" else
+                        ("int", -128, 127), ("normal", 0.0, 1.0 / (FH * FW)) if fmt != "i8"
+                        else ("int", -128, 127), ("uniform", -0.1, 0.1) if fmt != "i8"
+                        else ("int", -2**15, 2**15), 900 + FH)
+    x, w, b = make_inputs(wl)
+    h = dw.dwconv_create(N, H, W, C, FH, FW, S, D, P, fmt)
+    try:
+        OH, OW = dw.dwconv_output_dims(h)
+        xd, wd = to_dev(x, fmt), to_dev(w, fmt)
+        bd = to_dev(b, "f32" if fmt != "i8" else "i8")
+        ydt = y_torch_dtype(fmt)
+        rs = np.random.default_rng(7)
+        bns = torch.from_numpy(rs.uniform(0.5, 1.5, C).astype(np.float32)).to(DEV)
+        bnb = torch.from_numpy(rs.normal(0.0, 0.5, C).astype(np.float32)).to(DEV)
+        dyd = torch.randn(N, OH, OW, C, device=DEV).to(ydt) if fmt != "i8" else None
+        ws = torch.empty(max(dw.dwconv_bwd_filter_workspace(h), 16), dtype=torch.uint8,
+                         device=DEV) if fmt != "i8" else None
+
+        # (name, output shape and dtype, the call writing that output)
+        ops = [("fwd", ((N, OH, OW, C), ydt),
+                lambda y: dw.dwconv_fwd(h, xd, wd, bd, y))]
+        if fmt != "i8":
+            ops += [
+                ("fwd_bn_act", ((N, OH, OW, C), ydt),
+                 lambda y: dw.dwconv_fwd_bn_act(h, xd, wd, bd, bns, bnb, "relu", y)),
+                ("bwd_data", ((N, H, W, C), ydt),
+                 lambda y: dw.dwconv_bwd_data(h, dyd, wd, y)),
+                ("bwd_filter", ((FH, FW, C), torch.float32),
+                 lambda y: dw.dwconv_bwd_filter(h, xd, dyd, y, ws)),
+            ]
+        for name, (yshape, ytype), call in ops:
+            say(f"[gpu] graph {name} {fmt} shape {tuple(shape)}")
+            y_eager = torch.empty(yshape, dtype=ytype, device=DEV)
+            call(y_eager)
+            torch.cuda.synchronize()
+            y_graph = torch.zeros(yshape, dtype=ytype, device=DEV)
+            y_other = torch.empty(yshape, dtype=ytype, device=DEV)
+            g = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                call(y_graph)
+            torch.cuda.synchronize()
+            for r in range(REPLAYS):
+                # eager work between the replays: a fill kernel over the
+                # graph's output and an eager call of the same pass
+                y_graph.fill_(-7)
+                call(y_other)
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                assert torch.equal(bits(y_graph), bits(y_eager)), f"{name} replay {r}"
+                assert torch.equal(bits(y_other), bits(y_eager)), f"{name} eager {r}"
+            del g
+    finally:
+        dw.dwconv_destroy(h)
