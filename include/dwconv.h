@@ -154,8 +154,8 @@ dwconv_status_t dwconv_fwd(dwconv_handle_t h, const void *x, const void *w,
  * vector families form U as each input vector is loaded, the matrix cores as
  * their LDS ring is written, on the forward plan's own tiling.  LDS-tile
  * shapes run a row-window, row-chunk or direct kernel here.
- * Cost: measured on MI355X at 1.04x dwconv_fwd's time for the fp32 3x3
- * MobileNet layer, 1.08x for the fp16 7x7 ConvNeXt layer and 1.14x for the
+ * Cost: measured on MI355X at 1.05x dwconv_fwd's time for the fp32 3x3
+ * MobileNet layer, 1.07x for the fp16 7x7 ConvNeXt layer and 1.15x for the
  * bf16 31x31 large-kernel layer.
  * Enqueued on `stream` without waiting.  Returns DWCONV_ERR_INVALID_ARG for a
  * NULL handle, x, w, y, bn_scale or bn_shift or an unknown activation,
