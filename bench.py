@@ -9,7 +9,7 @@
 A step is one forward pass (one launch of the library's kernel) over one batch
 of seeded synthetic input, launched back to back (--launch graph also captures
 the K timed steps into one HIP graph and replays it).  Before each timed pass
-the bench runs about 100 ms of untimed steps: the GPU's clocks rise over the
+the bench runs about 300 ms of untimed steps (--clock-ms): the GPU's clocks rise over the
 first tens of milliseconds of sustained load (a compute-bound layer's launches
 start about 20 % slower than they settle), and the timed steps are meant to
 see the sustained state.  The inputs are copied to HBM before timing.  So
@@ -411,13 +411,14 @@ def run_sweep(args):
     return summary
 
 
-CLOCK_WARMUP_MS = 100.0
+CLOCK_WARMUP_MS = 300.0
 
 
-def clock_warmup(torch, stream, step, ms=CLOCK_WARMUP_MS):
+def clock_warmup(torch, stream, step, ms=None):
     """Untimed steps, back to back, for about `ms` of GPU time (estimated from
     ten timed steps), so that the clocks have settled when the timed steps
     start.  Returns the number of steps run."""
+    ms = CLOCK_WARMUP_MS if ms is None else ms
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -426,7 +427,7 @@ def clock_warmup(torch, stream, step, ms=CLOCK_WARMUP_MS):
     e1.record(stream)
     torch.cuda.synchronize()
     per = max(e0.elapsed_time(e1) / 10, 1e-3)
-    n = int(min(20000, max(0.0, ms - 10 * per) / per))
+    n = int(min(50000, max(0.0, ms - 10 * per) / per))
     for i in range(n):
         step(i)
     return 10 + n
@@ -698,6 +699,7 @@ def measure(torch, dw, wl, op, variant_req, K, warmup, cpu_budget, with_copy=Tru
 
 
 def main():
+    global CLOCK_WARMUP_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
@@ -717,6 +719,9 @@ def main():
                     help="also time K steps on one buffer set (labelled warm cache)")
     ap.add_argument("--no-copy", action="store_true",
                     help="skip the copy ceiling measurements")
+    ap.add_argument("--clock-ms", type=float, default=300.0,
+                    help="untimed back-to-back steps before each timed pass, in ms of GPU "
+                         "time, so that the clocks have settled (0: none)")
     ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
                     help="eager (default): the K timed steps are launched one by one; "
                          "graph: also captured into one HIP graph and replayed (reported "
@@ -731,6 +736,7 @@ def main():
     ap.add_argument("--sweep-seconds", type=float, default=0.3,
                     help="timed launches per point: about this many seconds, 1 to 20")
     args = ap.parse_args()
+    CLOCK_WARMUP_MS = args.clock_ms
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
               "supported (shard over the batch: one process per GPU, no exchange)",
