@@ -1,8 +1,10 @@
-"""HIP graph capture of the library's passes (the bench times its steps as one
-captured graph).  Each pass is captured once through torch's graph capture and
-replayed several times, with eager work and synchronisations between the
-replays and the outputs cleared by a fill kernel before each; every replay
-must reproduce the eager result bit for bit."""
+"""HIP graph capture of the library's passes (the bench can time its steps as
+one captured graph; the allocation-free filter gradient exists for callers
+such as code under graph capture).  Each pass is captured once through
+torch's graph capture and replayed several times, with eager work and
+synchronisations between the replays and the outputs cleared by a fill
+kernel before each; every replay must reproduce the eager result bit for
+bit."""
 import numpy as np
 import pytest
 import torch
@@ -66,6 +68,11 @@ def test_graph_replays_match_eager(case):
                  lambda y: dw.dwconv_bwd_data(h, dyd, wd, y)),
                 ("bwd_filter", ((FH, FW, C), torch.float32),
                  lambda y: dw.dwconv_bwd_filter(h, xd, dyd, y, ws)),
+                # the entry point for callers that cannot allocate (its
+                # scratch address is looked up by the eager call before the
+                # capture)
+                ("bwd_filter_noalloc", ((FH, FW, C), torch.float32),
+                 lambda y: dw.dwconv_bwd_filter_noalloc(h, xd, dyd, y)),
             ]
         for name, (yshape, ytype), call in ops:
             say(f"[gpu] graph {name} {fmt} shape {tuple(shape)}")
